@@ -1,0 +1,360 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for the conv2d training layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load this
+ * file: only the tests, the smoke check and the bench's cpu_baseline leg use it.  It
+ * shares no code, header, table or helper with the HIP library in
+ * convolution_layer_amd/csrc; the two meet only through the seeded inputs of
+ * workloads.py.
+ *
+ * Every routine is the textbook definition written out with fp64 accumulation, one
+ * output element at a time, with no blocking, fusion or reordering.  Parallelism
+ * (OpenMP) is only over independent outer indices, so results do not depend on the
+ * thread count.
+ *
+ * Pages cited (each is a source listing; the function name stands in for a section):
+ *   [generic] "rl_tools/nn/layers/conv2d/operations_generic.h" (hyperray 0.0.1 wheel)
+ *   [cuda]    "rl_tools/nn/layers/conv2d/operations_cuda.h"    (hyperray 0.0.1 wheel)
+ *   [mkl]     "rl_tools/nn/layers/conv2d/operations_cpu_mkl.h" (hyperray 0.0.1 wheel)
+ *   [wgsl]    "conv2d_backward_weight.wgsl" (@simulatte/doppler 0.1.0)
+ *
+ * Layouts (the pages' dense row-major NHWC activations and OHWI weights):
+ *   x  [N][H][W][IC], w [OC][KH][KW][IC], z/y/dy/dz [N][OH][OW][OC], dx like x,
+ *   dw like w, per-channel vectors [OC].
+ *
+ * Parity pinned by tests/test_oracle_pins.py: scipy correlate2d and torch fp64 conv
+ * (library routines), delta kernel, 1x1 = matmul, closed forms for constant inputs,
+ * adjoint identities, central finite differences, batch-norm invariants and torch fp64
+ * autograd through batch_norm + activation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef int64_t i64;
+
+enum { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_TANH = 2, ACT_SIGMOID = 3 };
+enum { NORM_NONE = 0, NORM_BATCH = 1 };
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Output extent along one axis: floor((in + 2p - k)/s) + 1 (symmetric zero padding,
+ * cross-correlation; [cuda] descriptor set-up uses symmetric padding and
+ * CUDNN_CROSS_CORRELATION; [generic] forward accepts a tap when p <= o*s+k < in+p).
+ * Returns 0 when the window does not fit, -1 for invalid s/k/p. */
+i64 oracle_out_extent(i64 in, i64 k, i64 s, i64 p) {
+    if (in <= 0 || k <= 0 || s <= 0 || p < 0) return -1;
+    i64 span = in + 2 * p - k;
+    if (span < 0) return 0;
+    return span / s + 1;
+}
+
+/* ---------------------------------------------------------------- activations ---- */
+/* [mkl] make_activation_post_ops: the activation set is identity, relu, tanh, sigmoid. */
+static double act_value(int act, double a) {
+    switch (act) {
+    case ACT_RELU: return a > 0.0 ? a : 0.0;
+    case ACT_TANH: return tanh(a);
+    case ACT_SIGMOID: return 1.0 / (1.0 + exp(-a));
+    default: return a;
+    }
+}
+
+/* Derivative d act(a) / da, evaluated at the activation input a ([generic]
+ * backward_input applies d_activation_d_x to the pre-activation).  relu'(0) = 0. */
+static double act_slope(int act, double a) {
+    switch (act) {
+    case ACT_RELU: return a > 0.0 ? 1.0 : 0.0;
+    case ACT_TANH: { double t = tanh(a); return 1.0 - t * t; }
+    case ACT_SIGMOID: { double s = 1.0 / (1.0 + exp(-a)); return s * (1.0 - s); }
+    default: return 1.0;
+    }
+}
+
+/* ---------------------------------------------------------------- a1 forward ---- */
+/* z[n,oh,ow,oc] = b[oc] + sum_{kh,kw,ic} w[oc,kh,kw,ic] * x[n, oh*sh-ph+kh, ow*sw-pw+kw, ic]
+ * with out-of-range taps contributing zero.  [generic] forward, phase 1 (conv + bias
+ * into pre_activations). */
+static double conv_point(const double* x, const double* w, const double* b,
+                         i64 H, i64 W, i64 IC, i64 KH, i64 KW, i64 sh, i64 sw, i64 ph, i64 pw,
+                         i64 n, i64 oh, i64 ow, i64 oc) {
+    double acc = b ? b[oc] : 0.0;
+    for (i64 kh = 0; kh < KH; ++kh) {
+        i64 ih = oh * sh - ph + kh;
+        if (ih < 0 || ih >= H) continue;
+        for (i64 kw = 0; kw < KW; ++kw) {
+            i64 iw = ow * sw - pw + kw;
+            if (iw < 0 || iw >= W) continue;
+            const double* xp = x + ((n * H + ih) * W + iw) * IC;
+            const double* wp = w + ((oc * KH + kh) * KW + kw) * IC;
+            for (i64 ic = 0; ic < IC; ++ic) acc += wp[ic] * xp[ic];
+        }
+    }
+    return acc;
+}
+
+void oracle_conv2d_forward(const double* x, const double* w, const double* b, double* z,
+                           i64 N, i64 H, i64 W, i64 IC, i64 OC, i64 KH, i64 KW,
+                           i64 sh, i64 sw, i64 ph, i64 pw) {
+    i64 OH = oracle_out_extent(H, KH, sh, ph), OW = oracle_out_extent(W, KW, sw, pw);
+    if (OH <= 0 || OW <= 0) return;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (i64 n = 0; n < N; ++n)
+        for (i64 oh = 0; oh < OH; ++oh)
+            for (i64 ow = 0; ow < OW; ++ow)
+                for (i64 oc = 0; oc < OC; ++oc)
+                    z[((n * OH + oh) * OW + ow) * OC + oc] =
+                        conv_point(x, w, b, H, W, IC, KH, KW, sh, sw, ph, pw, n, oh, ow, oc);
+}
+
+/* The same definition evaluated only at listed outputs idx[i] = (n, oh, ow, oc). */
+void oracle_conv2d_forward_at(const double* x, const double* w, const double* b,
+                              const i64* idx, i64 count, double* out,
+                              i64 N, i64 H, i64 W, i64 IC, i64 OC, i64 KH, i64 KW,
+                              i64 sh, i64 sw, i64 ph, i64 pw) {
+    (void)N; (void)OC;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i64 i = 0; i < count; ++i)
+        out[i] = conv_point(x, w, b, H, W, IC, KH, KW, sh, sw, ph, pw,
+                            idx[4 * i], idx[4 * i + 1], idx[4 * i + 2], idx[4 * i + 3]);
+}
+
+/* ---------------------------------------------------------------- a2 BN stats ---- */
+/* Per channel c over the M = N*OH*OW rows of z [M][C]:
+ *   mean = sum z / M;  var = sum (z - mean)^2 / M  (biased);  inv_std = 1/sqrt(var+eps)
+ *   running_mean <- (1-momentum)*running_mean + momentum*mean
+ *   running_var  <- (1-momentum)*running_var  + momentum*var   (the biased var)
+ * [generic] forward, batch-norm training branch (two passes); [cuda] bn_stats_training
+ * (same update rule, biased variance).  Running pointers may be NULL. */
+void oracle_bn_stats(const double* z, i64 M, i64 C, double momentum, double eps,
+                     double* mean, double* var, double* inv_std,
+                     double* running_mean, double* running_var) {
+#pragma omp parallel for schedule(static)
+    for (i64 c = 0; c < C; ++c) {
+        double s = 0.0;
+        for (i64 m = 0; m < M; ++m) s += z[m * C + c];
+        double mu = s / (double)M;
+        double q = 0.0;
+        for (i64 m = 0; m < M; ++m) {
+            double d = z[m * C + c] - mu;
+            q += d * d;
+        }
+        double v = q / (double)M;
+        mean[c] = mu;
+        if (var) var[c] = v;
+        inv_std[c] = 1.0 / sqrt(v + eps);
+        if (running_mean) running_mean[c] = (1.0 - momentum) * running_mean[c] + momentum * mu;
+        if (running_var) running_var[c] = (1.0 - momentum) * running_var[c] + momentum * v;
+    }
+}
+
+/* ------------------------------------------------------- a3 normalise + activate ---- */
+/* a = z (no norm) or gamma*(z-mean)*inv_std + beta (batch norm); y = act(a).
+ * [generic] forward phase 3 and the no-norm branch; [cuda] bn_forward_affine. */
+void oracle_apply_activation(const double* z, i64 M, i64 C, int act, int norm,
+                             const double* gamma, const double* beta,
+                             const double* mean, const double* inv_std, double* y) {
+#pragma omp parallel for schedule(static)
+    for (i64 m = 0; m < M; ++m)
+        for (i64 c = 0; c < C; ++c) {
+            double a = z[m * C + c];
+            if (norm == NORM_BATCH) a = gamma[c] * ((a - mean[c]) * inv_std[c]) + beta[c];
+            y[m * C + c] = act_value(act, a);
+        }
+}
+
+/* ReLU decides an integer (the mask) from a floating-point value.  With batch norm the
+ * library forms a in fp32 as fmaf(gamma, (z - mean) * inv_std, beta); the oracle takes
+ * that one decision in the same fp32 operations so both sides agree on the mask.  All
+ * other arithmetic stays fp64.  (Compiled with -ffp-contract=off.) */
+static int relu_mask_bn_f32(double z, double mean, double inv_std, double gamma, double beta) {
+    float zh = ((float)z - (float)mean) * (float)inv_std;
+    float a = fmaf((float)gamma, zh, (float)beta);
+    return a > 0.0f;
+}
+
+/* ------------------------------------------------------ a4 activation backward ---- */
+/* No norm:  dz = act'(z) * dy.
+ * Batch norm, training mode, per channel c over M rows:
+ *   zhat = (z - mean) * inv_std,  a = gamma*zhat + beta,  dno = act'(a) * dy,
+ *   dzhat = dno * gamma,  S1 = sum dzhat,  S2 = sum dzhat * zhat,
+ *   dz = inv_std / M * (M*dzhat - S1 - zhat*S2),
+ *   dgamma = sum dno * zhat,  dbeta = sum dno   (written, not accumulated).
+ * [generic] backward_input / backward, training-mode two-phase normalisation backward;
+ * [cuda] activation_backward and bn_training_backward.  dgamma/dbeta may be NULL. */
+void oracle_activation_backward(const double* z, const double* dy, i64 M, i64 C, int act, int norm,
+                                const double* gamma, const double* beta,
+                                const double* mean, const double* inv_std,
+                                double* dz, double* dgamma, double* dbeta) {
+    if (norm != NORM_BATCH) {
+#pragma omp parallel for schedule(static)
+        for (i64 i = 0; i < M * C; ++i) dz[i] = act_slope(act, z[i]) * dy[i];
+        return;
+    }
+#pragma omp parallel for schedule(static)
+    for (i64 c = 0; c < C; ++c) {
+        double g = gamma[c], mu = mean[c], is = inv_std[c];
+        double s1 = 0.0, s2 = 0.0, sg = 0.0, sb = 0.0;
+        for (i64 m = 0; m < M; ++m) {
+            i64 i = m * C + c;
+            double zh = (z[i] - mu) * is;
+            double a = g * zh + beta[c];
+            double slope = (act == ACT_RELU) ? (double)relu_mask_bn_f32(z[i], mu, is, g, beta[c])
+                                             : act_slope(act, a);
+            double dno = slope * dy[i];
+            double dzh = dno * g;
+            s1 += dzh;
+            s2 += dzh * zh;
+            sg += dno * zh;
+            sb += dno;
+        }
+        for (i64 m = 0; m < M; ++m) {
+            i64 i = m * C + c;
+            double zh = (z[i] - mu) * is;
+            double a = g * zh + beta[c];
+            double slope = (act == ACT_RELU) ? (double)relu_mask_bn_f32(z[i], mu, is, g, beta[c])
+                                             : act_slope(act, a);
+            double dzh = slope * dy[i] * g;
+            dz[i] = is / (double)M * ((double)M * dzh - s1 - zh * s2);
+        }
+        if (dgamma) dgamma[c] = sg;
+        if (dbeta) dbeta[c] = sb;
+    }
+}
+
+/* ---------------------------------------------------------------- a5 dX ---- */
+/* Scatter form of the adjoint of a1: for every output (n,oh,ow,oc) and every in-range
+ * tap (kh,kw), dx[n, oh*sh-ph+kh, ow*sw-pw+kw, ic] += w[oc,kh,kw,ic] * dz[n,oh,ow,oc].
+ * dx is overwritten (zeroed first).  [generic] backward_input (the scatter loop after
+ * the activation derivative); [cuda] backward_input = BackwardData with beta 0. */
+void oracle_conv2d_backward_data(const double* dz, const double* w, double* dx,
+                                 i64 N, i64 H, i64 W, i64 IC, i64 OC, i64 KH, i64 KW,
+                                 i64 sh, i64 sw, i64 ph, i64 pw) {
+    i64 OH = oracle_out_extent(H, KH, sh, ph), OW = oracle_out_extent(W, KW, sw, pw);
+    memset(dx, 0, sizeof(double) * (size_t)(N * H * W * IC));
+    if (OH <= 0 || OW <= 0) return;
+#pragma omp parallel for schedule(static)
+    for (i64 n = 0; n < N; ++n)
+        for (i64 oh = 0; oh < OH; ++oh)
+            for (i64 ow = 0; ow < OW; ++ow)
+                for (i64 oc = 0; oc < OC; ++oc) {
+                    double g = dz[((n * OH + oh) * OW + ow) * OC + oc];
+                    for (i64 kh = 0; kh < KH; ++kh) {
+                        i64 ih = oh * sh - ph + kh;
+                        if (ih < 0 || ih >= H) continue;
+                        for (i64 kw = 0; kw < KW; ++kw) {
+                            i64 iw = ow * sw - pw + kw;
+                            if (iw < 0 || iw >= W) continue;
+                            double* xp = dx + ((n * H + ih) * W + iw) * IC;
+                            const double* wp = w + ((oc * KH + kh) * KW + kw) * IC;
+                            for (i64 ic = 0; ic < IC; ++ic) xp[ic] += wp[ic] * g;
+                        }
+                    }
+                }
+}
+
+/* One dx element: the sum over every (oc, kh, kw) whose tap lands on (ih, iw), i.e.
+ * oh*sh - ph + kh == ih and ow*sw - pw + kw == iw with (oh, ow) in range. */
+void oracle_conv2d_backward_data_at(const double* dz, const double* w, const i64* idx, i64 count,
+                                    double* out, i64 N, i64 H, i64 W, i64 IC, i64 OC, i64 KH, i64 KW,
+                                    i64 sh, i64 sw, i64 ph, i64 pw) {
+    (void)N; (void)H; (void)W;
+    i64 OH = oracle_out_extent(H, KH, sh, ph), OW = oracle_out_extent(W, KW, sw, pw);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i64 i = 0; i < count; ++i) {
+        i64 n = idx[4 * i], ih = idx[4 * i + 1], iw = idx[4 * i + 2], ic = idx[4 * i + 3];
+        double acc = 0.0;
+        for (i64 oc = 0; oc < OC; ++oc)
+            for (i64 kh = 0; kh < KH; ++kh) {
+                i64 th = ih + ph - kh;
+                if (th < 0 || th % sh != 0 || th / sh >= OH) continue;
+                for (i64 kw = 0; kw < KW; ++kw) {
+                    i64 tw = iw + pw - kw;
+                    if (tw < 0 || tw % sw != 0 || tw / sw >= OW) continue;
+                    acc += w[((oc * KH + kh) * KW + kw) * IC + ic] *
+                           dz[((n * OH + th / sh) * OW + tw / sw) * OC + oc];
+                }
+            }
+        out[i] = acc;
+    }
+}
+
+/* ---------------------------------------------------------------- a6 dW, db ---- */
+/* dw[oc,kh,kw,ic] = sum_{n,oh,ow} dz[n,oh,ow,oc] * x[n, oh*sh-ph+kh, ow*sw-pw+kw, ic]
+ * (out-of-range taps contribute zero);  db[oc] = sum_{n,oh,ow} dz[n,oh,ow,oc].
+ * Written, not accumulated.  [generic] backward (weight and bias accumulators);
+ * [wgsl] conv2d_backward_weight (per-element sum over output positions); [cuda]
+ * bias_backward_partial/finalize.  db may be NULL. */
+void oracle_conv2d_backward_weight(const double* x, const double* dz, double* dw, double* db,
+                                   i64 N, i64 H, i64 W, i64 IC, i64 OC, i64 KH, i64 KW,
+                                   i64 sh, i64 sw, i64 ph, i64 pw) {
+    i64 OH = oracle_out_extent(H, KH, sh, ph), OW = oracle_out_extent(W, KW, sw, pw);
+    i64 K = KH * KW * IC;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i64 oc = 0; oc < OC; ++oc) {
+        double* row = dw + oc * K;
+        for (i64 k = 0; k < K; ++k) row[k] = 0.0;
+        double bsum = 0.0;
+        for (i64 n = 0; n < N; ++n)
+            for (i64 oh = 0; oh < OH; ++oh)
+                for (i64 ow = 0; ow < OW; ++ow) {
+                    double g = dz[((n * OH + oh) * OW + ow) * OC + oc];
+                    bsum += g;
+                    for (i64 kh = 0; kh < KH; ++kh) {
+                        i64 ih = oh * sh - ph + kh;
+                        if (ih < 0 || ih >= H) continue;
+                        for (i64 kw = 0; kw < KW; ++kw) {
+                            i64 iw = ow * sw - pw + kw;
+                            if (iw < 0 || iw >= W) continue;
+                            const double* xp = x + ((n * H + ih) * W + iw) * IC;
+                            double* rp = row + (kh * KW + kw) * IC;
+                            for (i64 ic = 0; ic < IC; ++ic) rp[ic] += g * xp[ic];
+                        }
+                    }
+                }
+        if (db) db[oc] = bsum;
+    }
+}
+
+/* One dw element (oc, kh, kw, ic), same definition. */
+void oracle_conv2d_backward_weight_at(const double* x, const double* dz, const i64* idx, i64 count,
+                                      double* out, i64 N, i64 H, i64 W, i64 IC, i64 OC, i64 KH, i64 KW,
+                                      i64 sh, i64 sw, i64 ph, i64 pw) {
+    i64 OH = oracle_out_extent(H, KH, sh, ph), OW = oracle_out_extent(W, KW, sw, pw);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i64 i = 0; i < count; ++i) {
+        i64 oc = idx[4 * i], kh = idx[4 * i + 1], kw = idx[4 * i + 2], ic = idx[4 * i + 3];
+        double acc = 0.0;
+        for (i64 n = 0; n < N; ++n)
+            for (i64 oh = 0; oh < OH; ++oh) {
+                i64 ih = oh * sh - ph + kh;
+                if (ih < 0 || ih >= H) continue;
+                for (i64 ow = 0; ow < OW; ++ow) {
+                    i64 iw = ow * sw - pw + kw;
+                    if (iw < 0 || iw >= W) continue;
+                    acc += dz[((n * OH + oh) * OW + ow) * OC + oc] * x[((n * H + ih) * W + iw) * IC + ic];
+                }
+            }
+        out[i] = acc;
+    }
+}
+
+/* db alone: db[oc] = sum over all rows of dz. */
+void oracle_bias_grad(const double* dz, i64 M, i64 C, double* db) {
+#pragma omp parallel for schedule(static)
+    for (i64 c = 0; c < C; ++c) {
+        double s = 0.0;
+        for (i64 m = 0; m < M; ++m) s += dz[m * C + c];
+        db[c] = s;
+    }
+}
