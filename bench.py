@@ -1,0 +1,222 @@
+"""Benchmark of the conv2d training layer on one MI355X.
+
+A step is one pass of the layer's hot path over one batch of seeded synthetic input:
+conv2d_forward (conv + bias + activation, z and y written), activation_backward, dX
+(conv2d_backward_data) and dW + db (conv2d_backward_weight), on the wide bf16 layer
+N=64, 56x56x128 -> 128, 3x3 s1 p1, bias + tanh (fp32 accumulate).  The headline value
+is (forward + dX + dW flops) / step time in TFLOP/s.  Batch-norm statistics GB/s are
+measured on the conv + batch-norm layer (fp32, N=128, 32x32x64 -> 64) in the same run.
+
+Per-call durations come from HIP events recorded on the stream the library launches on
+(torch's current stream) around every call of the timed steps.  The fp64 oracle is
+timed on a bounded sample of the same layer on the host cores (cpu_baseline).
+
+Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a message.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as WL  # noqa: E402
+
+PEAK_TFLOPS = {WL.BF16: 2516.6, WL.F32: 157.3}  # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+METRIC = "conv2d fwd+dX+dW TFLOP/s and % MFMA peak; BN-stats GB/s (1 MI355X)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Device buffers and the four library calls of one training step."""
+
+    def __init__(self, wl: WL.Workload, dz_from_act_bwd=True):
+        import torch
+
+        import convolution_layer_amd as cm
+        from tests import gpu_harness as G
+        self.cm, self.G, self.wl = cm, G, wl
+        s, dt = wl.shape, wl.dtype
+        d = WL.make_inputs(wl)
+        self.desc = G.desc_for(wl)
+        dev = lambda a, t=None: G.dev(a, t)
+        self.x, self.w = dev(d["x"], dt), dev(d["w"], dt)
+        self.b = dev(d.get("b"))
+        self.dy = dev(d["dy"], dt)
+        self.bn = wl.norm == WL.NORM_BATCH
+        self.gamma, self.beta = dev(d.get("gamma")), dev(d.get("beta"))
+        self.rm, self.rv = dev(d.get("running_mean")), dev(d.get("running_var"))
+        tdt = G.tdtype(dt)
+        self.z = torch.empty(s.y_shape, dtype=tdt, device="cuda")
+        self.y = torch.empty(s.y_shape, dtype=tdt, device="cuda")
+        self.dz = torch.empty(s.y_shape, dtype=tdt, device="cuda")
+        self.dx = torch.empty(s.x_shape, dtype=tdt, device="cuda")
+        self.dw = torch.empty(s.w_shape, dtype=torch.float32, device="cuda")
+        self.db = torch.empty(s.OC, dtype=torch.float32, device="cuda")
+        f32 = lambda: torch.empty(s.OC, dtype=torch.float32, device="cuda")
+        self.sm, self.si, self.dg, self.dbt = (f32(), f32(), f32(), f32()) if self.bn else (None,) * 4
+        n = max(cm.workspace_size(self.desc, op) for op in range(5))
+        self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+
+    def forward(self):
+        self.cm.conv2d_forward(self.desc, self.x, self.w, self.b, self.gamma, self.beta, self.rm, self.rv,
+                               self.sm, self.si, self.z, self.y, self.ws)
+
+    def act_bwd(self):
+        self.cm.activation_backward(self.desc, self.z, self.dy, self.gamma, self.beta, self.sm, self.si, self.dz,
+                                    self.dg, self.dbt, 0, self.ws)
+
+    def bwd_data(self):
+        self.cm.conv2d_backward_data(self.desc, self.dz, self.w, self.dx, self.ws)
+
+    def bwd_weight(self):
+        self.cm.conv2d_backward_weight(self.desc, self.x, self.dz, self.dw, self.db, 0, self.ws)
+
+    def bn_stats(self):
+        self.cm.bn_stats_training(self.desc, self.z, self.sm, self.si, None, None, self.ws)
+
+    def calls(self):
+        return [("forward", self.forward), ("activation_backward", self.act_bwd),
+                ("backward_data", self.bwd_data), ("backward_weight", self.bwd_weight)]
+
+
+def timed_steps(layer, steps, warmup):
+    """Run warmup + timed steps; returns (total seconds, {call: mean ms})."""
+    import torch
+    calls = layer.calls()
+    for _ in range(warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    ev = {name: [] for name, _ in calls}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for name, f in calls:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in v])) for name, v in ev.items()}
+    return total, ms
+
+
+def time_call(f, reps):
+    import torch
+    f()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        f()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+
+def cpu_baseline(wl: WL.Workload, n_images: int):
+    """The fp64 oracle, untuned, on n_images of the workload's batch: forward,
+    activation backward, dX and dW.  Returns (TFLOP/s, seconds, threads)."""
+    import oracle as O
+    sub = wl.with_batch(n_images)
+    s = sub.shape
+    d = WL.make_inputs(sub)
+    st, pd = (s.sh, s.sw), (s.ph, s.pw)
+    t0 = time.perf_counter()
+    z = O.conv2d_forward(d["x"], d["w"], d.get("b"), st, pd)
+    O.apply_activation(z, wl.act)
+    dz, _, _ = O.activation_backward(z, d["dy"], wl.act)
+    O.conv2d_backward_data(dz, d["w"], s.x_shape, st, pd)
+    O.conv2d_backward_weight(d["x"], dz, s.w_shape, st, pd)
+    sec = time.perf_counter() - t0
+    return 3 * s.flops() / sec / 1e12, sec, O.num_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", choices=sorted(WL.WORKLOADS))
+    ap.add_argument("--cpu-images", type=int, default=2, help="images of the batch the oracle baseline runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    wl = WL.WORKLOADS[args.workload]
+    s = wl.shape
+    log(f"bench: workload {wl.name} ({wl.note}); building inputs")
+    layer = Layer(wl)
+    log("bench: timing steps")
+    total, ms = timed_steps(layer, args.steps, args.warmup)
+    step_ms = total / args.steps * 1e3
+    flops = 3 * s.flops()
+    value = flops / (total / args.steps) / 1e12
+    log(f"bench: step {step_ms:.3f} ms; per call ms {ms}")
+
+    # dominant kernel: the convolution call with the longest mean duration
+    conv_calls = {k: v for k, v in ms.items() if k in ("forward", "backward_data", "backward_weight")}
+    dom = max(conv_calls, key=conv_calls.get)
+    achieved = s.flops() / (conv_calls[dom] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    roofline = {"bound": "mfma", "kernel": f"conv2d_{dom}", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "per_call_ms": {k: round(v, 4) for k, v in ms.items()},
+                "per_call_tflops": {k: round(s.flops() / (v * 1e-3) / 1e12, 2) for k, v in conv_calls.items()}}
+
+    # batch-norm statistics bandwidth on the conv + batch-norm layer
+    del layer
+    torch.cuda.empty_cache()
+    bn_wl = WL.WORKLOADS["c3"]
+    bn_layer = Layer(bn_wl)
+    bn_layer.forward()
+    bn_ms = time_call(bn_layer.bn_stats, 50)
+    zbytes = bn_wl.shape.P * bn_wl.shape.OC * 4
+    bn_gbs = zbytes / (bn_ms * 1e-3) / 1e9
+    bn = {"workload": "c3", "bytes": zbytes, "ms": round(bn_ms, 5), "GB/s": round(bn_gbs, 1),
+          "frac": round(bn_gbs / PEAK_HBM_GBS, 4)}
+    log(f"bench: bn_stats {bn}")
+    del bn_layer
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"bench: cpu baseline (oracle, {args.cpu_images} images)")
+        tf, sec, thr = cpu_baseline(wl, args.cpu_images)
+        cpu = {"value": round(tf, 6), "unit": "TFLOP/s", "cores": thr, "kind": "oracle",
+               "sample": f"{wl.name} with N={args.cpu_images} of {s.N} images: fwd + act bwd + dX + dW, "
+                         f"fp64, {sec:.1f} s"}
+
+    line = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == WL.BF16 else "f32",
+            "data": "synthetic",
+            "config": {"workload": f"{wl.name}: {wl.note}", "N": s.N, "H": s.H, "W": s.W, "IC": s.IC,
+                       "OC": s.OC, "kernel": f"{s.KH}x{s.KW}", "stride": s.sh, "pad": s.ph,
+                       "step": "forward + activation_backward + backward_data + backward_weight",
+                       "flops_per_step": flops},
+            "mfma_peak_frac": round(value / peak, 4),
+            "roofline": roofline, "bn_stats": bn, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

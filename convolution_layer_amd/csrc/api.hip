@@ -1,0 +1,317 @@
+// api.hip -- the extern "C" entry points of include/convmi.h: argument checking, kernel
+// selection and launch.  No allocation, no synchronisation: every kernel goes on the
+// caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/convmi.h"
+#include "internal.hpp"
+
+using namespace convmi;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+convmi_status fail(convmi_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+convmi_status hip_fail(hipError_t e, const char* where) {
+    return fail(CONVMI_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kI32Max = 2147483647LL;
+
+int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p) {
+    int64_t span = in + 2 * p - k;
+    return span < 0 ? 0 : span / s + 1;
+}
+
+// Validate a descriptor; fills kernel dims.  `need_bn_params` checks momentum/eps.
+convmi_status check_desc(const convmi_desc* d, ConvDims* out) {
+    if (!d) return fail(CONVMI_ERR_INVALID_ARG, "desc is NULL");
+    if (d->N < 1 || d->H < 1 || d->W < 1 || d->IC < 1 || d->OC < 1 || d->KH < 1 || d->KW < 1)
+        return fail(CONVMI_ERR_INVALID_ARG, "sizes must be >= 1 (N=%lld H=%lld W=%lld IC=%lld OC=%lld KH=%lld KW=%lld)",
+                    (long long)d->N, (long long)d->H, (long long)d->W, (long long)d->IC, (long long)d->OC,
+                    (long long)d->KH, (long long)d->KW);
+    if (d->stride_h < 1 || d->stride_w < 1) return fail(CONVMI_ERR_INVALID_ARG, "strides must be >= 1");
+    if (d->pad_h < 0 || d->pad_w < 0) return fail(CONVMI_ERR_INVALID_ARG, "padding must be >= 0");
+    if (d->dtype != CONVMI_F32 && d->dtype != CONVMI_BF16)
+        return fail(CONVMI_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+    if (d->activation < CONVMI_ACT_IDENTITY || d->activation > CONVMI_ACT_SIGMOID)
+        return fail(CONVMI_ERR_INVALID_ARG, "unknown activation %d", d->activation);
+    if (d->normalization != CONVMI_NORM_NONE && d->normalization != CONVMI_NORM_BATCH)
+        return fail(CONVMI_ERR_INVALID_ARG, "unknown normalization %d", d->normalization);
+    if (d->mode == CONVMI_MODE_EVAL)
+        return fail(CONVMI_ERR_UNSUPPORTED, "evaluation mode (running statistics) is not implemented");
+    if (d->mode != CONVMI_MODE_TRAIN) return fail(CONVMI_ERR_INVALID_ARG, "unknown mode %d", d->mode);
+    if (d->normalization == CONVMI_NORM_BATCH) {
+        if (!(d->momentum >= 0.0f && d->momentum <= 1.0f))
+            return fail(CONVMI_ERR_INVALID_ARG, "momentum must be in [0, 1]");
+        if (!(d->eps > 0.0f)) return fail(CONVMI_ERR_INVALID_ARG, "eps must be > 0");
+    }
+    const int64_t OH = out_extent(d->H, d->KH, d->stride_h, d->pad_h);
+    const int64_t OW = out_extent(d->W, d->KW, d->stride_w, d->pad_w);
+    if (OH < 1 || OW < 1)
+        return fail(CONVMI_ERR_INVALID_ARG, "kernel %lldx%lld does not fit the padded %lldx%lld input",
+                    (long long)d->KH, (long long)d->KW, (long long)d->H, (long long)d->W);
+    // Index arithmetic inside the kernels is int32 per image and for N*OH*OW rows.
+    if (d->H * d->W * d->IC > kI32Max || OH * OW * d->OC > kI32Max || d->N * OH * OW > kI32Max ||
+        d->N * d->H * d->W > kI32Max || d->OC * d->KH * d->KW * d->IC > kI32Max ||
+        d->stride_h > 65535 || d->stride_w > 65535 || d->pad_h > 65535 || d->pad_w > 65535 ||
+        d->H > kI32Max / 4 || d->W > kI32Max / 4)
+        return fail(CONVMI_ERR_UNSUPPORTED, "problem exceeds the int32 index limits of this build");
+    if (out) {
+        *out = ConvDims{(int)d->N, (int)d->H, (int)d->W, (int)d->IC, (int)d->OC, (int)d->KH, (int)d->KW,
+                        d->stride_h, d->stride_w, d->pad_h, d->pad_w, (int)OH, (int)OW};
+    }
+    return CONVMI_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+convmi_status need(const void* p, const char* name) {
+    if (!p) return fail(CONVMI_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(CONVMI_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+    return CONVMI_OK;
+}
+
+convmi_status need_vec(const float* p, const char* name) {
+    if (!p) return fail(CONVMI_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, 4)) return fail(CONVMI_ERR_MISALIGNED, "%s is not 4-byte aligned", name);
+    return CONVMI_OK;
+}
+
+convmi_status check_ws(void* ws, size_t have, size_t want, const char* op) {
+    if (want == 0) return CONVMI_OK;
+    if (have < want || !ws)
+        return fail(CONVMI_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu%s", op, want, have,
+                    ws ? "" : " (NULL)");
+    if (!aligned(ws, 256)) return fail(CONVMI_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+    return CONVMI_OK;
+}
+
+#define CHECK(expr)                        \
+    do {                                   \
+        convmi_status _st = (expr);        \
+        if (_st != CONVMI_OK) return _st;  \
+    } while (0)
+
+int64_t rows_of(const ConvDims& d) { return (int64_t)d.N * d.OH * d.OW; }
+
+size_t ws_forward(const convmi_desc* desc, const ConvDims& d) {
+    size_t a = igemm_fwd_supported(desc->dtype, d) ? igemm_fwd_ws_bytes(desc->dtype, d) : 0;
+    size_t b = desc->normalization == CONVMI_NORM_BATCH ? bn_stats_ws_bytes(rows_of(d), d.OC, desc->dtype) : 0;
+    return a > b ? a : b;
+}
+size_t ws_backward_data(const convmi_desc* desc, const ConvDims& d) {
+    return igemm_dx_supported(desc->dtype, d) ? igemm_dx_ws_bytes(desc->dtype, d) : 0;
+}
+size_t ws_backward_weight(const convmi_desc* desc, const ConvDims& d) {
+    return igemm_dw_supported(desc->dtype, d) ? igemm_dw_ws_bytes(desc->dtype, d) : 0;
+}
+size_t ws_bn_stats(const convmi_desc* desc, const ConvDims& d) {
+    return bn_stats_ws_bytes(rows_of(d), d.OC, desc->dtype);
+}
+size_t ws_act_bwd(const convmi_desc* desc, const ConvDims& d) {
+    return desc->normalization == CONVMI_NORM_BATCH ? bn_bwd_ws_bytes(rows_of(d), d.OC, desc->dtype) : 0;
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+}  // namespace
+
+#define CONVMI_API __attribute__((visibility("default")))
+
+extern "C" {
+
+CONVMI_API const char* convmi_last_error(void) { return g_last_error.c_str(); }
+
+CONVMI_API const char* convmi_version(void) { return "convmi 0.1 (gfx950)"; }
+
+CONVMI_API convmi_status convmi_output_dims(const convmi_desc* desc, int64_t* OH, int64_t* OW) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    if (!OH || !OW) return fail(CONVMI_ERR_INVALID_ARG, "OH/OW out-pointers are NULL");
+    *OH = d.OH;
+    *OW = d.OW;
+    return CONVMI_OK;
+}
+
+CONVMI_API convmi_status convmi_workspace_size(const convmi_desc* desc, int32_t op, size_t* bytes) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    if (!bytes) return fail(CONVMI_ERR_INVALID_ARG, "bytes out-pointer is NULL");
+    switch (op) {
+    case CONVMI_OP_FORWARD: *bytes = ws_forward(desc, d); break;
+    case CONVMI_OP_BACKWARD_DATA: *bytes = ws_backward_data(desc, d); break;
+    case CONVMI_OP_BACKWARD_WEIGHT: *bytes = ws_backward_weight(desc, d); break;
+    case CONVMI_OP_BN_STATS: *bytes = ws_bn_stats(desc, d); break;
+    case CONVMI_OP_ACTIVATION_BACKWARD: *bytes = ws_act_bwd(desc, d); break;
+    default: return fail(CONVMI_ERR_INVALID_ARG, "unknown op %d", op);
+    }
+    return CONVMI_OK;
+}
+
+CONVMI_API convmi_status conv2d_forward(const convmi_desc* desc, const void* x, const void* w, const float* bias,
+                             const float* gamma, const float* beta, float* running_mean, float* running_var,
+                             float* save_mean, float* save_inv_std, void* z, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    CHECK(need(x, "x"));
+    CHECK(need(w, "w"));
+    CHECK(need(y, "y"));
+    if (bias) CHECK(need_vec(bias, "bias"));
+    const bool bn = desc->normalization == CONVMI_NORM_BATCH;
+    const size_t es = dtype_size(desc->dtype);
+    const size_t ybytes = (size_t)rows_of(d) * d.OC * es;
+    if (bn) {
+        CHECK(need(z, "z (required with batch norm)"));
+        CHECK(need_vec(gamma, "gamma"));
+        CHECK(need_vec(beta, "beta"));
+        CHECK(need_vec(save_mean, "save_mean"));
+        CHECK(need_vec(save_inv_std, "save_inv_std"));
+        if ((running_mean == nullptr) != (running_var == nullptr))
+            return fail(CONVMI_ERR_INVALID_ARG, "running_mean and running_var must be both given or both NULL");
+        if (running_mean) {
+            CHECK(need_vec(running_mean, "running_mean"));
+            CHECK(need_vec(running_var, "running_var"));
+        }
+    } else if (z) {
+        CHECK(need(z, "z"));
+    }
+    if (z && z == y) return fail(CONVMI_ERR_INVALID_ARG, "z and y must be distinct buffers");
+    if (overlaps(y, ybytes, x, (size_t)d.N * d.H * d.W * d.IC * es) || overlaps(z, ybytes, x, (size_t)d.N * d.H * d.W * d.IC * es))
+        return fail(CONVMI_ERR_INVALID_ARG, "outputs overlap x");
+    CHECK(check_ws(workspace, workspace_bytes, ws_forward(desc, d), "conv2d_forward"));
+    hipStream_t s = (hipStream_t)stream;
+    const int act = desc->activation;
+    hipError_t e;
+    // Without batch norm the activation is fused into the convolution's epilogue.
+    void* conv_y = bn ? nullptr : y;
+    if (igemm_fwd_supported(desc->dtype, d))
+        e = launch_igemm_fwd(desc->dtype, x, w, bias, z, conv_y, d, act, workspace, s);
+    else
+        e = launch_conv_fwd_direct(desc->dtype, x, w, bias, z, conv_y, d, act, s);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_forward: convolution launch");
+    if (bn) {
+        e = launch_bn_stats(desc->dtype, z, rows_of(d), d.OC, desc->momentum, desc->eps, save_mean, save_inv_std,
+                            running_mean, running_var, workspace, s);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: batch-norm statistics launch");
+        e = launch_apply_act(desc->dtype, z, y, rows_of(d), d.OC, act, 1, gamma, beta, save_mean, save_inv_std, s);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: normalise/activate launch");
+    }
+    return CONVMI_OK;
+}
+
+CONVMI_API convmi_status conv2d_backward_data(const convmi_desc* desc, const void* dz, const void* w, void* dx,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    CHECK(need(dz, "dz"));
+    CHECK(need(w, "w"));
+    CHECK(need(dx, "dx"));
+    const size_t es = dtype_size(desc->dtype);
+    const size_t dxb = (size_t)d.N * d.H * d.W * d.IC * es;
+    if (overlaps(dx, dxb, dz, (size_t)rows_of(d) * d.OC * es) || overlaps(dx, dxb, w, (size_t)d.OC * d.KH * d.KW * d.IC * es))
+        return fail(CONVMI_ERR_INVALID_ARG, "dx overlaps an input");
+    CHECK(check_ws(workspace, workspace_bytes, ws_backward_data(desc, d), "conv2d_backward_data"));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = igemm_dx_supported(desc->dtype, d)
+                       ? launch_igemm_dx(desc->dtype, dz, w, dx, d, workspace, s)
+                       : launch_conv_dx_direct(desc->dtype, dz, w, dx, d, s);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_backward_data launch");
+    return CONVMI_OK;
+}
+
+CONVMI_API convmi_status conv2d_backward_weight(const convmi_desc* desc, const void* x, const void* dz, float* dw,
+                                     float* db, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    CHECK(need(x, "x"));
+    CHECK(need(dz, "dz"));
+    CHECK(need(dw, "dw"));
+    if (db) CHECK(need_vec(db, "db"));
+    if (accumulate != 0 && accumulate != 1) return fail(CONVMI_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    CHECK(check_ws(workspace, workspace_bytes, ws_backward_weight(desc, d), "conv2d_backward_weight"));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = igemm_dw_supported(desc->dtype, d)
+                       ? launch_igemm_dw(desc->dtype, x, dz, dw, db, accumulate, d, workspace, s)
+                       : launch_conv_dw_direct(desc->dtype, x, dz, dw, db, accumulate, d, s);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_backward_weight launch");
+    return CONVMI_OK;
+}
+
+CONVMI_API convmi_status bn_stats_training(const convmi_desc* desc, const void* z, float* save_mean, float* save_inv_std,
+                                float* running_mean, float* running_var,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    if (desc->normalization != CONVMI_NORM_BATCH)
+        return fail(CONVMI_ERR_INVALID_ARG, "bn_stats_training needs normalization = BATCH");
+    CHECK(need(z, "z"));
+    CHECK(need_vec(save_mean, "save_mean"));
+    CHECK(need_vec(save_inv_std, "save_inv_std"));
+    if ((running_mean == nullptr) != (running_var == nullptr))
+        return fail(CONVMI_ERR_INVALID_ARG, "running_mean and running_var must be both given or both NULL");
+    if (running_mean) {
+        CHECK(need_vec(running_mean, "running_mean"));
+        CHECK(need_vec(running_var, "running_var"));
+    }
+    CHECK(check_ws(workspace, workspace_bytes, ws_bn_stats(desc, d), "bn_stats_training"));
+    hipError_t e = launch_bn_stats(desc->dtype, z, rows_of(d), d.OC, desc->momentum, desc->eps, save_mean,
+                                   save_inv_std, running_mean, running_var, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "bn_stats_training launch");
+    return CONVMI_OK;
+}
+
+CONVMI_API convmi_status activation_backward(const convmi_desc* desc, const void* z, const void* dy,
+                                  const float* gamma, const float* beta,
+                                  const float* save_mean, const float* save_inv_std,
+                                  void* dz, float* dgamma, float* dbeta, int32_t accumulate,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    CHECK(need(z, "z"));
+    CHECK(need(dy, "dy"));
+    CHECK(need(dz, "dz"));
+    if (accumulate != 0 && accumulate != 1) return fail(CONVMI_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    const size_t bytes = (size_t)rows_of(d) * d.OC * dtype_size(desc->dtype);
+    if (dz != dy && overlaps(dz, bytes, dy, bytes)) return fail(CONVMI_ERR_INVALID_ARG, "dz partially overlaps dy");
+    if (overlaps(dz, bytes, z, bytes)) return fail(CONVMI_ERR_INVALID_ARG, "dz overlaps z");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (desc->normalization == CONVMI_NORM_BATCH) {
+        CHECK(need_vec(gamma, "gamma"));
+        CHECK(need_vec(beta, "beta"));
+        CHECK(need_vec(save_mean, "save_mean"));
+        CHECK(need_vec(save_inv_std, "save_inv_std"));
+        if (dgamma) CHECK(need_vec(dgamma, "dgamma"));
+        if (dbeta) CHECK(need_vec(dbeta, "dbeta"));
+        CHECK(check_ws(workspace, workspace_bytes, ws_act_bwd(desc, d), "activation_backward"));
+        e = launch_bn_bwd(desc->dtype, z, dy, dz, rows_of(d), d.OC, desc->activation, gamma, beta, save_mean,
+                          save_inv_std, dgamma, dbeta, accumulate, workspace, s);
+    } else {
+        e = launch_act_bwd(desc->dtype, z, dy, dz, rows_of(d), d.OC, desc->activation, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "activation_backward launch");
+    return CONVMI_OK;
+}
+
+}  // extern "C"

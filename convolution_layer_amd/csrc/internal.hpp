@@ -1,0 +1,76 @@
+// internal.hpp -- host-side interface between the C-ABI front end (api.hip) and the
+// kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace convmi {
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
+
+inline size_t dtype_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- direct kernels
+// General-shape kernels (any IC, stride, padding): one thread per output element.
+// They serve small layers and shapes the tiled MFMA kernels do not take.
+hipError_t launch_conv_fwd_direct(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
+                                  const ConvDims& d, int act, hipStream_t s);
+hipError_t launch_conv_dx_direct(int dt, const void* dz, const void* w, void* dx, const ConvDims& d,
+                                 hipStream_t s);
+hipError_t launch_conv_dw_direct(int dt, const void* x, const void* dz, float* dw, float* db, int accumulate,
+                                 const ConvDims& d, hipStream_t s);
+
+// ---------------------------------------------------------------- row reductions
+// Per-channel reductions over the M = N*OH*OW rows of a [M][C] tensor are split into
+// row slabs (one workgroup each) that write fp32 partials, then merged per channel in
+// a fixed order.  The plan depends only on (M, C, dtype), so the workspace size and the
+// summation order are reproducible.
+struct RowPlan {
+    int vec;              // elements per vector access (16 bytes, or 1 when C is not a multiple)
+    int tpr;              // threads per row slice
+    int rpi;              // rows per iteration of a workgroup
+    int chunks;           // channel slices (grid.y)
+    int64_t rows_per_block;
+    int blocks;           // row slabs (grid.x)
+};
+RowPlan row_plan(int64_t M, int C, int dt);
+size_t bn_stats_ws_bytes(int64_t M, int C, int dt);
+size_t bn_bwd_ws_bytes(int64_t M, int C, int dt);
+
+hipError_t launch_bn_stats(int dt, const void* z, int64_t M, int C, float momentum, float eps, float* mean,
+                           float* inv_std, float* run_mean, float* run_var, void* ws, hipStream_t s);
+// y = act(a), a = z (norm 0) or the batch-norm affine (norm 1).
+hipError_t launch_apply_act(int dt, const void* z, void* y, int64_t M, int C, int act, int norm,
+                            const float* gamma, const float* beta, const float* mean, const float* inv_std,
+                            hipStream_t s);
+// dz = act'(z) * dy (no norm).
+hipError_t launch_act_bwd(int dt, const void* z, const void* dy, void* dz, int64_t M, int C, int act,
+                          hipStream_t s);
+// Batch-norm training backward (+ activation derivative), dgamma/dbeta optional.
+hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_t M, int C, int act,
+                         const float* gamma, const float* beta, const float* mean, const float* inv_std,
+                         float* dgamma, float* dbeta, int accumulate, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- MFMA implicit GEMM
+// Returns false (and launches nothing) when the shape is outside what the tiled
+// kernels take; the caller then uses the direct kernels.
+bool igemm_fwd_supported(int dt, const ConvDims& d);
+bool igemm_dx_supported(int dt, const ConvDims& d);
+bool igemm_dw_supported(int dt, const ConvDims& d);
+size_t igemm_fwd_ws_bytes(int dt, const ConvDims& d);
+size_t igemm_dx_ws_bytes(int dt, const ConvDims& d);
+size_t igemm_dw_ws_bytes(int dt, const ConvDims& d);
+hipError_t launch_igemm_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
+                            const ConvDims& d, int act, void* ws, hipStream_t s);
+hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, const ConvDims& d, void* ws,
+                           hipStream_t s);
+hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, float* db, int accumulate,
+                           const ConvDims& d, void* ws, hipStream_t s);
+
+}  // namespace convmi

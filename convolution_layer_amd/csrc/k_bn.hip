@@ -1,0 +1,406 @@
+// k_bn.hip -- bandwidth-bound kernels of the conv2d training layer for gfx950:
+// batch-norm training statistics, normalise + activation, activation backward and the
+// batch-norm training backward.
+//
+// All tensors are [M][C] rows (M = N*OH*OW, channels fastest).  Instead of one
+// workgroup per channel reading a column with stride C (the layout of the
+// bn_stats_training / bn_training_backward kernels in the rl_tools conv2d CUDA
+// listing, "operations_cuda.h"), each workgroup streams a contiguous slab of rows with
+// 16-byte loads across all channels, keeps per-lane partial sums, merges its rows in
+// LDS in a fixed order and writes one partial per channel.  A second kernel merges the
+// slab partials per channel in fp64, in slab order.  Summation order therefore depends
+// only on the shape: results are bitwise reproducible.
+#include "internal.hpp"
+
+namespace convmi {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTargetBlocks = 1024;  // row slabs: 4 workgroups per CU over 256 CUs
+
+template <typename T, int VEC> struct Vec;
+template <> struct Vec<float, 4> {
+    using raw = float4;
+    static __device__ __forceinline__ void load(const float* p, float* v) {
+        float4 r = *(const float4*)p;
+        v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float* v) {
+        *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+template <> struct Vec<bf16, 8> {
+    static __device__ __forceinline__ void load(const bf16* p, float* v) {
+        uint4 r = *(const uint4*)p;
+        uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(u[j] << 16);
+            v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(bf16* p, const float* v) {
+        uint32_t u[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
+        *(uint4*)p = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+};
+template <typename T> struct Vec<T, 1> {
+    static __device__ __forceinline__ void load(const T* p, float* v) { v[0] = to_f32(*p); }
+    static __device__ __forceinline__ void store(T* p, const float* v) { *p = from_f32<T>(v[0]); }
+};
+
+// Fixed-order merge of `rpi` row groups held in red[r][lane_slot] (any rpi >= 1):
+// halve the count each step, adding the upper part onto the lower.  Result in red[0][*].
+__device__ __forceinline__ void merge_rows(float* red, int rpi, int width, int r, int slot, int nvals,
+                                           bool active) {
+    int n = rpi;
+    while (n > 1) {
+        int h = (n + 1) / 2;
+        if (active && r < n - h)
+            for (int j = 0; j < nvals; ++j) red[r * width + slot + j] += red[(r + h) * width + slot + j];
+        __syncthreads();
+        n = h;
+    }
+}
+
+// Per-slab sums over rows of (z - shift_c) and (z - shift_c)^2, shift_c = z[0][c]
+// (shifted sums keep E[z^2] - E[z]^2 free of cancellation when |mean| >> std).
+// part layout: [C][2][blocks] so the per-channel merge reads contiguously.
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void bn_stats_partials(const T* __restrict__ z, int64_t M, int C, int tpr,
+                                                              int rpi, int64_t rows_per_block,
+                                                              float* __restrict__ part) {
+    extern __shared__ float red[];  // [rpi][tpr*VEC*2]
+    const int t = threadIdx.x, cv = t % tpr, r = t / tpr;
+    const int c0 = (blockIdx.y * tpr + cv) * VEC;
+    const bool active = r < rpi && c0 < C;
+    const int64_t m0 = (int64_t)blockIdx.x * rows_per_block;
+    const int64_t m1 = m0 + rows_per_block < M ? m0 + rows_per_block : M;
+    float s1[VEC], s2[VEC], sh[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) s1[j] = s2[j] = 0.0f;
+    if (active) {
+        Vec<T, VEC>::load(z + c0, sh);
+        for (int64_t m = m0 + r; m < m1; m += rpi) {
+            float v[VEC];
+            Vec<T, VEC>::load(z + m * C + c0, v);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                float dd = v[j] - sh[j];
+                s1[j] += dd;
+                s2[j] = __builtin_fmaf(dd, dd, s2[j]);
+            }
+        }
+    }
+    const int width = tpr * VEC * 2, slot = cv * VEC * 2;
+    if (active)
+        for (int j = 0; j < VEC; ++j) {
+            red[r * width + slot + 2 * j] = s1[j];
+            red[r * width + slot + 2 * j + 1] = s2[j];
+        }
+    __syncthreads();
+    merge_rows(red, rpi, width, r, slot, VEC * 2, active);
+    if (active && r == 0)
+        for (int j = 0; j < VEC; ++j) {
+            int c = c0 + j;
+            part[((int64_t)c * 2 + 0) * gridDim.x + blockIdx.x] = red[slot + 2 * j];
+            part[((int64_t)c * 2 + 1) * gridDim.x + blockIdx.x] = red[slot + 2 * j + 1];
+        }
+}
+
+// Sum `n` partials starting at p (fp64, fixed order: thread-strided then tree).
+__device__ double block_sum_f64(const float* __restrict__ p, int n, double* red) {
+    double a = 0.0;
+    for (int i = threadIdx.x; i < n; i += kThreads) a += (double)p[i];
+    red[threadIdx.x] = a;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    double r = red[0];
+    __syncthreads();
+    return r;
+}
+
+// One workgroup per channel: merge slab partials; mean = shift + S1/M,
+// var = S2/M - (S1/M)^2 (biased, clamped at 0), inv_std = 1/sqrt(var + eps), running
+// statistics updated with momentum.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bn_stats_finalize(const float* __restrict__ part, int blocks,
+                                                              const T* __restrict__ z, int64_t M, float momentum,
+                                                              float eps, float* __restrict__ mean,
+                                                              float* __restrict__ inv_std,
+                                                              float* __restrict__ run_mean,
+                                                              float* __restrict__ run_var) {
+    __shared__ double red[kThreads];
+    const int c = blockIdx.x;
+    double S1 = block_sum_f64(part + (int64_t)c * 2 * blocks, blocks, red);
+    double S2 = block_sum_f64(part + ((int64_t)c * 2 + 1) * blocks, blocks, red);
+    if (threadIdx.x == 0) {
+        double d = S1 / (double)M;
+        double var = S2 / (double)M - d * d;
+        if (var < 0.0) var = 0.0;
+        double mu = (double)to_f32(z[c]) + d;
+        mean[c] = (float)mu;
+        inv_std[c] = (float)(1.0 / sqrt(var + (double)eps));
+        if (run_mean) {
+            run_mean[c] = (float)((1.0 - (double)momentum) * (double)run_mean[c] + (double)momentum * mu);
+            run_var[c] = (float)((1.0 - (double)momentum) * (double)run_var[c] + (double)momentum * var);
+        }
+    }
+}
+
+// y = act(a) with a = z or the batch-norm affine; grid-stride over 16-byte vectors.
+template <typename T, int VEC, int ACT, bool BN>
+__global__ __launch_bounds__(kThreads) void apply_act(const T* __restrict__ z, T* __restrict__ y, int64_t nvec, int C,
+                                                      const float* __restrict__ gamma,
+                                                      const float* __restrict__ beta,
+                                                      const float* __restrict__ mean,
+                                                      const float* __restrict__ inv_std) {
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads) {
+        float a[VEC];
+        Vec<T, VEC>::load(z + v * VEC, a);
+        const int c0 = (int)((v * VEC) % C);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            float in = a[j];
+            if constexpr (BN) {
+                float zh;
+                in = bn_affine(in, mean[c0 + j], inv_std[c0 + j], gamma[c0 + j], beta[c0 + j], &zh);
+            }
+            a[j] = act_fwd<ACT>(in);
+        }
+        Vec<T, VEC>::store(y + v * VEC, a);
+    }
+}
+
+// dz = act'(z) * dy, no norm.
+template <typename T, int VEC, int ACT>
+__global__ __launch_bounds__(kThreads) void act_bwd(const T* __restrict__ z, const T* dy, T* dz, int64_t nvec) {
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads) {
+        float a[VEC], g[VEC];
+        Vec<T, VEC>::load(z + v * VEC, a);
+        Vec<T, VEC>::load(dy + v * VEC, g);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) g[j] *= act_slope<ACT>(a[j]);
+        Vec<T, VEC>::store(dz + v * VEC, g);
+    }
+}
+
+// Batch-norm backward, pass 1: per-slab sums of dno and dno*zhat, where
+// zhat = (z-mean)*inv_std, a = gamma*zhat + beta, dno = act'(a)*dy.
+template <typename T, int VEC, int ACT>
+__global__ __launch_bounds__(kThreads) void bn_bwd_partials(const T* __restrict__ z, const T* __restrict__ dy,
+                                                            int64_t M, int C, int tpr, int rpi,
+                                                            int64_t rows_per_block, const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta,
+                                                            const float* __restrict__ mean,
+                                                            const float* __restrict__ inv_std,
+                                                            float* __restrict__ part) {
+    extern __shared__ float red[];
+    const int t = threadIdx.x, cv = t % tpr, r = t / tpr;
+    const int c0 = (blockIdx.y * tpr + cv) * VEC;
+    const bool active = r < rpi && c0 < C;
+    const int64_t m0 = (int64_t)blockIdx.x * rows_per_block;
+    const int64_t m1 = m0 + rows_per_block < M ? m0 + rows_per_block : M;
+    float sa[VEC], sb[VEC], g[VEC], bt[VEC], mu[VEC], is[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) sa[j] = sb[j] = 0.0f;
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j]; mu[j] = mean[c0 + j]; is[j] = inv_std[c0 + j];
+        }
+        for (int64_t m = m0 + r; m < m1; m += rpi) {
+            float zv[VEC], gv[VEC];
+            Vec<T, VEC>::load(z + m * C + c0, zv);
+            Vec<T, VEC>::load(dy + m * C + c0, gv);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                float zh, a = bn_affine(zv[j], mu[j], is[j], g[j], bt[j], &zh);
+                float dno = act_slope<ACT>(a) * gv[j];
+                sa[j] += dno;
+                sb[j] = __builtin_fmaf(dno, zh, sb[j]);
+            }
+        }
+    }
+    const int width = tpr * VEC * 2, slot = cv * VEC * 2;
+    if (active)
+        for (int j = 0; j < VEC; ++j) {
+            red[r * width + slot + 2 * j] = sa[j];
+            red[r * width + slot + 2 * j + 1] = sb[j];
+        }
+    __syncthreads();
+    merge_rows(red, rpi, width, r, slot, VEC * 2, active);
+    if (active && r == 0)
+        for (int j = 0; j < VEC; ++j) {
+            int c = c0 + j;
+            part[((int64_t)c * 2 + 0) * gridDim.x + blockIdx.x] = red[slot + 2 * j];
+            part[((int64_t)c * 2 + 1) * gridDim.x + blockIdx.x] = red[slot + 2 * j + 1];
+        }
+}
+
+// Pass 2: per channel A = sum dno, B = sum dno*zhat; dgamma (+)= B, dbeta (+)= A;
+// coefficients for dz = gamma*inv_std*(dno - A/M - zhat*B/M) into coef[c][3].
+__global__ __launch_bounds__(kThreads) void bn_bwd_finalize(const float* __restrict__ part, int blocks, int64_t M,
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ inv_std,
+                                                            float* __restrict__ dgamma, float* __restrict__ dbeta,
+                                                            int accumulate, float* __restrict__ coef) {
+    __shared__ double red[kThreads];
+    const int c = blockIdx.x;
+    double A = block_sum_f64(part + (int64_t)c * 2 * blocks, blocks, red);
+    double B = block_sum_f64(part + ((int64_t)c * 2 + 1) * blocks, blocks, red);
+    if (threadIdx.x == 0) {
+        if (dgamma) dgamma[c] = accumulate ? (float)((double)dgamma[c] + B) : (float)B;
+        if (dbeta) dbeta[c] = accumulate ? (float)((double)dbeta[c] + A) : (float)A;
+        coef[3 * c + 0] = gamma[c] * inv_std[c];
+        coef[3 * c + 1] = (float)(A / (double)M);
+        coef[3 * c + 2] = (float)(B / (double)M);
+    }
+}
+
+// Pass 3: dz = k0*(dno - k1 - zhat*k2) elementwise.
+template <typename T, int VEC, int ACT>
+__global__ __launch_bounds__(kThreads) void bn_bwd_apply(const T* __restrict__ z, const T* dy, T* dz, int64_t nvec,
+                                                         int C, const float* __restrict__ gamma,
+                                                         const float* __restrict__ beta,
+                                                         const float* __restrict__ mean,
+                                                         const float* __restrict__ inv_std,
+                                                         const float* __restrict__ coef) {
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads) {
+        float zv[VEC], gv[VEC];
+        Vec<T, VEC>::load(z + v * VEC, zv);
+        Vec<T, VEC>::load(dy + v * VEC, gv);
+        const int c0 = (int)((v * VEC) % C);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const int c = c0 + j;
+            float zh, a = bn_affine(zv[j], mean[c], inv_std[c], gamma[c], beta[c], &zh);
+            float dno = act_slope<ACT>(a) * gv[j];
+            gv[j] = coef[3 * c] * (dno - coef[3 * c + 1] - zh * coef[3 * c + 2]);
+        }
+        Vec<T, VEC>::store(dz + v * VEC, gv);
+    }
+}
+
+int elementwise_grid(int64_t nvec) {
+    int64_t g = ceil_div(nvec, kThreads * 4);  // ~4 vectors per thread
+    if (g < 1) g = 1;
+    if (g > 8192) g = 8192;
+    return (int)g;
+}
+
+size_t partial_bytes(const RowPlan& p, int C) { return align_up((size_t)C * 2 * p.blocks * sizeof(float), 256); }
+
+}  // namespace
+
+RowPlan row_plan(int64_t M, int C, int dt) {
+    RowPlan p;
+    const int full = dt == DT_BF16 ? 8 : 4;
+    p.vec = (C % full == 0) ? full : 1;
+    const int cv = C / p.vec;
+    p.tpr = cv < kThreads ? cv : kThreads;
+    p.rpi = kThreads / p.tpr;
+    p.chunks = (int)ceil_div(cv, p.tpr);
+    int64_t rpb = ceil_div(M, kTargetBlocks);
+    rpb = ceil_div(rpb, p.rpi) * p.rpi;
+    if (rpb < p.rpi) rpb = p.rpi;
+    p.rows_per_block = rpb;
+    p.blocks = (int)ceil_div(M, rpb);
+    return p;
+}
+
+size_t bn_stats_ws_bytes(int64_t M, int C, int dt) { return partial_bytes(row_plan(M, C, dt), C); }
+
+size_t bn_bwd_ws_bytes(int64_t M, int C, int dt) {
+    return partial_bytes(row_plan(M, C, dt), C) + align_up((size_t)C * 3 * sizeof(float), 256);
+}
+
+#define CONVMI_VEC_SWITCH(dt, vec, T, VEC, ...)                                  \
+    if (dt == DT_BF16) {                                                         \
+        using T = bf16;                                                          \
+        if (vec == 8) { constexpr int VEC = 8; __VA_ARGS__; }                    \
+        else { constexpr int VEC = 1; __VA_ARGS__; }                             \
+    } else {                                                                     \
+        using T = float;                                                         \
+        if (vec == 4) { constexpr int VEC = 4; __VA_ARGS__; }                    \
+        else { constexpr int VEC = 1; __VA_ARGS__; }                             \
+    }
+
+hipError_t launch_bn_stats(int dt, const void* z, int64_t M, int C, float momentum, float eps, float* mean,
+                           float* inv_std, float* run_mean, float* run_var, void* ws, hipStream_t s) {
+    RowPlan p = row_plan(M, C, dt);
+    float* part = (float*)ws;
+    dim3 grid(p.blocks, p.chunks), block(kThreads);
+    size_t lds = (size_t)p.rpi * p.tpr * p.vec * 2 * sizeof(float);
+    CONVMI_VEC_SWITCH(dt, p.vec, T, VEC,
+                      (bn_stats_partials<T, VEC><<<grid, block, lds, s>>>((const T*)z, M, C, p.tpr, p.rpi,
+                                                                          p.rows_per_block, part)));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (dt == DT_BF16)
+        bn_stats_finalize<bf16><<<C, kThreads, 0, s>>>(part, p.blocks, (const bf16*)z, M, momentum, eps, mean,
+                                                       inv_std, run_mean, run_var);
+    else
+        bn_stats_finalize<float><<<C, kThreads, 0, s>>>(part, p.blocks, (const float*)z, M, momentum, eps, mean,
+                                                        inv_std, run_mean, run_var);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply_act(int dt, const void* z, void* y, int64_t M, int C, int act, int norm,
+                            const float* gamma, const float* beta, const float* mean, const float* inv_std,
+                            hipStream_t s) {
+    const int full = dt == DT_BF16 ? 8 : 4;
+    const int vec = (C % full == 0) ? full : 1;
+    const int64_t nvec = M * C / vec;
+    dim3 grid(elementwise_grid(nvec)), block(kThreads);
+    CONVMI_VEC_SWITCH(dt, vec, T, VEC, CONVMI_ACT_SWITCH(act, A, {
+        if (norm)
+            apply_act<T, VEC, A, true><<<grid, block, 0, s>>>((const T*)z, (T*)y, nvec, C, gamma, beta, mean, inv_std);
+        else
+            apply_act<T, VEC, A, false><<<grid, block, 0, s>>>((const T*)z, (T*)y, nvec, C, gamma, beta, mean, inv_std);
+    }));
+    return hipGetLastError();
+}
+
+hipError_t launch_act_bwd(int dt, const void* z, const void* dy, void* dz, int64_t M, int C, int act,
+                          hipStream_t s) {
+    const int full = dt == DT_BF16 ? 8 : 4;
+    const int vec = (C % full == 0) ? full : 1;
+    const int64_t nvec = M * C / vec;
+    dim3 grid(elementwise_grid(nvec)), block(kThreads);
+    CONVMI_VEC_SWITCH(dt, vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (act_bwd<T, VEC, A><<<grid, block, 0, s>>>(
+                                                                   (const T*)z, (const T*)dy, (T*)dz, nvec))));
+    return hipGetLastError();
+}
+
+hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_t M, int C, int act,
+                         const float* gamma, const float* beta, const float* mean, const float* inv_std,
+                         float* dgamma, float* dbeta, int accumulate, void* ws, hipStream_t s) {
+    RowPlan p = row_plan(M, C, dt);
+    float* part = (float*)ws;
+    float* coef = (float*)((char*)ws + partial_bytes(p, C));
+    dim3 grid(p.blocks, p.chunks), block(kThreads);
+    size_t lds = (size_t)p.rpi * p.tpr * p.vec * 2 * sizeof(float);
+    CONVMI_VEC_SWITCH(dt, p.vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (bn_bwd_partials<T, VEC, A><<<grid, block, lds, s>>>(
+                                                                      (const T*)z, (const T*)dy, M, C, p.tpr, p.rpi,
+                                                                      p.rows_per_block, gamma, beta, mean, inv_std,
+                                                                      part))));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bn_bwd_finalize<<<C, kThreads, 0, s>>>(part, p.blocks, M, gamma, inv_std, dgamma, dbeta, accumulate, coef);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nvec = M * C / p.vec;
+    dim3 g2(elementwise_grid(nvec));
+    CONVMI_VEC_SWITCH(dt, p.vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (bn_bwd_apply<T, VEC, A><<<g2, block, 0, s>>>(
+                                                                      (const T*)z, (const T*)dy, (T*)dz, nvec, C,
+                                                                      gamma, beta, mean, inv_std, coef))));
+    return hipGetLastError();
+}
+
+}  // namespace convmi

@@ -1,0 +1,181 @@
+/*
+ * convmi.h -- C ABI of the MI355X (gfx950) conv2d training-layer library.
+ *
+ * One 2D convolution layer for training, NHWC activations and OHWI weights:
+ *   forward    z = conv(x, w) + b;  [batch norm: batch statistics, then
+ *              a = gamma*(z-mean)*inv_std + beta, else a = z];  y = act(a)
+ *   backward   dz = d act / d a * dy  (+ batch-norm training backward, dgamma, dbeta)
+ *              dx = conv^T(dz, w)     dw (+)= sum dz * x,  db (+)= sum dz
+ *
+ * Pages the operations come from (source listings; a function name stands in for a
+ * section):
+ *   [generic] "rl_tools/nn/layers/conv2d/operations_generic.h" (hyperray 0.0.1 wheel)
+ *   [cuda]    "rl_tools/nn/layers/conv2d/operations_cuda.h"    (hyperray 0.0.1 wheel)
+ *   [mkl]     "rl_tools/nn/layers/conv2d/operations_cpu_mkl.h" (hyperray 0.0.1 wheel)
+ *   [wgsl]    "conv2d_backward_weight.wgsl" (@simulatte/doppler 0.1.0)
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller (for example the
+ *     data_ptr() of torch tensors on the same GPU).  The library never allocates,
+ *     frees or synchronises: every kernel is enqueued on `stream` (a hipStream_t;
+ *     NULL means the default stream) and the call returns before the work is done.
+ *   - Layouts are dense and row-major, as the [cuda] listing requires of its inputs:
+ *       x, dx          [N][H][W][IC]
+ *       w              [OC][KH][KW][IC]
+ *       z, y, dy, dz   [N][OH][OW][OC],  OH = (H + 2*pad_h - KH)/stride_h + 1 (floor),
+ *                                          OW likewise
+ *       bias, gamma, beta, running_*, save_*, db, dgamma, dbeta   [OC]
+ *       dw             [OC][KH][KW][IC]
+ *   - Element type: x, w, z, y, dy, dz, dx are `desc->dtype` (fp32 or bf16, the latter
+ *     as raw IEEE bfloat16 bits).  bias, gamma, beta, running and saved statistics,
+ *     dw, db, dgamma, dbeta are always fp32.  Accumulation is fp32.
+ *   - Data tensors (x, w, z, y, dy, dz, dx, dw) must be 16-byte aligned; the workspace
+ *     must be 256-byte aligned.  Otherwise CONVMI_ERR_MISALIGNED.
+ *   - `workspace` is caller-owned device scratch of at least the size that
+ *     convmi_workspace_size() reports for the operation (may be NULL when that size
+ *     is 0).  Its contents on entry do not matter.  Too small: CONVMI_ERR_WORKSPACE.
+ *   - Every argument is checked on the host before any device work is enqueued; on a
+ *     non-OK status nothing has been enqueued, except CONVMI_ERR_HIP (a launch
+ *     failed).  convmi_last_error() then returns a message for the calling thread.
+ *   - Results are deterministic: the same inputs give bitwise identical outputs
+ *     (fixed-order reductions, no floating-point atomics; the [cuda] listing likewise
+ *     insists on deterministic backward algorithms).
+ *   - Output buffers must not overlap inputs, except dz == dy in activation_backward
+ *     (the pages apply the activation derivative in place).
+ */
+#ifndef CONVMI_H
+#define CONVMI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONVMI_OK = 0,
+    CONVMI_ERR_INVALID_ARG = 1, /* bad size, stride, pad, enum value, NULL pointer, aliasing */
+    CONVMI_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (e.g. eval mode) */
+    CONVMI_ERR_WORKSPACE = 3,   /* workspace smaller than convmi_workspace_size() */
+    CONVMI_ERR_MISALIGNED = 4,  /* a pointer violates the alignment rule above */
+    CONVMI_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+} convmi_status;
+
+typedef enum { CONVMI_F32 = 0, CONVMI_BF16 = 1 } convmi_dtype;
+
+/* The activation set of the [mkl] listing's post-op table: identity, relu, tanh,
+ * sigmoid.  relu'(0) is taken as 0. */
+typedef enum {
+    CONVMI_ACT_IDENTITY = 0,
+    CONVMI_ACT_RELU = 1,
+    CONVMI_ACT_TANH = 2,
+    CONVMI_ACT_SIGMOID = 3
+} convmi_act;
+
+typedef enum { CONVMI_NORM_NONE = 0, CONVMI_NORM_BATCH = 1 } convmi_norm;
+
+/* Only training mode is implemented; CONVMI_MODE_EVAL returns CONVMI_ERR_UNSUPPORTED. */
+typedef enum { CONVMI_MODE_TRAIN = 0, CONVMI_MODE_EVAL = 1 } convmi_mode;
+
+typedef enum {
+    CONVMI_OP_FORWARD = 0,
+    CONVMI_OP_BACKWARD_DATA = 1,
+    CONVMI_OP_BACKWARD_WEIGHT = 2,
+    CONVMI_OP_BN_STATS = 3,
+    CONVMI_OP_ACTIVATION_BACKWARD = 4
+} convmi_op;
+
+/* The layer's problem statement: the [generic] listing's compile-time layer spec
+ * (batch, input height/width/channels, output channels, kernel height/width, stride,
+ * padding, activation, normalisation, batch-norm momentum and epsilon), here as a
+ * runtime descriptor.  Padding is symmetric and zero-filled; the operation is a
+ * cross-correlation (the [cuda] descriptor uses CUDNN_CROSS_CORRELATION).
+ * Limits: all sizes >= 1, strides >= 1, pads >= 0, OH and OW >= 1, each tensor of one
+ * image below 2^31 elements, N*OH*OW below 2^31.  momentum in [0,1]; eps > 0 when
+ * normalization is BATCH. */
+typedef struct convmi_desc {
+    int64_t N, H, W, IC, OC, KH, KW;
+    int32_t stride_h, stride_w, pad_h, pad_w;
+    int32_t activation;    /* convmi_act */
+    int32_t normalization; /* convmi_norm */
+    int32_t mode;          /* convmi_mode */
+    int32_t dtype;         /* convmi_dtype */
+    float momentum;        /* running <- (1-momentum)*running + momentum*batch */
+    float eps;             /* inv_std = 1/sqrt(var + eps) */
+} convmi_desc;
+
+/* OH, OW for a descriptor (floor formula above).  Checks the descriptor. */
+convmi_status convmi_output_dims(const convmi_desc* desc, int64_t* OH, int64_t* OW);
+
+/* Bytes of workspace `op` needs for `desc` (0 is possible). */
+convmi_status convmi_workspace_size(const convmi_desc* desc, int32_t op, size_t* bytes);
+
+/* a1 + a2 + a3: convolution + bias, then (batch norm) training statistics and the
+ * normalise/affine step, then the activation.  [generic] forward (conv + bias into
+ * pre_activations; batch-norm training statistics; normalise + activate); [cuda]
+ * forward (conv, add bias, bn_stats_training, bn_forward_affine, activation).
+ *   x, w: inputs.  bias: fp32 [OC] or NULL (no bias).
+ *   gamma, beta, running_mean, running_var, save_mean, save_inv_std: batch norm only
+ *     (NULL otherwise).  running_* are updated in place with the biased batch variance
+ *     (as on the pages); save_mean / save_inv_std receive the batch mean and
+ *     1/sqrt(var+eps) for the backward pass.
+ *   z: pre-activation output (conv + bias).  Required with batch norm; may be NULL
+ *     without it.  y: the layer output act(a).  Both overwritten. */
+convmi_status conv2d_forward(const convmi_desc* desc, const void* x, const void* w, const float* bias,
+                             const float* gamma, const float* beta, float* running_mean, float* running_var,
+                             float* save_mean, float* save_inv_std, void* z, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* a5: dx[n,ih,iw,ic] = sum over (oc,kh,kw) with oh*stride_h - pad_h + kh == ih and
+ * ow*stride_w - pad_w + kw == iw of w[oc,kh,kw,ic] * dz[n,oh,ow,oc].  Linear in dz:
+ * the activation / batch-norm derivative is applied beforehand by
+ * activation_backward.  dx is overwritten.  [generic] backward_input (the scatter
+ * after the activation derivative); [cuda] backward_input (BackwardData, beta 0). */
+convmi_status conv2d_backward_data(const convmi_desc* desc, const void* dz, const void* w, void* dx,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* a6: dw[oc,kh,kw,ic] = sum_{n,oh,ow} dz[n,oh,ow,oc] * x[n, oh*sh-ph+kh, ow*sw-pw+kw, ic]
+ * (zero outside the image); db[oc] = sum_{n,oh,ow} dz[n,oh,ow,oc].  accumulate = 0
+ * overwrites dw/db, 1 adds into them (the pages accumulate parameter gradients).
+ * db may be NULL.  [generic] backward; [wgsl] conv2d_backward_weight; [cuda]
+ * BackwardFilter and bias_backward_partial/finalize. */
+convmi_status conv2d_backward_weight(const convmi_desc* desc, const void* x, const void* dz, float* dw,
+                                     float* db, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* a2: per-channel training statistics of z over the N*OH*OW rows: mean, biased var,
+ * save_inv_std = 1/sqrt(var+eps); running_mean/var (nullable, both or neither)
+ * updated with momentum.  [generic] forward, batch-norm training statistics; [cuda]
+ * bn_stats_training. */
+convmi_status bn_stats_training(const convmi_desc* desc, const void* z, float* save_mean, float* save_inv_std,
+                                float* running_mean, float* running_var,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* a4: activation backward, plus the batch-norm training backward when
+ * desc->normalization is BATCH.
+ *   No norm:   dz = act'(z) * dy.
+ *   Batch norm: zhat = (z-mean)*inv_std, a = gamma*zhat + beta, dno = act'(a)*dy,
+ *     per channel over M = N*OH*OW rows: S1 = sum dno*gamma, S2 = sum dno*gamma*zhat,
+ *     dz = inv_std/M * (M*dno*gamma - S1 - zhat*S2), dgamma (+)= sum dno*zhat,
+ *     dbeta (+)= sum dno.  gamma, beta, save_mean, save_inv_std are required and
+ *     dgamma, dbeta optional (NULL skips them); `accumulate` as for dw.
+ * dz may equal dy (in place).  [generic] backward_input / backward (training-mode
+ * two-phase normalisation backward); [cuda] activation_backward, bn_training_backward. */
+convmi_status activation_backward(const convmi_desc* desc, const void* z, const void* dy,
+                                  const float* gamma, const float* beta,
+                                  const float* save_mean, const float* save_inv_std,
+                                  void* dz, float* dgamma, float* dbeta, int32_t accumulate,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message describing the last non-OK status returned on the calling thread. */
+const char* convmi_last_error(void);
+
+/* Library version string. */
+const char* convmi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVMI_H */

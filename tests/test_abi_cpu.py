@@ -1,0 +1,159 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/convmi.h
+declares, computes output sizes and workspace sizes, and rejects bad arguments with the
+documented status before any device work (no GPU needed: argument checking happens on
+the host and returns before the first HIP call)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convmi.h")
+
+
+@pytest.fixture(scope="module")
+def cm():
+    import convolution_layer_amd as cm_
+    return cm_
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for n in ("conv2d_forward", "conv2d_backward_data", "conv2d_backward_weight", "bn_stats_training",
+              "activation_backward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(cm):
+    names = header_functions()
+    assert set(names) == set(cm.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", cm.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(cm.lib, n)
+    # nothing but the C ABI is exported
+    assert exported == set(names), exported - set(names)
+
+
+def test_version(cm):
+    assert "gfx950" in cm.version()
+
+
+@pytest.mark.parametrize("name", sorted(WL.WORKLOADS))
+def test_output_dims_match_workloads(cm, name):
+    wl = WL.WORKLOADS[name]
+    s = wl.shape
+    d = cm.make_desc(s.N, s.H, s.W, s.IC, s.OC, s.KH, s.KW, (s.sh, s.sw), (s.ph, s.pw), wl.act, wl.norm)
+    assert cm.output_dims(d) == (s.OH, s.OW)
+    for op in range(5):
+        n = cm.workspace_size(d, op)
+        assert n >= 0 and n % 256 == 0
+    if wl.norm == WL.NORM_BATCH:
+        assert cm.workspace_size(d, cm.OP_BN_STATS) > 0
+        assert cm.workspace_size(d, cm.OP_ACTIVATION_BACKWARD) > 0
+
+
+def _good(cm, **kw):
+    base = dict(N=2, H=8, W=8, IC=16, OC=16, KH=3, KW=3, stride=(1, 1), pad=(1, 1))
+    base.update(kw)
+    return cm.make_desc(base["N"], base["H"], base["W"], base["IC"], base["OC"], base["KH"], base["KW"],
+                        base["stride"], base["pad"], base.get("activation", 0), base.get("normalization", 0),
+                        base.get("mode", 0), base.get("dtype", 0), base.get("momentum", 0.1), base.get("eps", 1e-5))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 1), (dict(IC=-1), 1), (dict(KH=0), 1), (dict(stride=(0, 1)), 1), (dict(pad=(-1, 0)), 1),
+    (dict(KH=11, pad=(0, 0)), 1), (dict(dtype=7), 1), (dict(activation=9), 1), (dict(normalization=3), 1),
+    (dict(mode=1), 2), (dict(mode=5), 1), (dict(normalization=1, eps=0.0), 1),
+    (dict(normalization=1, momentum=1.5), 1), (dict(N=1 << 40), 2),
+])
+def test_bad_descriptor(cm, kw, status):
+    d = _good(cm, **kw)
+    oh, ow = C.c_int64(), C.c_int64()
+    st = cm.lib.convmi_output_dims(C.byref(d), C.byref(oh), C.byref(ow))
+    assert st == status, cm.lib.convmi_last_error()
+    assert cm.lib.convmi_last_error().decode()
+
+
+def test_null_desc(cm):
+    assert cm.lib.convmi_output_dims(None, None, None) == cm.ERR_INVALID_ARG
+
+
+# fake device addresses: argument checks run first, so these are never dereferenced
+A = 0x7F0000000000
+MIS = A + 4
+
+
+def test_forward_argument_checks(cm):
+    d = _good(cm)
+    f = cm.lib.conv2d_forward
+    ok = [C.byref(d), A, A + 0x100000, None, None, None, None, None, None, None, None, A + 0x200000, None, 0, None]
+    args = list(ok); args[1] = None
+    assert f(*args) == cm.ERR_INVALID_ARG  # x NULL
+    args = list(ok); args[2] = MIS
+    assert f(*args) == cm.ERR_MISALIGNED  # w misaligned
+    args = list(ok); args[11] = None
+    assert f(*args) == cm.ERR_INVALID_ARG  # y NULL
+    args = list(ok); args[10] = args[11]
+    assert f(*args) == cm.ERR_INVALID_ARG  # z == y
+    args = list(ok); args[11] = A
+    assert f(*args) == cm.ERR_INVALID_ARG  # y overlaps x
+    dbn = _good(cm, normalization=1)
+    args = list(ok); args[0] = C.byref(dbn)
+    assert f(*args) == cm.ERR_INVALID_ARG  # batch norm without z / gamma / ...
+    assert "z" in cm.lib.convmi_last_error().decode()
+
+
+def test_workspace_checks(cm):
+    d = _good(cm, normalization=1)
+    need = cm.workspace_size(d, cm.OP_BN_STATS)
+    assert need > 0
+    f = cm.lib.bn_stats_training
+    base = [C.byref(d), A, A + 0x1000, A + 0x2000, None, None]
+    assert f(*base, None, 0, None) == cm.ERR_WORKSPACE
+    assert f(*base, A + 0x10000, need - 1, None) == cm.ERR_WORKSPACE
+    assert f(*base, A + 0x10000 + 16, need, None) == cm.ERR_MISALIGNED
+    assert f(*base[:4], A + 0x3000, None, A + 0x10000, need, None) == cm.ERR_INVALID_ARG  # running pair
+    dn = _good(cm)
+    assert f(C.byref(dn), A, A + 0x1000, A + 0x2000, None, None, A + 0x10000, need, None) == cm.ERR_INVALID_ARG
+
+
+def test_backward_argument_checks(cm):
+    d = _good(cm)
+    assert cm.lib.conv2d_backward_data(C.byref(d), A, A + 0x100000, None, None, 0, None) == cm.ERR_INVALID_ARG
+    assert cm.lib.conv2d_backward_data(C.byref(d), A, A + 0x100000, A, None, 0, None) == cm.ERR_INVALID_ARG
+    assert cm.lib.conv2d_backward_weight(C.byref(d), A, A + 0x100000, A + 0x200000, None, 2, None, 0,
+                                         None) == cm.ERR_INVALID_ARG  # accumulate must be 0/1
+    assert cm.lib.conv2d_backward_weight(C.byref(d), A, MIS, A + 0x200000, None, 0, None, 0,
+                                         None) == cm.ERR_MISALIGNED
+    f = cm.lib.activation_backward
+    assert f(C.byref(d), A, A + 0x100000, None, None, None, None, A + 0x100000 + 16, None, None, 0, None, 0,
+             None) == cm.ERR_INVALID_ARG  # dz partially overlaps dy
+    dbn = _good(cm, normalization=1)
+    assert f(C.byref(dbn), A, A + 0x100000, None, None, None, None, A + 0x200000, None, None, 0, None, 0,
+             None) == cm.ERR_INVALID_ARG  # gamma missing
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The product path has no CPU fallback: a missing library is an ImportError."""
+    import importlib.util
+    src = os.path.join(ROOT, "convolution_layer_amd", "__init__.py")
+    pkg = tmp_path / "fakepkg"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("fakepkg", pkg / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)

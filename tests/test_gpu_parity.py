@@ -1,0 +1,351 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on the same
+seeded inputs.
+
+* Medium shapes (the oracle finishes in well under a second): every output element
+  compared, shapes chosen to span several tiles with ragged tails, odd channel counts,
+  strides, paddings, 1x1 and whole-image kernels, fp32 and bf16.
+* The workload configurations at full size, in the launch configuration the bench
+  times: full comparison where the oracle takes seconds, sampled outputs (random plus
+  every corner) where it would take longer.
+* Edge and contract cases: accumulate, in-place activation backward, determinism.
+
+Inputs always come from workloads.py or from the oracle; nothing computed by the
+library is fed to the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import convolution_layer_amd  # noqa: F401  (raises if the library is not built)
+
+
+ACTS = {WL.ACT_IDENTITY: "id", WL.ACT_RELU: "relu", WL.ACT_TANH: "tanh", WL.ACT_SIGMOID: "sigm"}
+
+# (N, H, W, IC, OC, KH, KW, sh, sw, ph, pw), dtype, activation
+MEDIUM = [
+    ((2, 13, 11, 8, 24, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_RELU),
+    ((3, 17, 19, 64, 64, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_RELU),
+    ((2, 15, 15, 128, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH),
+    ((2, 23, 23, 4, 32, 8, 8, 4, 4, 0, 0), WL.F32, WL.ACT_RELU),
+    ((4, 20, 20, 32, 64, 4, 4, 2, 2, 0, 0), WL.F32, WL.ACT_RELU),
+    ((4, 9, 9, 64, 64, 3, 3, 1, 1, 0, 0), WL.F32, WL.ACT_RELU),
+    ((1, 40, 37, 64, 64, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_IDENTITY),
+    ((2, 10, 12, 3, 8, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_RELU),
+    ((2, 9, 7, 5, 7, 2, 3, 2, 1, 1, 0), WL.F32, WL.ACT_SIGMOID),
+    ((2, 8, 8, 16, 40, 1, 1, 1, 1, 0, 0), WL.BF16, WL.ACT_RELU),
+    ((1, 7, 7, 8, 8, 7, 7, 1, 1, 0, 0), WL.F32, WL.ACT_IDENTITY),
+    ((2, 11, 11, 16, 16, 3, 3, 2, 2, 1, 1), WL.BF16, WL.ACT_SIGMOID),
+    ((3, 12, 10, 32, 96, 5, 5, 1, 1, 2, 2), WL.F32, WL.ACT_TANH),
+    ((2, 30, 30, 64, 32, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+]
+
+
+def _mid_id(case):
+    s, dt, act = case
+    return f"{'x'.join(map(str, s[:7]))}_s{s[7]}{s[8]}_p{s[9]}{s[10]}_{dt}_{ACTS[act]}"
+
+
+def _problem(case, seed):
+    s, dt, act = case
+    shape = WL.ConvShape(*s)
+    x = WL.random_tensor(shape.x_shape, dt, seed, ("normal", 0.0, 1.0))
+    w = WL.random_tensor(shape.w_shape, dt, seed + 1, ("normal", 0.0, (2.0 / shape.Kdim) ** 0.5))
+    b = WL.random_tensor((shape.OC,), WL.F32, seed + 2, ("uniform", -0.5, 0.5))
+    dy = WL.random_tensor(shape.y_shape, dt, seed + 3, ("normal", 0.0, 1.0))
+    return shape, dt, act, x, w, b, dy
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=_mid_id)
+def test_medium_forward(case):
+    shape, dt, act, x, w, b, _ = _problem(case, 10)
+    desc = G.shape_desc(shape, dt, act)
+    out = G.run_forward(desc, dt, G.dev(x, dt), G.dev(w, dt), G.dev(b))
+    z_r = O.conv2d_forward(x, w, b, (shape.sh, shape.sw), (shape.ph, shape.pw))
+    G.assert_close(G.host(out["z"]), z_r, dt, "z")
+    y_r = O.apply_activation(WL.round_to(dt, z_r), act)
+    G.assert_close(G.host(out["y"]), y_r, dt, "y")
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=_mid_id)
+def test_medium_backward_data(case):
+    shape, dt, act, x, w, b, dy = _problem(case, 20)
+    desc = G.shape_desc(shape, dt, act)
+    dx = G.run_backward_data(desc, dt, G.dev(dy, dt), G.dev(w, dt))
+    dx_r = O.conv2d_backward_data(dy, w, shape.x_shape, (shape.sh, shape.sw), (shape.ph, shape.pw))
+    G.assert_close(G.host(dx), dx_r, dt, "dx")
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=_mid_id)
+def test_medium_backward_weight(case):
+    shape, dt, act, x, w, b, dy = _problem(case, 30)
+    desc = G.shape_desc(shape, dt, act)
+    dw, db = G.run_backward_weight(desc, G.dev(x, dt), G.dev(dy, dt))
+    dw_r, db_r = O.conv2d_backward_weight(x, dy, shape.w_shape, (shape.sh, shape.sw), (shape.ph, shape.pw))
+    G.assert_close(G.host(dw), dw_r, WL.F32 if dt == WL.F32 else dt, "dw")
+    G.assert_close(G.host(db), db_r, WL.F32 if dt == WL.F32 else dt, "db")
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=_mid_id)
+def test_medium_activation_backward(case):
+    shape, dt, act, x, w, b, dy = _problem(case, 40)
+    z = WL.random_tensor(shape.y_shape, dt, 41, ("normal", 0.0, 2.0))
+    desc = G.shape_desc(shape, dt, act)
+    dz, _, _ = G.run_act_bwd(desc, dt, G.dev(z, dt), G.dev(dy, dt))
+    dz_r, _, _ = O.activation_backward(z, dy, act)
+    G.assert_close(G.host(dz), dz_r, dt, "dz")
+
+
+BN_MEDIUM = [
+    ((2, 13, 11, 64, 64, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_RELU),
+    ((3, 9, 10, 16, 24, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_SIGMOID),
+    ((2, 12, 12, 32, 40, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH),
+    ((2, 7, 9, 5, 6, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_IDENTITY),
+    ((1, 33, 35, 8, 300, 1, 1, 1, 1, 0, 0), WL.F32, WL.ACT_RELU),
+]
+
+
+@pytest.mark.parametrize("case", BN_MEDIUM, ids=_mid_id)
+def test_medium_batchnorm_layer(case):
+    """Forward with batch norm (z, batch statistics, running update, y) and the
+    batch-norm activation backward (dz, dgamma, dbeta), all against the oracle."""
+    shape, dt, act, x, w, b, dy = _problem(case, 50)
+    r = np.random.default_rng(51)
+    gamma = WL.round_to(WL.F32, r.uniform(0.5, 1.5, shape.OC))
+    beta = WL.round_to(WL.F32, r.normal(0.0, 0.1, shape.OC))
+    rm0 = WL.round_to(WL.F32, r.normal(0.0, 0.2, shape.OC))
+    rv0 = WL.round_to(WL.F32, r.uniform(0.5, 2.0, shape.OC))
+    mom, eps = 0.1, 1e-5
+    desc = G.shape_desc(shape, dt, act, WL.NORM_BATCH, mom, eps)
+    rm_d, rv_d = G.dev(rm0), G.dev(rv0)
+    out = G.run_forward(desc, dt, G.dev(x, dt), G.dev(w, dt), G.dev(b), G.dev(gamma), G.dev(beta), rm_d, rv_d)
+    z_r = O.conv2d_forward(x, w, b, (shape.sh, shape.sw), (shape.ph, shape.pw))
+    G.assert_close(G.host(out["z"]), z_r, dt, "z")
+    zs = WL.round_to(dt, z_r)
+    mean_r, var_r, inv_r, rm_r, rv_r = O.bn_stats(zs, mom, eps, rm0, rv0)
+    G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, eps, "fwd")
+    G.assert_close(G.host(rm_d), rm_r, WL.F32, "running_mean")
+    G.assert_close(G.host(rv_d), rv_r, WL.F32, "running_var")
+    y_r = O.apply_activation(zs, act, WL.NORM_BATCH, gamma, beta, mean_r, inv_r)
+    G.assert_close(G.host(out["y"]), y_r, dt, "y")
+    # backward on oracle-made inputs: z (rounded), statistics rounded to fp32
+    m32, i32 = WL.round_to(WL.F32, mean_r), WL.round_to(WL.F32, inv_r)
+    dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(zs, dt), G.dev(dy, dt), G.dev(gamma), G.dev(beta), G.dev(m32),
+                                G.dev(i32))
+    dz_r, dg_r, db_r = O.activation_backward(zs, dy, act, WL.NORM_BATCH, gamma, beta, m32, i32)
+    G.assert_close(G.host(dz), dz_r, dt, "dz")
+    G.assert_close(G.host(dg), dg_r, dt, "dgamma")
+    G.assert_close(G.host(dbt), db_r, dt, "dbeta")
+
+
+# ------------------------------------------------------------------ full-size workloads
+_CACHE = {}
+
+
+def _inputs(name):
+    """Seeded inputs of a workload; the RL stack chains layer inputs through the oracle."""
+    if name in _CACHE:
+        return _CACHE[name]
+    wl = WL.WORKLOADS[name]
+    if name in WL.RL_STACK:
+        rng = np.random.default_rng(2)
+        x = None
+        for nm in WL.RL_STACK:
+            w_ = WL.WORKLOADS[nm]
+            d = WL.make_inputs(w_, rng)
+            if x is not None:
+                d["x"] = x
+            s = w_.shape
+            z = O.conv2d_forward(d["x"], d["w"], d.get("b"), (s.sh, s.sw), (s.ph, s.pw))
+            d["z_oracle"] = z
+            x = WL.round_to(w_.dtype, O.apply_activation(WL.round_to(w_.dtype, z), w_.act))
+            _CACHE[nm] = d
+        return _CACHE[name]
+    _CACHE.clear()  # keep at most one large workload resident
+    _CACHE[name] = WL.make_inputs(wl)
+    return _CACHE[name]
+
+
+FULL = ["c1", "c2a", "c2b", "c2c", "c3", "c4", "c5"]
+BIG = {"c4", "c5"}  # sampled comparisons for the forward and dX
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_forward(name):
+    wl = WL.WORKLOADS[name]
+    s, dt = wl.shape, wl.dtype
+    d = _inputs(name)
+    desc = G.desc_for(wl)
+    bn = wl.norm == WL.NORM_BATCH
+    rm_d = G.dev(d["running_mean"]) if bn else None
+    rv_d = G.dev(d["running_var"]) if bn else None
+    out = G.run_forward(desc, dt, G.dev(d["x"], dt), G.dev(d["w"], dt), G.dev(d.get("b")),
+                        G.dev(d.get("gamma")), G.dev(d.get("beta")), rm_d, rv_d)
+    st, pd = (s.sh, s.sw), (s.ph, s.pw)
+    if name in BIG:
+        idx = G.sample_indices(s.y_shape, 4096, 7)
+        z_r = O.conv2d_forward_at(d["x"], d["w"], d.get("b"), idx, st, pd)
+        z_g = G.host(out["z"])[tuple(idx.T)]
+        G.assert_close(z_g, z_r, dt, f"{name} z (sampled)")
+        y_r = O.apply_activation(WL.round_to(dt, z_r).reshape(-1, 1), wl.act).reshape(-1)
+        G.assert_close(G.host(out["y"])[tuple(idx.T)], y_r, dt, f"{name} y (sampled)")
+        return
+    z_r = d.get("z_oracle")
+    if z_r is None:
+        z_r = O.conv2d_forward(d["x"], d["w"], d.get("b"), st, pd)
+    G.assert_close(G.host(out["z"]), z_r, dt, f"{name} z")
+    zs = WL.round_to(dt, z_r)
+    if bn:
+        mean_r, var_r, inv_r, rm_r, rv_r = O.bn_stats(zs, wl.momentum, wl.eps, d["running_mean"], d["running_var"])
+        G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, wl.eps, name)
+        G.assert_close(G.host(rm_d), rm_r, WL.F32, "running_mean")
+        G.assert_close(G.host(rv_d), rv_r, WL.F32, "running_var")
+        y_r = O.apply_activation(zs, wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], mean_r, inv_r)
+    else:
+        y_r = O.apply_activation(zs, wl.act)
+    G.assert_close(G.host(out["y"]), y_r, dt, f"{name} y")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_activation_backward(name):
+    wl = WL.WORKLOADS[name]
+    s, dt = wl.shape, wl.dtype
+    d = _inputs(name)
+    desc = G.desc_for(wl)
+    if "z_oracle" in d:
+        z = WL.round_to(dt, d["z_oracle"])
+    elif name == "c3":
+        z = WL.round_to(dt, O.conv2d_forward(d["x"], d["w"], d["b"], (s.sh, s.sw), (s.ph, s.pw)))
+    else:
+        z = WL.synthetic_preactivation(wl)
+    dy = d["dy"]
+    if wl.norm == WL.NORM_BATCH:
+        mean_r, _, inv_r, *_ = O.bn_stats(z, wl.momentum, wl.eps)
+        m32, i32 = WL.round_to(WL.F32, mean_r), WL.round_to(WL.F32, inv_r)
+        dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(z, dt), G.dev(dy, dt), G.dev(d["gamma"]), G.dev(d["beta"]),
+                                    G.dev(m32), G.dev(i32))
+        dz_r, dg_r, db_r = O.activation_backward(z, dy, wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32)
+        G.assert_close(G.host(dg), dg_r, dt, "dgamma")
+        G.assert_close(G.host(dbt), db_r, dt, "dbeta")
+    else:
+        dz, _, _ = G.run_act_bwd(desc, dt, G.dev(z, dt), G.dev(dy, dt))
+        dz_r, _, _ = O.activation_backward(z, dy, wl.act)
+    G.assert_close(G.host(dz), dz_r, dt, f"{name} dz")
+
+
+def _grad_input(name):
+    wl = WL.WORKLOADS[name]
+    # the gradient reaching the convolution: activation-backward output stand-in
+    return WL.synthetic_grad(wl, scale=1.0)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_backward_data(name):
+    wl = WL.WORKLOADS[name]
+    s, dt = wl.shape, wl.dtype
+    d = _inputs(name)
+    dz = _grad_input(name)
+    dx = G.run_backward_data(G.desc_for(wl), dt, G.dev(dz, dt), G.dev(d["w"], dt))
+    st, pd = (s.sh, s.sw), (s.ph, s.pw)
+    if name in BIG:
+        idx = G.sample_indices(s.x_shape, 4096, 8)
+        dx_r = O.conv2d_backward_data_at(dz, d["w"], s.x_shape, idx, st, pd)
+        G.assert_close(G.host(dx)[tuple(idx.T)], dx_r, dt, f"{name} dx (sampled)")
+    else:
+        G.assert_close(G.host(dx), O.conv2d_backward_data(dz, d["w"], s.x_shape, st, pd), dt, f"{name} dx")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_backward_weight(name):
+    wl = WL.WORKLOADS[name]
+    s, dt = wl.shape, wl.dtype
+    d = _inputs(name)
+    dz = _grad_input(name)
+    dw, db = G.run_backward_weight(G.desc_for(wl), G.dev(d["x"], dt), G.dev(dz, dt))
+    st, pd = (s.sh, s.sw), (s.ph, s.pw)
+    if name == "c4":
+        idx = G.sample_indices(s.w_shape, 1024, 9)
+        dw_r = O.conv2d_backward_weight_at(d["x"], dz, s.w_shape, idx, st, pd)
+        G.assert_close(G.host(dw)[tuple(idx.T)], dw_r, dt, f"{name} dw (sampled)")
+        G.assert_close(G.host(db), O.bias_grad(dz), dt, f"{name} db")
+    else:
+        dw_r, db_r = O.conv2d_backward_weight(d["x"], dz, s.w_shape, st, pd)
+        G.assert_close(G.host(dw), dw_r, dt, f"{name} dw")
+        G.assert_close(G.host(db), db_r, dt, f"{name} db")
+
+
+def test_full_bn_stats_c3():
+    """bn_stats_training alone on a synthetic pre-activation of the c3 shape."""
+    wl = WL.WORKLOADS["c3"]
+    z = WL.synthetic_preactivation(wl)
+    desc = G.desc_for(wl)
+    rm0, rv0 = np.zeros(wl.shape.OC), np.ones(wl.shape.OC)
+    rm_d, rv_d = G.dev(rm0), G.dev(rv0)
+    sm, si = G.run_bn_stats(desc, G.dev(z, wl.dtype), rm_d, rv_d)
+    mean_r, var_r, inv_r, rm_r, rv_r = O.bn_stats(z, wl.momentum, wl.eps, rm0, rv0)
+    G.assert_bn_stats(G.host(sm), G.host(si), mean_r, var_r, inv_r, wl.eps, "c3 stats")
+    G.assert_close(G.host(rm_d), rm_r, WL.F32, "running_mean")
+    G.assert_close(G.host(rv_d), rv_r, WL.F32, "running_var")
+
+
+def test_bn_stats_large_offset():
+    """Channels with |mean| >> std: the statistics must not lose the variance."""
+    r = np.random.default_rng(60)
+    C = 32
+    z = 1000.0 + np.arange(C) + r.standard_normal((64, 16, 16, C)) * 0.01
+    z = WL.round_to(WL.F32, z)
+    desc = G.shape_desc(WL.ConvShape(64, 16, 16, 1, C, 1, 1), WL.F32, 0, WL.NORM_BATCH)
+    sm, si = G.run_bn_stats(desc, G.dev(z))
+    mean_r, var_r, inv_r, *_ = O.bn_stats(z, 0.1, 1e-5)
+    G.assert_bn_stats(G.host(sm), G.host(si), mean_r, var_r, inv_r, 1e-5, "offset")
+
+
+# ------------------------------------------------------------------ contract cases
+def test_accumulate_adds_into_gradients():
+    case = ((2, 13, 11, 64, 64, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_RELU)
+    shape, dt, act, x, w, b, dy = _problem(case, 70)
+    desc = G.shape_desc(shape, dt, act)
+    dw0 = WL.random_tensor(shape.w_shape, WL.F32, 71)
+    db0 = WL.random_tensor((shape.OC,), WL.F32, 72)
+    dw_d, db_d = G.dev(dw0), G.dev(db0)
+    G.run_backward_weight(desc, G.dev(x, dt), G.dev(dy, dt), accumulate=1, dw=dw_d, db=db_d)
+    dw_r, db_r = O.conv2d_backward_weight(x, dy, shape.w_shape, (1, 1), (1, 1))
+    G.assert_close(G.host(dw_d), dw0 + dw_r, dt, "dw accumulate")
+    G.assert_close(G.host(db_d), db0 + db_r, dt, "db accumulate")
+
+
+def test_activation_backward_in_place():
+    shape = WL.ConvShape(2, 9, 9, 4, 48, 3, 3, 1, 1, 1, 1)
+    z = WL.random_tensor(shape.y_shape, WL.F32, 80)
+    dy = WL.random_tensor(shape.y_shape, WL.F32, 81)
+    desc = G.shape_desc(shape, WL.F32, WL.ACT_TANH)
+    buf = G.dev(dy)
+    G.run_act_bwd(desc, WL.F32, G.dev(z), buf, dz=buf)
+    G.assert_close(G.host(buf), O.activation_backward(z, dy, WL.ACT_TANH)[0], WL.F32, "in place")
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_deterministic(name):
+    """Same inputs, bitwise identical outputs on repeated calls."""
+    wl = WL.WORKLOADS[name]
+    s, dt = wl.shape, wl.dtype
+    x = G.dev(WL.random_tensor(s.x_shape, dt, 90), dt)
+    dz = G.dev(WL.synthetic_grad(wl), dt)
+    w = G.dev(WL.random_tensor(s.w_shape, dt, 91, ("normal", 0.0, 0.05)), dt)
+    desc = G.desc_for(wl)
+    a = [G.run_backward_weight(desc, x, dz) for _ in range(2)]
+    assert torch.equal(a[0][0], a[1][0]) and torch.equal(a[0][1], a[1][1])
+    dxs = [G.run_backward_data(desc, dt, dz, w) for _ in range(2)]
+    assert torch.equal(dxs[0], dxs[1])
+    if wl.norm == WL.NORM_BATCH:
+        st = [G.run_bn_stats(desc, dz) for _ in range(2)]
+        assert torch.equal(st[0][0], st[1][0]) and torch.equal(st[0][1], st[1][1])
