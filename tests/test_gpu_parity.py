@@ -132,9 +132,16 @@ def test_medium_batchnorm_layer(case):
     G.assert_close(G.host(out["z"]), z_r, dt, "z")
     zs = WL.round_to(dt, z_r)
     mean_r, var_r, inv_r, rm_r, rv_r = O.bn_stats(zs, mom, eps, rm0, rv0)
-    G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, eps, "fwd")
-    G.assert_close(G.host(rm_d), rm_r, WL.F32, "running_mean")
-    G.assert_close(G.host(rv_d), rv_r, WL.F32, "running_var")
+    # The forward's statistics are taken over the library's own stored z, which for
+    # bf16 differs from the oracle's rounded z by up to one bf16 ulp per element: there
+    # they inherit the bf16 tolerance.  The 1e-5 bound is checked on identical z below.
+    stat_tol = G.BN_STAT_TOL if dt == WL.F32 else G.TOL[dt]
+    G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, eps, "fwd",
+                      stat_tol)
+    G.assert_close(G.host(rm_d), rm_r, WL.F32 if dt == WL.F32 else dt, "running_mean")
+    G.assert_close(G.host(rv_d), rv_r, WL.F32 if dt == WL.F32 else dt, "running_var")
+    sm, si = G.run_bn_stats(desc, G.dev(zs, dt))
+    G.assert_bn_stats(G.host(sm), G.host(si), mean_r, var_r, inv_r, eps, "bn_stats_training on oracle z")
     y_r = O.apply_activation(zs, act, WL.NORM_BATCH, gamma, beta, mean_r, inv_r)
     G.assert_close(G.host(out["y"]), y_r, dt, "y")
     # backward on oracle-made inputs: z (rounded), statistics rounded to fp32
