@@ -1,10 +1,367 @@
-// k_dw.hip -- weight gradient on MFMA (not yet enabled: the direct kernel serves).
+// k_dw.hip -- weight and bias gradients (a6) as a split-K GEMM on gfx950 MFMA.
+//
+//   dw[oc][k] = sum_p dz[p][oc] * x_col[p][k],   db[oc] = sum_p dz[p][oc]
+//   p = (n, oh, ow) over the N*OH*OW output positions (the reduction),
+//   k = (kh, kw, ic), x_col[p][k] = x[n, oh*sh - ph + kh, ow*sw - pw + kw, ic] (0 outside).
+// This is the per-weight sum over output positions of the weight-gradient WGSL kernel
+// ("conv2d_backward_weight.wgsl", @simulatte/doppler) and of the rl_tools generic
+// listing's backward, extended over the batch.
+//
+// Both operands arrive with the reduction index p strided (channels are contiguous in
+// NHWC), while the MFMA wants each lane's 16-byte operand vector to hold consecutive p.
+// Each thread therefore loads a VEC x VEC block (VEC consecutive positions x VEC
+// consecutive channels, one 16-byte load per position), transposes it in registers and
+// writes VEC position-contiguous vectors into the LDS tiles.  Tiles are then consumed
+// exactly as in the forward kernel (16x16 MFMA, lane vector = 8 bf16 / 4 fp32 of k).
+//
+// The P reduction is split over S slabs (grid.z) to fill the 256 CUs; each slab writes an
+// fp32 partial tile, and a second kernel adds the S partials in slab order (and into the
+// existing gradient when accumulating).  No atomics: results are bitwise reproducible.
+// The bias gradient comes from the same dz loads: workgroups of the first k tile keep
+// per-channel sums of their dz block and write them beside the partial tile.
 #include "internal.hpp"
 
 namespace convmi {
-bool igemm_dw_supported(int, const ConvDims&) { return false; }
-size_t igemm_dw_ws_bytes(int, const ConvDims&) { return 0; }
-hipError_t launch_igemm_dw(int, const void*, const void*, float*, float*, int, const ConvDims&, void*, hipStream_t) {
-    return hipErrorNotSupported;
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int NT = 256;
+
+template <typename T> struct Mma;
+template <> struct Mma<bf16> {
+    static constexpr int VEC = 8, KM = 32;
+    static __device__ __forceinline__ void run(floatx4& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                    0, 0, 0);
+    }
+    // r[i] = 8 channels of position i  ->  o[j] = 8 positions of channel j
+    static __device__ __forceinline__ void transpose(const uint4* r, uint4* o) {
+        uint32_t in[8][4], out[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { in[i][0] = r[i].x; in[i][1] = r[i].y; in[i][2] = r[i].z; in[i][3] = r[i].w; }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = in[2 * d][j >> 1], hi = in[2 * d + 1][j >> 1];
+                out[j][d] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = make_uint4(out[j][0], out[j][1], out[j][2], out[j][3]);
+    }
+    static __device__ __forceinline__ void add_channels(const uint4& v, float* s) {
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            s[2 * d] += __uint_as_float(u[d] << 16);
+            s[2 * d + 1] += __uint_as_float(u[d] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Mma<float> {
+    static constexpr int VEC = 4, KM = 16;
+    static __device__ __forceinline__ void run(floatx4& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void transpose(const uint4* r, uint4* o) {
+        o[0] = make_uint4(r[0].x, r[1].x, r[2].x, r[3].x);
+        o[1] = make_uint4(r[0].y, r[1].y, r[2].y, r[3].y);
+        o[2] = make_uint4(r[0].z, r[1].z, r[2].z, r[3].z);
+        o[3] = make_uint4(r[0].w, r[1].w, r[2].w, r[3].w);
+    }
+    static __device__ __forceinline__ void add_channels(const uint4& v, float* s) {
+        s[0] += __uint_as_float(v.x); s[1] += __uint_as_float(v.y);
+        s[2] += __uint_as_float(v.z); s[3] += __uint_as_float(v.w);
+    }
+};
+
+struct DwGeom {
+    int N, H, W, IC, OC, KW, sh, sw, ph, pw, OH, OW;
+    int Kdim;       // KH*KW*IC
+    int P;          // N*OH*OW
+    int Pc;         // positions per slab (multiple of BK)
+    int tiles_n;    // k tiles
+};
+
+template <typename T, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(NT) void dw_kernel(const T* __restrict__ x, const T* __restrict__ dz, DwGeom g,
+                                                float* __restrict__ part, float* __restrict__ part_db,
+                                                int want_db) {
+    using MM = Mma<T>;
+    constexpr int VEC = MM::VEC, KM = MM::KM;
+    static_assert(WM * WN == 4, "four waves");
+    constexpr int TM = BM / (WM * 16), TN = BN / (WN * 16);
+    static_assert(TM * WM * 16 == BM && TN * WN * 16 == BN, "tile shape");
+    constexpr int LDK = BK + VEC;
+    constexpr int PG = BK / VEC;                 // position groups per K step
+    constexpr int NBA = PG * (BM / VEC);         // VEC x VEC blocks of the dz tile
+    constexpr int NBB = PG * (BN / VEC);         // blocks of the x tile
+    constexpr int ITER = (NBA + NBB + NT - 1) / NT;
+    constexpr int STAGE = (BM + BN) * LDK;
+    constexpr int LDS_AB = 2 * STAGE * (int)sizeof(T);
+    constexpr int LDS_R = PG * BM * 4;           // bias partials
+    constexpr int LDS_BYTES = LDS_AB > LDS_R ? LDS_AB : LDS_R;
+    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+    T* lds = (T*)smem;
+
+    const int t = threadIdx.x;
+    const int tn = blockIdx.x % g.tiles_n, tm = blockIdx.x / g.tiles_n;
+    const int oc0 = tm * BM, k0 = tn * BN;
+    const int p_begin = blockIdx.z * g.Pc;
+    const int p_end = min(g.P, p_begin + g.Pc);
+    const bool do_db = want_db && tn == 0;
+
+    // Static per-thread block assignment.  Block b < NBA: dz block (channel group
+    // fastest so a wave reads whole dz rows); otherwise an x block (k group fastest).
+    int kind[ITER], cg[ITER], pg[ITER];
+    int tap_h[ITER], tap_w[ITER], tap_c[ITER];
+    bool col_ok[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int b = t + it * NT;
+        if (b < NBA) {
+            kind[it] = 0;
+            cg[it] = b % (BM / VEC);
+            pg[it] = b / (BM / VEC);
+            col_ok[it] = oc0 + cg[it] * VEC < g.OC;
+            tap_h[it] = tap_w[it] = tap_c[it] = 0;
+        } else if (b < NBA + NBB) {
+            const int bb = b - NBA;
+            kind[it] = 1;
+            cg[it] = bb % (BN / VEC);
+            pg[it] = bb / (BN / VEC);
+            const int k = k0 + cg[it] * VEC;
+            col_ok[it] = k < g.Kdim;
+            const int kk = col_ok[it] ? k : 0;
+            const int tap = kk / g.IC;
+            tap_c[it] = kk - tap * g.IC;
+            tap_h[it] = tap / g.KW;
+            tap_w[it] = tap - tap_h[it] * g.KW;
+        } else {
+            kind[it] = 2;
+            cg[it] = pg[it] = 0;
+            col_ok[it] = false;
+            tap_h[it] = tap_w[it] = tap_c[it] = 0;
+        }
+    }
+
+    uint4 reg[ITER][VEC];
+    float dbs[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) dbs[j] = 0.0f;
+
+    auto load = [&](int pk) {  // pk: first position of this K step
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            if (kind[it] == 2) continue;
+            const int p0 = pk + pg[it] * VEC;
+            if (kind[it] == 0) {
+                const T* src = dz + (int64_t)p0 * g.OC + oc0 + cg[it] * VEC;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    const bool ok = col_ok[it] && p0 + i < p_end;
+                    reg[it][i] = ok ? *(const uint4*)(src + (int64_t)i * g.OC) : make_uint4(0, 0, 0, 0);
+                }
+            } else {
+                // decompose the first position once, then step along ow with carry
+                int ow = p0 % g.OW;
+                int q = p0 / g.OW;
+                int oh = q % g.OH;
+                int n = q / g.OH;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    const int ih = oh * g.sh - g.ph + tap_h[it];
+                    const int iw = ow * g.sw - g.pw + tap_w[it];
+                    const bool ok = col_ok[it] && p0 + i < p_end && (unsigned)ih < (unsigned)g.H &&
+                                    (unsigned)iw < (unsigned)g.W;
+                    reg[it][i] = ok ? *(const uint4*)(x + (((int64_t)n * g.H + ih) * g.W + iw) * g.IC + tap_c[it])
+                                    : make_uint4(0, 0, 0, 0);
+                    if (++ow == g.OW) {
+                        ow = 0;
+                        if (++oh == g.OH) { oh = 0; ++n; }
+                    }
+                }
+            }
+        }
+    };
+    auto stash = [&](int buf) {
+        T* As = lds + buf * STAGE;
+        T* Bs = As + BM * LDK;
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            if (kind[it] == 2) continue;
+            if (kind[it] == 0 && do_db)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) MM::add_channels(reg[it][i], dbs);
+            uint4 o[VEC];
+            MM::transpose(reg[it], o);
+            T* base = (kind[it] == 0 ? As : Bs) + (cg[it] * VEC) * LDK + pg[it] * VEC;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) *(uint4*)(base + j * LDK) = o[j];
+        }
+    };
+
+    const int lane = t & 63, wid = t >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+    const int lr = lane & 15, lk = (lane >> 4) * VEC;
+    floatx4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = (p_end - p_begin + BK - 1) / BK;
+    if (KT > 0) {
+        load(p_begin);
+        stash(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) load(p_begin + (kt + 1) * BK);
+        const T* As = lds + buf * STAGE;
+        const T* Bs = As + BM * LDK;
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += KM) {
+            uint4 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) af[i] = *(const uint4*)(As + (wm * TM * 16 + i * 16 + lr) * LDK + kk + lk);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) bfr[j] = *(const uint4*)(Bs + (wn * TN * 16 + j * 16 + lr) * LDK + kk + lk);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) MM::run(acc[i][j], af[i], bfr[j]);
+        }
+        if (kt + 1 < KT) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    // partial tile: part[slab][oc][k], only the in-range part
+    float* dst = part + (int64_t)blockIdx.z * g.OC * g.Kdim;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int oc = oc0 + wm * TM * 16 + i * 16 + (lane >> 4) * 4 + e;
+                const int k = k0 + wn * TN * 16 + j * 16 + lr;
+                if (oc < g.OC && k < g.Kdim) dst[(int64_t)oc * g.Kdim + k] = acc[i][j][e];
+            }
+
+    if (do_db) {  // uniform per workgroup
+        float* red = (float*)smem;  // [PG][BM], free after the last barrier of the loop
+#pragma unroll
+        for (int it = 0; it < ITER; ++it)
+            if (kind[it] == 0)
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) red[pg[it] * BM + cg[it] * VEC + j] = dbs[j];
+        __syncthreads();
+        if (t < BM && oc0 + t < g.OC) {
+            float s = 0.0f;
+            for (int q = 0; q < PG; ++q) s += red[q * BM + t];
+            part_db[(int64_t)blockIdx.z * g.OC + oc0 + t] = s;
+        }
+    }
 }
+
+// dw = (accumulate ? dw : 0) + sum over slabs in slab order; db likewise.
+__global__ __launch_bounds__(NT) void dw_reduce(const float* __restrict__ part, const float* __restrict__ part_db,
+                                                float* __restrict__ dw, float* __restrict__ db, int64_t count,
+                                                int OC, int S, int accumulate) {
+    const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+    if (i < count) {
+        float s = accumulate ? dw[i] : 0.0f;
+        float r = 0.0f;
+        for (int k = 0; k < S; ++k) r += part[(int64_t)k * count + i];
+        dw[i] = s + r;
+    }
+    if (db && i < OC) {
+        float s = accumulate ? db[i] : 0.0f;
+        float r = 0.0f;
+        for (int k = 0; k < S; ++k) r += part_db[(int64_t)k * OC + i];
+        db[i] = s + r;
+    }
+}
+
+struct Plan {
+    int bm, bn, bk, tiles_m, tiles_n, S, Pc;
+};
+
+Plan plan(int dt, const ConvDims& d) {
+    Plan p;
+    const int P = d.N * d.OH * d.OW;
+    const int Kdim = d.KH * d.KW * d.IC;
+    p.bm = d.OC <= 32 ? 32 : (d.OC <= 64 ? 64 : 128);
+    p.bn = dt == DT_BF16 ? 128 : 64;
+    if (Kdim <= 64) p.bn = 64;
+    p.bk = dt == DT_BF16 ? 64 : 32;
+    p.tiles_m = (int)ceil_div(d.OC, p.bm);
+    p.tiles_n = (int)ceil_div(Kdim, p.bn);
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int steps = (int)ceil_div(P, p.bk);
+    int S = (int)ceil_div(512, tiles);       // about two workgroups per CU
+    if (S > steps) S = steps;
+    if (S < 1) S = 1;
+    p.Pc = (int)ceil_div(ceil_div(P, S), p.bk) * p.bk;
+    p.S = (int)ceil_div(P, p.Pc);
+    return p;
+}
+
+template <typename T, int BM, int BN, int BK>
+hipError_t launch_cfg(const T* x, const T* dz, const DwGeom& g, const Plan& p, float* part, float* part_db,
+                      int want_db, hipStream_t s) {
+    constexpr int WN = BN >= 64 ? (BM >= 64 ? 2 : 4) : 1;
+    constexpr int WM = 4 / WN;
+    dim3 grid(p.tiles_m * p.tiles_n, 1, p.S);
+    dw_kernel<T, BM, BN, BK, WM, WN><<<grid, NT, 0, s>>>(x, dz, g, part, part_db, want_db);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool igemm_dw_supported(int dt, const ConvDims& d) {
+    const int vec = dt == DT_BF16 ? 8 : 4;
+    return d.IC % vec == 0 && d.OC % vec == 0 && d.OC >= 16;
+}
+
+size_t igemm_dw_ws_bytes(int dt, const ConvDims& d) {
+    const Plan p = plan(dt, d);
+    const size_t Kdim = (size_t)d.KH * d.KW * d.IC;
+    return align_up((size_t)p.S * d.OC * Kdim * 4, 256) + align_up((size_t)p.S * d.OC * 4, 256);
+}
+
+hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, float* db, int accumulate,
+                           const ConvDims& d, void* ws, hipStream_t s) {
+    const Plan p = plan(dt, d);
+    DwGeom g{d.N, d.H, d.W, d.IC, d.OC, d.KW, d.sh, d.sw, d.ph, d.pw, d.OH, d.OW,
+             d.KH * d.KW * d.IC, d.N * d.OH * d.OW, p.Pc, p.tiles_n};
+    float* part = (float*)ws;
+    float* part_db = (float*)((char*)ws + align_up((size_t)p.S * d.OC * g.Kdim * 4, 256));
+    const int want_db = db != nullptr;
+    hipError_t e = hipErrorInvalidValue;
+    if (dt == DT_BF16) {
+        if (p.bm == 128) e = launch_cfg<bf16, 128, 128, 64>((const bf16*)x, (const bf16*)dz, g, p, part, part_db, want_db, s);
+        else if (p.bm == 64 && p.bn == 128) e = launch_cfg<bf16, 64, 128, 64>((const bf16*)x, (const bf16*)dz, g, p, part, part_db, want_db, s);
+        else if (p.bm == 64) e = launch_cfg<bf16, 64, 64, 64>((const bf16*)x, (const bf16*)dz, g, p, part, part_db, want_db, s);
+        else if (p.bn == 128) e = launch_cfg<bf16, 32, 128, 64>((const bf16*)x, (const bf16*)dz, g, p, part, part_db, want_db, s);
+        else e = launch_cfg<bf16, 32, 64, 64>((const bf16*)x, (const bf16*)dz, g, p, part, part_db, want_db, s);
+    } else {
+        if (p.bm == 128) e = launch_cfg<float, 128, 64, 32>((const float*)x, (const float*)dz, g, p, part, part_db, want_db, s);
+        else if (p.bm == 64) e = launch_cfg<float, 64, 64, 32>((const float*)x, (const float*)dz, g, p, part, part_db, want_db, s);
+        else e = launch_cfg<float, 32, 64, 32>((const float*)x, (const float*)dz, g, p, part, part_db, want_db, s);
+    }
+    if (e != hipSuccess) return e;
+    const int64_t count = (int64_t)d.OC * g.Kdim;
+    const int64_t n = count > d.OC ? count : d.OC;
+    dw_reduce<<<(unsigned)ceil_div(n, NT), NT, 0, s>>>(part, part_db, dw, db, count, d.OC, p.S, accumulate);
+    return hipGetLastError();
+}
+
 }  // namespace convmi
