@@ -18,12 +18,32 @@ struct ConvDims {
 
 __device__ __forceinline__ float bf16_to_f32(bf16 h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ bf16 f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16)(u >> 16);
+typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float hw_floatx2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even: the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) { return __builtin_bit_cast(bf16, (__bf16)f); }
+
+// Two fp32 values -> two bf16 packed in 32 bits (low half = a), one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    hw_floatx2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2));
+}
+
+// Division by a divisor fixed for the whole launch, as a multiply-high and a shift
+// (round-up method, Granlund & Montgomery 1994; valid for numerators below 2^31).
+struct FastDiv {
+    uint32_t d, m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, s};
+}
+__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+    return (int)((__umulhi((uint32_t)n, f.m) + (uint32_t)n) >> f.s);
 }
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
@@ -36,19 +56,31 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return f32
 // Storage round trip: the value a stored T reads back as.
 template <typename T> __device__ __forceinline__ float round_trip(float v) { return to_f32(from_f32<T>(v)); }
 
-// act(a).  tanh and the exponential come from the device math library.
+// tanh(a) = sign(a) * (1 - e) / (1 + e) with e = exp(-2|a|) in (0, 1]: no overflow, and
+// the hardware exponential and reciprocal (v_exp_f32, v_rcp_f32) keep it to a handful of
+// instructions.  Absolute error stays near fp32 rounding of values of order 1.
+__device__ __forceinline__ float fast_tanh(float a) {
+    const float e = __expf(-2.0f * __builtin_fabsf(a));
+    const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+    return __builtin_copysignf(t, a);
+}
+
+// 1 / (1 + exp(-a)); the exponential saturates to inf for a < -88, giving 0.
+__device__ __forceinline__ float fast_sigmoid(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+
+// act(a)
 template <int ACT> __device__ __forceinline__ float act_fwd(float a) {
     if constexpr (ACT == ACT_RELU) return a > 0.0f ? a : 0.0f;
-    else if constexpr (ACT == ACT_TANH) return tanhf(a);
-    else if constexpr (ACT == ACT_SIGMOID) return 1.0f / (1.0f + expf(-a));
+    else if constexpr (ACT == ACT_TANH) return fast_tanh(a);
+    else if constexpr (ACT == ACT_SIGMOID) return fast_sigmoid(a);
     else return a;
 }
 
 // d act / d a at a.  relu'(0) = 0.
 template <int ACT> __device__ __forceinline__ float act_slope(float a) {
     if constexpr (ACT == ACT_RELU) return a > 0.0f ? 1.0f : 0.0f;
-    else if constexpr (ACT == ACT_TANH) { float t = tanhf(a); return 1.0f - t * t; }
-    else if constexpr (ACT == ACT_SIGMOID) { float s = 1.0f / (1.0f + expf(-a)); return s * (1.0f - s); }
+    else if constexpr (ACT == ACT_TANH) { float t = fast_tanh(a); return 1.0f - t * t; }
+    else if constexpr (ACT == ACT_SIGMOID) { float s = fast_sigmoid(a); return s * (1.0f - s); }
     else return 1.0f;
 }
 

@@ -71,21 +71,75 @@ struct GatherGeom {
     int R1, R2, rs1, ro1, rs2, ro2;
     int M;
     int64_t img_stride;  // Hin*Win*Cin
+    FastDiv fR1, fR2, fCin, fKWC;
 };
 
-// Epilogue targets.
+// Epilogue targets.  For each 16-byte output vector (VEC columns from col) of row m:
+// colinit() once per thread for its fixed column range, store() per row.
+template <typename T> __device__ __forceinline__ void store_vec(T* p, const float* v);
+template <> __device__ __forceinline__ void store_vec<float>(float* p, const float* v) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void store_vec<bf16>(bf16* p, const float* v) {
+    *(uint4*)p = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7]));
+}
+
+// z = acc + bias (stored in T), y = act(stored z).
 struct FwdOut {
     void* z;            // nullable
     void* y;            // nullable
     const float* bias;  // nullable
     int OC;
     int act;
+    template <int VEC> __device__ __forceinline__ void colinit(int col, float* bv) const {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) bv[j] = (bias && col + j < OC) ? bias[col + j] : 0.0f;
+    }
+    template <typename T, int ACT, int VEC>
+    __device__ __forceinline__ void store(int m, int col, const float* v, const float* bv) const {
+        float zr[VEC], yr[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            zr[j] = round_trip<T>(v[j] + bv[j]);
+            yr[j] = act_fwd<ACT>(zr[j]);
+        }
+        const int64_t base = (int64_t)m * OC + col;
+        if (col + VEC <= OC && (OC % VEC) == 0) {
+            if (z) store_vec<T>((T*)z + base, zr);
+            if (y) store_vec<T>((T*)y + base, yr);
+        } else {
+            for (int j = 0; j < VEC && col + j < OC; ++j) {
+                if (z) ((T*)z)[base + j] = from_f32<T>(zr[j]);
+                if (y) ((T*)y)[base + j] = from_f32<T>(yr[j]);
+            }
+        }
+    }
 };
+
+// dx[n, sh*qh + rh - ph, sw*qw + rw - pw, ic] = C[(n, qh, qw)][(rh, rw, ic)] where in range.
 struct DxOut {
     void* dx;
     int N, H, W, IC;
     int QH, QW, qh0, qw0;  // row grid and its origin in block units
     int sh, sw, ph, pw;
+    FastDiv fQW, fQH, fIC, fsw;
+    template <int VEC> __device__ __forceinline__ void colinit(int, float*) const {}
+    template <typename T, int ACT, int VEC>
+    __device__ __forceinline__ void store(int m, int col, const float* v, const float*) const {
+        // IC is a multiple of VEC, so the vector stays inside one phase (rh, rw)
+        const int phs = fdiv(col, fIC);
+        const int ic = col - phs * IC;
+        const int rh = fdiv(phs, fsw), rw = phs - rh * sw;
+        const int q = fdiv(m, fQW);
+        const int qw = m - q * QW;
+        const int n = fdiv(q, fQH);
+        const int qh = q - n * QH;
+        const int ih = (qh + qh0) * sh + rh - ph;
+        const int iw = (qw + qw0) * sw + rw - pw;
+        if (ih < 0 || ih >= H || iw < 0 || iw >= W) return;
+        store_vec<T>((T*)dx + (((int64_t)n * H + ih) * W + iw) * IC + ic, v);
+    }
 };
 
 __device__ __forceinline__ int xcd_tile(int bid, int nb) {
@@ -94,60 +148,6 @@ __device__ __forceinline__ int xcd_tile(int bid, int nb) {
     if (bid >= full) return bid;
     const int per = full >> 3;
     return (bid & 7) * per + (bid >> 3);
-}
-
-template <typename T> __device__ __forceinline__ void store_vec(T* p, const float* v);
-template <> __device__ __forceinline__ void store_vec<float>(float* p, const float* v) {
-    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
-}
-template <> __device__ __forceinline__ void store_vec<bf16>(bf16* p, const float* v) {
-    uint32_t u[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) u[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
-    *(uint4*)p = make_uint4(u[0], u[1], u[2], u[3]);
-}
-
-// Forward epilogue for one 16-byte output vector (VEC columns starting at col).
-template <typename T, int ACT, int VEC>
-__device__ __forceinline__ void epi_store(const FwdOut& o, int m, int col, const float* v) {
-    float zr[VEC], yr[VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-        const int c = col + j;
-        float a = v[j] + ((o.bias && c < o.OC) ? o.bias[c] : 0.0f);
-        zr[j] = round_trip<T>(a);
-        yr[j] = act_fwd<ACT>(zr[j]);
-    }
-    const int64_t base = (int64_t)m * o.OC + col;
-    if (col + VEC <= o.OC && (o.OC % VEC) == 0) {
-        if (o.z) store_vec<T>((T*)o.z + base, zr);
-        if (o.y) store_vec<T>((T*)o.y + base, yr);
-    } else {
-        for (int j = 0; j < VEC && col + j < o.OC; ++j) {
-            if (o.z) ((T*)o.z)[base + j] = from_f32<T>(zr[j]);
-            if (o.y) ((T*)o.y)[base + j] = from_f32<T>(yr[j]);
-        }
-    }
-}
-
-template <typename T, int ACT, int VEC>
-__device__ __forceinline__ void epi_store(const DxOut& o, int m, int col, const float* v) {
-    // col = (rh*sw + rw)*IC + ic, IC a multiple of VEC so the vector stays in one phase
-    const int ic = col % o.IC;
-    const int ph_ = col / o.IC;
-    const int rh = ph_ / o.sw, rw = ph_ % o.sw;
-    if (rh >= o.sh) return;  // padded column
-    const int qw = m % o.QW;
-    const int t = m / o.QW;
-    const int qh = t % o.QH;
-    const int n = t / o.QH;
-    const int ih = (qh + o.qh0) * o.sh + rh - o.ph;
-    const int iw = (qw + o.qw0) * o.sw + rw - o.pw;
-    if (ih < 0 || ih >= o.H || iw < 0 || iw >= o.W) return;
-    float r[VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) r[j] = v[j];
-    store_vec<T>((T*)o.dx + (((int64_t)n * o.H + ih) * o.W + iw) * o.IC + ic, r);
 }
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, int SIGN, int ACT, class Out>
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NT) void igemm_kernel(const T* __restrict__ A, Gath
     // ---- per-thread gather state (fixed for the whole K loop)
     const int kv = t % KV, rr = t / KV;
     const int kofs = kv * VEC;
-    const int kq = kofs / g.Cin, kr = kofs - kq * g.Cin;  // tap and channel offset of this vector
+    const int kq = fdiv(kofs, g.fCin), kr = kofs - kq * g.Cin;  // tap and channel offset of this vector
     int64_t a_base[AP];
     int a_h[AP], a_w[AP];
     bool a_ok[AP];
@@ -188,10 +188,10 @@ __global__ __launch_bounds__(NT) void igemm_kernel(const T* __restrict__ A, Gath
         const int m = m0 + p * RPP + rr;
         a_ok[p] = m < g.M;
         const int mm = a_ok[p] ? m : 0;
-        const int r2 = mm % g.R2;
-        const int q = mm / g.R2;
-        const int r1 = q % g.R1;
-        const int n = q / g.R1;
+        const int q = fdiv(mm, g.fR2);
+        const int r2 = mm - q * g.R2;
+        const int n = fdiv(q, g.fR1);
+        const int r1 = q - n * g.R1;
         a_h[p] = r1 * g.rs1 + g.ro1;
         a_w[p] = r2 * g.rs2 + g.ro2 + SIGN * kq;
         a_base[p] = (int64_t)n * g.img_stride + ((int64_t)a_h[p] * g.Win + a_w[p]) * g.Cin + kr;
@@ -209,9 +209,9 @@ __global__ __launch_bounds__(NT) void igemm_kernel(const T* __restrict__ A, Gath
 
     uint4 ra[AP], rb[BP];
     auto load = [&](int k0) {
-        const int kh = k0 / KWC;
+        const int kh = fdiv(k0, g.fKWC);
         const int rem = k0 - kh * KWC;
-        const int kw = rem / g.Cin;
+        const int kw = fdiv(rem, g.fCin);
         const int c0 = rem - kw * g.Cin;
         const int dh = SIGN * kh, dw = SIGN * kw;
         const int64_t U = ((int64_t)dh * g.Win + dw) * g.Cin + c0;
@@ -279,12 +279,208 @@ __global__ __launch_bounds__(NT) void igemm_kernel(const T* __restrict__ A, Gath
                 Cs[(wm * TM * 16 + i * 16 + (lane >> 4) * 4 + e) * LDC + wn * TN * 16 + j * 16 + lr] = acc[i][j][e];
     __syncthreads();
     constexpr int OVR = BN / VEC;  // output vectors per row
-    for (int v = t; v < BM * OVR; v += NT) {
-        const int r = v / OVR, cv = v % OVR;
-        const int m = m0 + r, col = n0 + cv * VEC;
-        if (m >= g.M || col >= Nn) continue;
-        epi_store<T, ACT, VEC>(out, m, col, Cs + r * LDC + cv * VEC);
+    static_assert(NT % OVR == 0, "each thread keeps one column range");
+    const int cv = t % OVR, col = n0 + cv * VEC;
+    float bv[VEC];
+    out.template colinit<VEC>(col, bv);
+    if (col < Nn)
+        for (int r = t / OVR; r < BM; r += NT / OVR) {
+            const int m = m0 + r;
+            if (m >= g.M) break;
+            out.template store<T, ACT, VEC>(m, col, Cs + r * LDC + cv * VEC, bv);
+        }
+}
+
+// ------------------------------------------------------------------ asynchronous-copy kernel
+// The same GEMM with the operand tiles brought into LDS by the gfx950 LDS-DMA path
+// (global_load_lds_dwordx4: lane i writes 16 bytes at M0 + 16*i), so no registers stage
+// the tiles and STAGES-1 K steps are in flight while one is consumed.  A K step is one
+// 128-byte row per tile row (64 bf16 or 32 fp32 of k); each group of 8 rows is one DMA
+// instruction.  16-byte chunks are XOR-swizzled within a row (chunk c of row r lives at
+// c ^ ((r >> 1) & 7)) so that 16 lanes reading the same chunk of 16 consecutive rows hit
+// distinct LDS banks.  Rows outside the image or the matrix load a 16-byte zero page.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)(p); }
+
+// 16 bytes per lane, global -> LDS.  The LDS base must be wave-uniform.  Issued through
+// inline assembly so the compiler does not serialise it with a vmcnt(0) before every LDS
+// read; completion is awaited explicitly with wait_dma().
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+}
+
+// Wait until at most n of this wave's copies are outstanding (n wave-uniform; values
+// above 31 wait for 31, which is only more conservative).
+__device__ __forceinline__ void wait_dma(int n) {
+#define CONVMI_W(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+    switch (n) {
+        CONVMI_W(0) CONVMI_W(1) CONVMI_W(2) CONVMI_W(3) CONVMI_W(4) CONVMI_W(5) CONVMI_W(6) CONVMI_W(7)
+        CONVMI_W(8) CONVMI_W(9) CONVMI_W(10) CONVMI_W(11) CONVMI_W(12) CONVMI_W(13) CONVMI_W(14) CONVMI_W(15)
+        CONVMI_W(16) CONVMI_W(17) CONVMI_W(18) CONVMI_W(19) CONVMI_W(20) CONVMI_W(21) CONVMI_W(22) CONVMI_W(23)
+        CONVMI_W(24) CONVMI_W(25) CONVMI_W(26) CONVMI_W(27) CONVMI_W(28) CONVMI_W(29) CONVMI_W(30)
+        default: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
     }
+#undef CONVMI_W
+}
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+template <typename T, int BM, int BN, int WM, int WN, int STAGES, int SIGN, int ACT, class Out>
+__global__ __launch_bounds__(WM * WN * 64) void igemm2_kernel(const T* __restrict__ A, GatherGeom g,
+                                                              const T* __restrict__ B, int Nn, int Kb, Out out,
+                                                              int tiles_n) {
+    using MM = Mma<T>;
+    constexpr int NWAVE = WM * WN, NTH = NWAVE * 64;
+    constexpr int VEC = MM::VEC;
+    constexpr int BK = 128 / (int)sizeof(T);
+    constexpr int TM = BM / (WM * 16), TN = BN / (WN * 16);
+    static_assert(TM * WM * 16 == BM && TN * WN * 16 == BN, "tile shape");
+    static_assert(BM % 8 == 0 && BN % 8 == 0, "8-row copy groups");
+    constexpr int GA = BM / 8, GB = BN / 8;
+    constexpr int GPW = (GA + GB + NWAVE - 1) / NWAVE;
+    constexpr int STAGE_BYTES = (BM + BN) * 128;
+    constexpr int RING = STAGES * STAGE_BYTES;
+    constexpr int LDC = BN + 4;
+    constexpr int EPI = BM * LDC * 4;
+    constexpr int LDS_BYTES = RING > EPI ? RING : EPI;
+    __shared__ __align__(1024) unsigned char smem[LDS_BYTES];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, kept in an SGPR
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+    const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+    // per-lane copy state for each 8-row group this wave owns
+    const int rg = lane >> 3, pc = lane & 7;
+    int64_t cbase[GPW];
+    int ch[GPW], cw[GPW];
+    bool cok[GPW];
+    int n_w = 0;  // copies this wave issues per stage (wave-uniform)
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const int grp = wid + NWAVE * j;
+        cbase[j] = 0; ch[j] = 0; cw[j] = 0; cok[j] = false;
+        if (grp >= GA + GB) continue;
+        ++n_w;
+        const int rl = (grp < GA ? grp : grp - GA) * 8 + rg;  // row within its tile
+        const int kofs = (pc ^ swz(rl)) * VEC;                // logical k offset of this lane's chunk
+        if (grp < GA) {
+            const int m = m0 + rl;
+            const int kq = fdiv(kofs, g.fCin), kr = kofs - kq * g.Cin;
+            cok[j] = m < g.M;
+            const int mm = cok[j] ? m : 0;
+            const int q = fdiv(mm, g.fR2);
+            const int r2 = mm - q * g.R2;
+            const int n = fdiv(q, g.fR1);
+            const int r1 = q - n * g.R1;
+            ch[j] = r1 * g.rs1 + g.ro1;
+            cw[j] = r2 * g.rs2 + g.ro2 + SIGN * kq;
+            cbase[j] = (int64_t)n * g.img_stride + ((int64_t)ch[j] * g.Win + cw[j]) * g.Cin + kr;
+        } else {
+            const int n = n0 + rl;
+            cok[j] = n < Nn;
+            cbase[j] = (int64_t)(cok[j] ? n : 0) * Kb + kofs;
+        }
+    }
+    const int KWC = g.KWk * g.Cin;
+
+    auto issue = [&](int st) {  // copy K step st into ring slot st % STAGES
+        const int k0 = st * BK;
+        const int kh = fdiv(k0, g.fKWC);
+        const int rem = k0 - kh * KWC;
+        const int kw = fdiv(rem, g.fCin);
+        const int c0 = rem - kw * g.Cin;
+        const int dh = SIGN * kh, dw = SIGN * kw;
+        const int64_t U = ((int64_t)dh * g.Win + dw) * g.Cin + c0;
+        const uint32_t slot = smem_base + (uint32_t)((st % STAGES) * STAGE_BYTES);
+#pragma unroll
+        for (int j = 0; j < GPW; ++j) {
+            const int grp = wid + NWAVE * j;
+            if (grp >= GA + GB) break;
+            const void* src;
+            uint32_t dst;
+            if (grp < GA) {
+                const int ih = ch[j] + dh, iw = cw[j] + dw;
+                const bool ok = cok[j] && (unsigned)ih < (unsigned)g.Hin && (unsigned)iw < (unsigned)g.Win;
+                src = ok ? (const void*)(A + cbase[j] + U) : (const void*)&kZero16;
+                dst = slot + grp * 1024;
+            } else {
+                src = cok[j] ? (const void*)(B + cbase[j] + k0) : (const void*)&kZero16;
+                dst = slot + BM * 128 + (grp - GA) * 1024;
+            }
+            dma16(src, __builtin_amdgcn_readfirstlane(dst));
+        }
+    };
+
+    const int wm = wid / WN, wn = wid % WN;
+    const int lr = lane & 15, lg = lane >> 4;
+    floatx4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int st) {
+        const unsigned char* As = smem + (st % STAGES) * STAGE_BYTES;
+        const unsigned char* Bs = As + BM * 128;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int lc = kk * 4 + lg;
+            uint4 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * TM * 16 + i * 16 + lr;
+                af[i] = *(const uint4*)(As + r * 128 + ((lc ^ swz(r)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int r = wn * TN * 16 + j * 16 + lr;
+                bfr[j] = *(const uint4*)(Bs + r * 128 + ((lc ^ swz(r)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) MM::run(acc[i][j], af[i], bfr[j]);
+        }
+    };
+
+    const int KT = Kb / BK;
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < KT) issue(st);
+    for (int k = 0; k < KT; ++k) {
+        const int later = (KT - 1 - k) < (STAGES - 2) ? (KT - 1 - k) : (STAGES - 2);
+        wait_dma(later * n_w);
+        __syncthreads();
+        if (k + STAGES - 1 < KT) issue(k + STAGES - 1);
+        compute(k);
+    }
+    __syncthreads();
+
+    float* Cs = (float*)smem;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Cs[(wm * TM * 16 + i * 16 + lg * 4 + e) * LDC + wn * TN * 16 + j * 16 + lr] = acc[i][j][e];
+    __syncthreads();
+    constexpr int OVR = BN / VEC;
+    static_assert(NTH % OVR == 0, "each thread keeps one column range");
+    const int cv = t % OVR, col = n0 + cv * VEC;
+    float bv[VEC];
+    out.template colinit<VEC>(col, bv);
+    if (col < Nn)
+        for (int r = t / OVR; r < BM; r += NTH / OVR) {
+            const int m = m0 + r;
+            if (m >= g.M) break;
+            out.template store<T, ACT, VEC>(m, col, Cs + r * LDC + cv * VEC, bv);
+        }
 }
 
 // B for the input gradient: Bt[(rh, rw, ic)][(a, b, oc)] = w[oc, rh + sh*a, rw + sw*b, ic].
@@ -341,17 +537,75 @@ hipError_t launch_cfg(const T* A, const GatherGeom& g, const T* B, int Nn, int K
     return hipGetLastError();
 }
 
+// Two ring stages (one K step in flight while one is consumed) keep a 128x128 block
+// under 80 KB of LDS, so two workgroups share a CU and cover each other's load latency
+// and epilogue; measured on MI355X this beats three stages at one workgroup per CU.
+constexpr int kStages = 2;
+
+// Asynchronous-copy kernel: pick the block tile whose last wave of workgroups leaves
+// the fewest CUs idle (tiles are 16-row multiples so e.g. 200704 rows split evenly).
+template <typename T, int BM, int BN, int WM, int WN, int SIGN, int ACT, class Out>
+hipError_t launch2_cfg(const T* A, const GatherGeom& g, const T* B, int Nn, int Kb, const Out& out,
+                       hipStream_t s) {
+    const int tiles_m = (int)ceil_div(g.M, BM), tiles_n = (int)ceil_div(Nn, BN);
+    igemm2_kernel<T, BM, BN, WM, WN, kStages, SIGN, ACT, Out><<<tiles_m * tiles_n, WM * WN * 64, 0, s>>>(
+        A, g, B, Nn, Kb, out, tiles_n);
+    return hipGetLastError();
+}
+
+double tile_cost(int M, int Nn, int bm, int bn, int lds_bytes, double eff) {
+    int occ = 163840 / lds_bytes;
+    occ = occ < 1 ? 1 : (occ > 2 ? 2 : occ);
+    const int64_t tiles = ceil_div(M, bm) * ceil_div(Nn, bn);
+    const int64_t rounds = ceil_div(tiles, 256LL * occ);
+    return (double)rounds * occ * bm * bn / eff;
+}
+
+int lds2(int bm, int bn) {
+    const int ring = kStages * (bm + bn) * 128, epi = bm * (bn + 4) * 4;
+    return ring > epi ? ring : epi;
+}
+
+template <typename T, int SIGN, int ACT, class Out>
+hipError_t launch2_any(const T* A, const GatherGeom& g, const T* B, int Nn, int Kb, const Out& out,
+                       hipStream_t s) {
+    const int bn = pick_bn(Nn);
+    if (bn == 128) {
+        const double c128 = tile_cost(g.M, Nn, 128, 128, lds2(128, 128), 1.0);
+        const double c112 = tile_cost(g.M, Nn, 112, 128, lds2(112, 128), 0.97);
+        if (c112 < c128) return launch2_cfg<T, 112, 128, 1, 4, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
+        return launch2_cfg<T, 128, 128, 2, 2, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
+    }
+    if (bn == 64) {
+        const double c128 = tile_cost(g.M, Nn, 128, 64, lds2(128, 64), 1.0);
+        const double c112 = tile_cost(g.M, Nn, 112, 64, lds2(112, 64), 0.97);
+        if (c112 < c128) return launch2_cfg<T, 112, 64, 1, 4, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
+        return launch2_cfg<T, 128, 64, 2, 2, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
+    }
+    const double c128 = tile_cost(g.M, Nn, 128, 32, lds2(128, 32), 1.0);
+    const double c64 = tile_cost(g.M, Nn, 64, 32, lds2(64, 32), 0.85);
+    if (c64 < c128) return launch2_cfg<T, 64, 32, 4, 1, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
+    return launch2_cfg<T, 128, 32, 4, 1, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
+}
+
 template <typename T, int SIGN, int ACT, class Out>
 hipError_t launch_any(const T* A, const GatherGeom& g, const T* B, int Nn, int Kb, int bk, const Out& out,
                       hipStream_t s) {
     constexpr int KM = Mma<T>::KM;
+    if (bk == 2 * KM) return launch2_any<T, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
     const int bn = pick_bn(Nn);
 #define CONVMI_IG(BN_, BK_)                                                                        \
     if (bn == BN_ && bk == BK_) return launch_cfg<T, 128, BN_, BK_, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
-    CONVMI_IG(32, KM) CONVMI_IG(32, 2 * KM) CONVMI_IG(64, KM) CONVMI_IG(64, 2 * KM) CONVMI_IG(128, KM)
-    CONVMI_IG(128, 2 * KM)
+    CONVMI_IG(32, KM) CONVMI_IG(64, KM) CONVMI_IG(128, KM)
 #undef CONVMI_IG
     return hipErrorInvalidValue;
+}
+
+void set_divs(GatherGeom& g) {
+    g.fR1 = make_fastdiv(g.R1);
+    g.fR2 = make_fastdiv(g.R2);
+    g.fCin = make_fastdiv(g.Cin);
+    g.fKWC = make_fastdiv(g.KWk * g.Cin);
 }
 
 int dx_khs(const ConvDims& d) { return (int)ceil_div(d.KH, d.sh); }
@@ -385,6 +639,7 @@ hipError_t launch_igemm_fwd(int dt, const void* x, const void* w, const float* b
     g.R1 = d.OH; g.R2 = d.OW; g.rs1 = d.sh; g.ro1 = -d.ph; g.rs2 = d.sw; g.ro2 = -d.pw;
     g.M = d.N * d.OH * d.OW;
     g.img_stride = (int64_t)d.H * d.W * d.IC;
+    set_divs(g);
     FwdOut o{z, y, bias, d.OC, act};
     const int Kb = d.KH * d.KW * d.IC;
     const int bk = pick_bk(dt, d.IC, d.KW);
@@ -422,7 +677,9 @@ hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, cons
     g.rs1 = 1; g.ro1 = qh0; g.rs2 = 1; g.ro2 = qw0;
     g.M = d.N * g.R1 * g.R2;
     g.img_stride = (int64_t)d.OH * d.OW * d.OC;
-    DxOut o{dx, d.N, d.H, d.W, d.IC, g.R1, g.R2, qh0, qw0, d.sh, d.sw, d.ph, d.pw};
+    set_divs(g);
+    DxOut o{dx, d.N, d.H, d.W, d.IC, g.R1, g.R2, qh0, qw0, d.sh, d.sw, d.ph, d.pw,
+            make_fastdiv(g.R2), make_fastdiv(g.R1), make_fastdiv(d.IC), make_fastdiv(d.sw)};
     const int bk = pick_bk(dt, d.OC, KWs);
     if (dt == DT_BF16)
         return launch_any<bf16, -1, ACT_IDENTITY, DxOut>((const bf16*)dz, g, (const bf16*)ws, Ncol, Kb, bk, o, s);
