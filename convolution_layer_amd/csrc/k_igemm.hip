@@ -33,6 +33,7 @@
 // convolution + bias into pre_activations; backward_input: scatter of w * d_pre_act) and
 // "operations_cuda.h" (forward with bias + activation; backward_input = BackwardData).
 #include "internal.hpp"
+#include "lds_dma.hpp"
 
 namespace convmi {
 namespace {
@@ -141,14 +142,6 @@ struct DxOut {
         store_vec<T>((T*)dx + (((int64_t)n * H + ih) * W + iw) * IC + ic, v);
     }
 };
-
-__device__ __forceinline__ int xcd_tile(int bid, int nb) {
-    // Hardware places block b on XCD b % 8.  Give each XCD a contiguous run of tiles.
-    const int full = nb & ~7;
-    if (bid >= full) return bid;
-    const int per = full >> 3;
-    return (bid & 7) * per + (bid >> 3);
-}
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, int SIGN, int ACT, class Out>
 __global__ __launch_bounds__(NT) void igemm_kernel(const T* __restrict__ A, GatherGeom g, const T* __restrict__ B,
@@ -299,33 +292,6 @@ __global__ __launch_bounds__(NT) void igemm_kernel(const T* __restrict__ A, Gath
 // instruction.  16-byte chunks are XOR-swizzled within a row (chunk c of row r lives at
 // c ^ ((r >> 1) & 7)) so that 16 lanes reading the same chunk of 16 consecutive rows hit
 // distinct LDS banks.  Rows outside the image or the matrix load a 16-byte zero page.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)(p); }
-
-// 16 bytes per lane, global -> LDS.  The LDS base must be wave-uniform.  Issued through
-// inline assembly so the compiler does not serialise it with a vmcnt(0) before every LDS
-// read; completion is awaited explicitly with wait_dma().
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
-}
-
-// Wait until at most n of this wave's copies are outstanding (n wave-uniform; values
-// above 31 wait for 31, which is only more conservative).
-__device__ __forceinline__ void wait_dma(int n) {
-#define CONVMI_W(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
-    switch (n) {
-        CONVMI_W(0) CONVMI_W(1) CONVMI_W(2) CONVMI_W(3) CONVMI_W(4) CONVMI_W(5) CONVMI_W(6) CONVMI_W(7)
-        CONVMI_W(8) CONVMI_W(9) CONVMI_W(10) CONVMI_W(11) CONVMI_W(12) CONVMI_W(13) CONVMI_W(14) CONVMI_W(15)
-        CONVMI_W(16) CONVMI_W(17) CONVMI_W(18) CONVMI_W(19) CONVMI_W(20) CONVMI_W(21) CONVMI_W(22) CONVMI_W(23)
-        CONVMI_W(24) CONVMI_W(25) CONVMI_W(26) CONVMI_W(27) CONVMI_W(28) CONVMI_W(29) CONVMI_W(30)
-        default: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
-    }
-#undef CONVMI_W
-}
-
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 template <typename T, int BM, int BN, int WM, int WN, int STAGES, int SIGN, int ACT, class Out>
