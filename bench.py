@@ -11,9 +11,21 @@ Per-call durations come from HIP events recorded on the stream the library launc
 (torch's current stream) around every call of the timed steps.  The fp64 oracle is
 timed on a bounded sample of the same layer on the host cores (cpu_baseline).
 
+HBM traffic of the dominant call comes from rocprofv3 counter runs of this script
+(FETCH_SIZE, WRITE_SIZE), scaled by what the same counters read for a plain device copy
+of known size; the figures live in profiles/traffic.json together with a hash of the
+kernel sources they were taken on, and are reported as null once the sources change.
+Modes for producing them:
+  python bench.py --only CALL --steps 3 --warmup 1 --no-cpu-baseline --no-bn   (counter runs)
+  python bench.py --calibrate-copy                                              (copy kernel)
+  python bench.py --summarize DIR                          (rocprofv3 CSVs -> summary text)
+
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a message.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -29,16 +41,29 @@ import workloads as WL  # noqa: E402
 PEAK_TFLOPS = {WL.BF16: 2516.6, WL.F32: 157.3}  # MI355X dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
 METRIC = "conv2d fwd+dX+dW TFLOP/s and % MFMA peak; BN-stats GB/s (1 MI355X)"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+CONV_CALLS = ("forward", "backward_data", "backward_weight")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def source_hash() -> str:
+    """Hash of the library's kernel and host sources (traffic figures are tied to it)."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "convolution_layer_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 class Layer:
     """Device buffers and the four library calls of one training step."""
 
-    def __init__(self, wl: WL.Workload, dz_from_act_bwd=True):
+    def __init__(self, wl: WL.Workload):
         import torch
 
         import convolution_layer_amd as cm
@@ -88,10 +113,10 @@ class Layer:
                 ("backward_data", self.bwd_data), ("backward_weight", self.bwd_weight)]
 
 
-def timed_steps(layer, steps, warmup):
+def timed_steps(layer, steps, warmup, only=None):
     """Run warmup + timed steps; returns (total seconds, {call: mean ms})."""
     import torch
-    calls = layer.calls()
+    calls = [(n, f) for n, f in layer.calls() if only is None or n == only]
     for _ in range(warmup):
         for _, f in calls:
             f()
@@ -146,6 +171,92 @@ def cpu_baseline(wl: WL.Workload, n_images: int):
     return 3 * s.flops() / sec / 1e12, sec, O.num_threads()
 
 
+def calibrate_copy(reps=5):
+    """A plain device-to-device copy of COPY_BYTES, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "reps": reps}), flush=True)
+
+
+# ------------------------------------------------------------------ rocprofv3 summaries
+KERNEL_OF_CALL = {  # kernel-name fragments each library call launches
+    "forward": ("igemm2_kernel<", "igemm_kernel<", "conv_fwd_direct"),
+    "backward_data": ("dx_weights", "igemm2_kernel<", "igemm_kernel<", "conv_dx_direct"),
+    "backward_weight": ("dw2_kernel", "dw_kernel", "dw_reduce4", "conv_dw_direct"),
+}
+
+
+def _read_counters(d):
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            out.setdefault(key, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize(d):
+    """Summarise rocprofv3 output under d (kt/, fetch/, write/, copy_fetch/, copy_write/):
+    kernel durations, and FETCH_SIZE/WRITE_SIZE per dispatch scaled by the copy
+    calibration.  Writes d/traffic.json and prints the text summary."""
+    lines = [f"rocprofv3 summary of {d} (library sources {source_hash()})", ""]
+    stats = glob.glob(os.path.join(d, "kt", "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        lines.append(f"{'kernel':90s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}")
+        for r in csv.DictReader(open(stats[0])):
+            lines.append(f"{r['Name'][:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.2f} "
+                         f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+        lines.append("")
+    scale = {}
+    for cnt, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
+        c = _read_counters(os.path.join(d, sub))
+        vals = [v for (k, n), vs in c.items() if n == cnt and "copy" in k.lower() for v in vs]
+        if vals:
+            kib = float(np.median(vals))
+            scale[cnt] = (COPY_BYTES / 1024.0) / kib
+            lines.append(f"copy calibration {cnt}: {kib:.0f} KiB per {COPY_BYTES >> 20} MiB copy -> factor "
+                         f"{scale[cnt]:.4f}")
+    traffic = {"sources": source_hash(), "scale": scale, "calls": {}}
+    per_kernel = {}
+    for cnt, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        c = _read_counters(os.path.join(d, sub))
+        for (k, n), vs in c.items():
+            if n == cnt:
+                per_kernel.setdefault(k, {})[cnt] = float(np.median(vs))
+    if per_kernel:
+        lines.append("")
+        lines.append(f"{'kernel':90s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} (per dispatch, raw)")
+        for k, v in sorted(per_kernel.items()):
+            lines.append(f"{k[:90]:90s} {v.get('FETCH_SIZE', float('nan')):12.0f} "
+                         f"{v.get('WRITE_SIZE', float('nan')):12.0f}")
+        traffic["kernels"] = {k: v for k, v in per_kernel.items()}
+    with open(os.path.join(d, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    print("\n".join(lines))
+
+
+def call_traffic(call: str):
+    """HBM bytes per launch of one library call from profiles/traffic.json, or None when
+    absent or taken on different sources."""
+    try:
+        t = json.load(open(TRAFFIC_JSON))
+    except (OSError, ValueError):
+        return None
+    if t.get("sources") != source_hash() or "kernels" not in t or len(t.get("scale", {})) != 2:
+        return None
+    frags = KERNEL_OF_CALL[call]
+    total, seen = 0.0, False
+    for k, v in t["kernels"].items():
+        if any(f in k for f in frags) and ("igemm" not in k or ("FwdOut" in k) == (call == "forward")):
+            total += v.get("FETCH_SIZE", 0) * t["scale"]["FETCH_SIZE"] + v.get("WRITE_SIZE", 0) * t["scale"]["WRITE_SIZE"]
+            seen = True
+    return total * 1024.0 if seen else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,48 +265,64 @@ def main():
     ap.add_argument("--workload", default="c4", choices=sorted(WL.WORKLOADS))
     ap.add_argument("--cpu-images", type=int, default=2, help="images of the batch the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bn", action="store_true", help="skip the batch-norm statistics measurement")
+    ap.add_argument("--only", choices=("forward", "activation_backward", "backward_data", "backward_weight"))
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is not built.",
               file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench needs a GPU"
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     wl = WL.WORKLOADS[args.workload]
     s = wl.shape
     log(f"bench: workload {wl.name} ({wl.note}); building inputs")
     layer = Layer(wl)
     log("bench: timing steps")
-    total, ms = timed_steps(layer, args.steps, args.warmup)
+    total, ms = timed_steps(layer, args.steps, args.warmup, args.only)
     step_ms = total / args.steps * 1e3
     flops = 3 * s.flops()
     value = flops / (total / args.steps) / 1e12
     log(f"bench: step {step_ms:.3f} ms; per call ms {ms}")
+    if args.only:
+        print(json.dumps({"only": args.only, "ms": ms}), flush=True)
+        return
 
-    # dominant kernel: the convolution call with the longest mean duration
-    conv_calls = {k: v for k, v in ms.items() if k in ("forward", "backward_data", "backward_weight")}
+    # dominant call: the convolution call with the longest mean duration
+    conv_calls = {k: v for k, v in ms.items() if k in CONV_CALLS}
     dom = max(conv_calls, key=conv_calls.get)
     achieved = s.flops() / (conv_calls[dom] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
+    tr = call_traffic(dom)
     roofline = {"bound": "mfma", "kernel": f"conv2d_{dom}", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None if tr is None else round(tr),
                 "per_call_ms": {k: round(v, 4) for k, v in ms.items()},
-                "per_call_tflops": {k: round(s.flops() / (v * 1e-3) / 1e12, 2) for k, v in conv_calls.items()}}
+                "per_call_tflops": {k: round(s.flops() / (v * 1e-3) / 1e12, 2) for k, v in conv_calls.items()},
+                "per_call_hbm_bytes": {k: call_traffic(k) for k in CONV_CALLS}}
 
-    # batch-norm statistics bandwidth on the conv + batch-norm layer
-    del layer
-    torch.cuda.empty_cache()
-    bn_wl = WL.WORKLOADS["c3"]
-    bn_layer = Layer(bn_wl)
-    bn_layer.forward()
-    bn_ms = time_call(bn_layer.bn_stats, 50)
-    zbytes = bn_wl.shape.P * bn_wl.shape.OC * 4
-    bn_gbs = zbytes / (bn_ms * 1e-3) / 1e9
-    bn = {"workload": "c3", "bytes": zbytes, "ms": round(bn_ms, 5), "GB/s": round(bn_gbs, 1),
-          "frac": round(bn_gbs / PEAK_HBM_GBS, 4)}
-    log(f"bench: bn_stats {bn}")
-    del bn_layer
-    torch.cuda.empty_cache()
+    bn = None
+    if not args.no_bn:
+        del layer
+        torch.cuda.empty_cache()
+        bn_wl = WL.WORKLOADS["c3"]
+        bn_layer = Layer(bn_wl)
+        bn_layer.forward()
+        bn_ms = time_call(bn_layer.bn_stats, 50)
+        zbytes = bn_wl.shape.P * bn_wl.shape.OC * 4
+        bn_gbs = zbytes / (bn_ms * 1e-3) / 1e9
+        bn = {"workload": "c3", "bytes": zbytes, "ms": round(bn_ms, 5), "GB/s": round(bn_gbs, 1),
+              "frac": round(bn_gbs / PEAK_HBM_GBS, 4)}
+        log(f"bench: bn_stats {bn}")
+        del bn_layer
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -87,6 +87,7 @@ struct DwGeom {
     int P;          // N*OH*OW
     int Pc;         // positions per slab (multiple of BK)
     int tiles_n;    // k tiles
+    int S;          // slabs
 };
 
 template <typename T, int BM, int BN, int BK, int WM, int WN>
@@ -309,9 +310,15 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
 
     const int t = threadIdx.x, lane = t & 63;
     const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int tn = blockIdx.x % g.tiles_n, tm = blockIdx.x / g.tiles_n;
+    // One-dimensional grid over (slab, tile), renumbered so each XCD gets whole slabs:
+    // the tiles of one slab read the same dz rows and overlapping x rows, which then
+    // stay in that XCD's L2.
+    const int tiles = gridDim.x / g.S;
+    const int lin = xcd_tile(blockIdx.x, gridDim.x);
+    const int slab = lin / tiles, tile = lin - slab * tiles;
+    const int tn = tile % g.tiles_n, tm = tile / g.tiles_n;
     const int oc0 = tm * BM, k0 = tn * BN;
-    const int p_begin = blockIdx.z * g.Pc;
+    const int p_begin = slab * g.Pc;
     const int p_end = min(g.P, p_begin + g.Pc);
     const bool do_db = want_db && tn == 0;
     const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
         compute(k);
     }
 
-    float* dst = part + (int64_t)blockIdx.z * g.OC * g.Kdim;
+    float* dst = part + (int64_t)slab * g.OC * g.Kdim;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -471,7 +478,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
         if (t < BM && oc0 + t < g.OC) {
             float s_ = 0.0f;
             for (int q = 0; q < NT / CA; ++q) s_ += red[q * BM + t];
-            part_db[(int64_t)blockIdx.z * g.OC + oc0 + t] = s_;
+            part_db[(int64_t)slab * g.OC + oc0 + t] = s_;
         }
     }
 }
@@ -542,7 +549,7 @@ hipError_t launch_dw2(const T* x, const T* dz, const DwGeom& g, const ConvDims& 
                       float* part_db, int want_db, hipStream_t s) {
     constexpr int WN = (BM == 128 || BN == 64) ? 2 : 4;
     constexpr int WM = 4 / WN;
-    dim3 grid(p.tiles_m * p.tiles_n, 1, p.S);
+    dim3 grid(p.tiles_m * p.tiles_n * p.S);
     dw2_kernel<T, BM, BN, WM, WN><<<grid, NT, 0, s>>>(x, dz, g, make_fastdiv(d.OW), make_fastdiv(d.OH),
                                                       make_fastdiv(d.IC), make_fastdiv(d.KW), part, part_db,
                                                       want_db);
@@ -576,7 +583,7 @@ hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, flo
                            const ConvDims& d, void* ws, hipStream_t s) {
     const Plan p = plan(dt, d);
     DwGeom g{d.N, d.H, d.W, d.IC, d.OC, d.KW, d.sh, d.sw, d.ph, d.pw, d.OH, d.OW,
-             d.KH * d.KW * d.IC, d.N * d.OH * d.OW, p.Pc, p.tiles_n};
+             d.KH * d.KW * d.IC, d.N * d.OH * d.OW, p.Pc, p.tiles_n, p.S};
     float* part = (float*)ws;
     float* part_db = (float*)((char*)ws + align_up((size_t)p.S * d.OC * g.Kdim * 4, 256));
     const int want_db = db != nullptr;
