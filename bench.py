@@ -263,7 +263,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4", choices=sorted(WL.WORKLOADS))
-    ap.add_argument("--cpu-images", type=int, default=2, help="images of the batch the oracle baseline runs")
+    ap.add_argument("--cpu-images", type=int, default=64, help="images of the batch the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bn", action="store_true", help="skip the batch-norm statistics measurement")
     ap.add_argument("--only", choices=("forward", "activation_backward", "backward_data", "backward_weight"))
