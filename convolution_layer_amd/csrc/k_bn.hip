@@ -7,16 +7,18 @@
 // bn_stats_training / bn_training_backward kernels in the rl_tools conv2d CUDA
 // listing, "operations_cuda.h"), each workgroup streams a contiguous slab of rows with
 // 16-byte loads across all channels, keeps per-lane partial sums, merges its rows in
-// LDS in a fixed order and writes one partial per channel.  A second kernel merges the
-// slab partials per channel in fp64, in slab order.  Summation order therefore depends
-// only on the shape: results are bitwise reproducible.
+// LDS in a fixed order and writes one partial per channel; a second small launch merges
+// the slab partials per channel in fp64 in a fixed order.  (A single launch whose last
+// workgroup merges, signalled through a device-scope atomic, measured several times
+// slower here: the cross-XCD fences and atomics cost more than the second launch.)
+// Summation order depends only on the shape: results are bitwise reproducible.
 #include "internal.hpp"
 
 namespace convmi {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTargetBlocks = 1024;  // row slabs: 4 workgroups per CU over 256 CUs
+constexpr int kTargetBlocks = 512;  // row slabs: two workgroups per CU over 256 CUs
 
 template <typename T, int VEC> struct Vec;
 template <> struct Vec<float, 4> {
@@ -65,33 +67,40 @@ __device__ __forceinline__ void merge_rows(float* red, int rpi, int width, int r
     }
 }
 
-// Per-slab sums over rows of (z - shift_c) and (z - shift_c)^2, shift_c = z[0][c]
-// (shifted sums keep E[z^2] - E[z]^2 free of cancellation when |mean| >> std).
-// part layout: [C][2][blocks] so the per-channel merge reads contiguously.
-template <typename T, int VEC>
-__global__ __launch_bounds__(kThreads) void bn_stats_partials(const T* __restrict__ z, int64_t M, int C, int tpr,
-                                                              int rpi, int64_t rows_per_block,
-                                                              float* __restrict__ part) {
-    extern __shared__ float red[];  // [rpi][tpr*VEC*2]
+// Per-slab sums of two quantities per channel over a slab of rows, merged across the
+// workgroup's row groups in a fixed order and written to part[c][q][slab] (q = 0, 1).
+// Each lane streams UNROLL 16-byte vectors per iteration.
+template <typename T, int VEC, class Acc>
+__device__ __forceinline__ void slab_partials(const T* __restrict__ a, const T* __restrict__ b, int64_t M, int C,
+                                              int tpr, int rpi, int64_t rows_per_block, Acc accf,
+                                              float* __restrict__ part, float* red) {
+    constexpr int UNROLL = 4;
     const int t = threadIdx.x, cv = t % tpr, r = t / tpr;
     const int c0 = (blockIdx.y * tpr + cv) * VEC;
     const bool active = r < rpi && c0 < C;
     const int64_t m0 = (int64_t)blockIdx.x * rows_per_block;
     const int64_t m1 = m0 + rows_per_block < M ? m0 + rows_per_block : M;
-    float s1[VEC], s2[VEC], sh[VEC];
+    float s1[VEC], s2[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) s1[j] = s2[j] = 0.0f;
     if (active) {
-        Vec<T, VEC>::load(z + c0, sh);
-        for (int64_t m = m0 + r; m < m1; m += rpi) {
-            float v[VEC];
-            Vec<T, VEC>::load(z + m * C + c0, v);
+        accf.init(c0);
+        int64_t m = m0 + r;
+        for (; m + (UNROLL - 1) * rpi < m1; m += UNROLL * rpi) {
+            float va[UNROLL][VEC], vb[UNROLL][VEC];
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                float dd = v[j] - sh[j];
-                s1[j] += dd;
-                s2[j] = __builtin_fmaf(dd, dd, s2[j]);
+            for (int u = 0; u < UNROLL; ++u) {
+                Vec<T, VEC>::load(a + (m + u * rpi) * C + c0, va[u]);
+                if (b) Vec<T, VEC>::load(b + (m + u * rpi) * C + c0, vb[u]);
             }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) accf.add(va[u], vb[u], s1, s2);
+        }
+        for (; m < m1; m += rpi) {
+            float va[VEC], vb[VEC];
+            Vec<T, VEC>::load(a + m * C + c0, va);
+            if (b) Vec<T, VEC>::load(b + m * C + c0, vb);
+            accf.add(va, vb, s1, s2);
         }
     }
     const int width = tpr * VEC * 2, slot = cv * VEC * 2;
@@ -104,53 +113,152 @@ __global__ __launch_bounds__(kThreads) void bn_stats_partials(const T* __restric
     merge_rows(red, rpi, width, r, slot, VEC * 2, active);
     if (active && r == 0)
         for (int j = 0; j < VEC; ++j) {
-            int c = c0 + j;
+            const int c = c0 + j;
             part[((int64_t)c * 2 + 0) * gridDim.x + blockIdx.x] = red[slot + 2 * j];
             part[((int64_t)c * 2 + 1) * gridDim.x + blockIdx.x] = red[slot + 2 * j + 1];
         }
 }
 
-// Sum `n` partials starting at p (fp64, fixed order: thread-strided then tree).
-__device__ double block_sum_f64(const float* __restrict__ p, int n, double* red) {
-    double a = 0.0;
-    for (int i = threadIdx.x; i < n; i += kThreads) a += (double)p[i];
-    red[threadIdx.x] = a;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+// Shifted sums for the statistics: shift_c = z[0][c] keeps E[(z-s)^2] - E[z-s]^2 free of
+// cancellation when |mean| >> std.
+template <typename T, int VEC> struct StatsAcc {
+    const T* z;
+    float sh[VEC];
+    __device__ __forceinline__ void init(int c0) { Vec<T, VEC>::load(z + c0, sh); }
+    __device__ __forceinline__ void add(const float* v, const float*, float* s1, float* s2) const {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const float d = v[j] - sh[j];
+            s1[j] += d;
+            s2[j] = __builtin_fmaf(d, d, s2[j]);
+        }
+    }
+};
+
+// Sums of dno and dno*zhat for the batch-norm backward.
+template <typename T, int VEC, int ACT> struct BwdAcc {
+    const float *gamma, *beta, *mean, *inv_std;
+    float g[VEC], bt[VEC], mu[VEC], is[VEC];
+    __device__ __forceinline__ void init(int c0) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j]; mu[j] = mean[c0 + j]; is[j] = inv_std[c0 + j];
+        }
+    }
+    __device__ __forceinline__ void add(const float* zv, const float* gv, float* s1, float* s2) const {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            float zh;
+            const float a = bn_affine(zv[j], mu[j], is[j], g[j], bt[j], &zh);
+            const float dno = act_slope<ACT>(a) * gv[j];
+            s1[j] += dno;
+            s2[j] = __builtin_fmaf(dno, zh, s2[j]);
+        }
+    }
+};
+
+// Merge the slab partials per channel in fp64: each workgroup takes a contiguous group of
+// channels; for each pass of up to kThreads of them, P2 threads per channel (a power of
+// two) take slabs j, j + P2, ... in order and their sums are combined in thread order.
+// fin(c, S1, S2) runs once per channel.
+template <class Fin>
+__device__ __forceinline__ void merge_slabs(const float* __restrict__ part, int slabs, int C, double* dred,
+                                            Fin fin) {
+    const int t = threadIdx.x;
+    const int cpb = (C + gridDim.x - 1) / gridDim.x;  // channels of this workgroup
+    const int c_lo = blockIdx.x * cpb, c_hi = c_lo + cpb < C ? c_lo + cpb : C;
+    for (int cb = c_lo; cb < c_hi; cb += kThreads) {
+        const int pass_c = c_hi - cb < kThreads ? c_hi - cb : kThreads;
+        int p2 = 1;
+        while (p2 * 2 * pass_c <= kThreads) p2 *= 2;
+        const int cl = t / p2, j = t % p2, c = cb + cl;
+        const bool own = cl < pass_c;
+        double a = 0.0, b = 0.0;
+        if (own) {
+            const float* p1 = part + (int64_t)c * 2 * slabs;
+            for (int k = j; k < slabs; k += p2) {
+                a += (double)p1[k];
+                b += (double)p1[slabs + k];
+            }
+        }
+        dred[2 * t] = a;
+        dred[2 * t + 1] = b;
+        __syncthreads();
+        for (int h = p2 / 2; h > 0; h >>= 1) {  // fixed-order tree over the P2 partial sums
+            if (j < h) {
+                dred[2 * t] += dred[2 * (t + h)];
+                dred[2 * t + 1] += dred[2 * (t + h) + 1];
+            }
+            __syncthreads();
+        }
+        if (own && j == 0) fin(c, dred[2 * t], dred[2 * t + 1]);
         __syncthreads();
     }
-    double r = red[0];
-    __syncthreads();
-    return r;
 }
 
-// One workgroup per channel: merge slab partials; mean = shift + S1/M,
-// var = S2/M - (S1/M)^2 (biased, clamped at 0), inv_std = 1/sqrt(var + eps), running
-// statistics updated with momentum.
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void bn_stats_partials(const T* __restrict__ z, int64_t M, int C, int tpr,
+                                                              int rpi, int64_t rows_per_block,
+                                                              float* __restrict__ part) {
+    extern __shared__ float red[];
+    StatsAcc<T, VEC> acc{z, {}};
+    slab_partials<T, VEC>(z, (const T*)nullptr, M, C, tpr, rpi, rows_per_block, acc, part, red);
+}
+
+// Statistics from the slab partials (one workgroup per kThreads/P2 channels):
+// mean = shift + S1/M, biased var = S2/M - (S1/M)^2 (clamped at 0), inv_std =
+// 1/sqrt(var + eps), running statistics with momentum.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void bn_stats_finalize(const float* __restrict__ part, int blocks,
+__global__ __launch_bounds__(kThreads) void bn_stats_finalize(const float* __restrict__ part, int slabs, int C,
                                                               const T* __restrict__ z, int64_t M, float momentum,
                                                               float eps, float* __restrict__ mean,
                                                               float* __restrict__ inv_std,
                                                               float* __restrict__ run_mean,
                                                               float* __restrict__ run_var) {
-    __shared__ double red[kThreads];
-    const int c = blockIdx.x;
-    double S1 = block_sum_f64(part + (int64_t)c * 2 * blocks, blocks, red);
-    double S2 = block_sum_f64(part + ((int64_t)c * 2 + 1) * blocks, blocks, red);
-    if (threadIdx.x == 0) {
-        double d = S1 / (double)M;
+    __shared__ double dred[2 * kThreads];
+    merge_slabs(part, slabs, C, dred, [&](int c, double S1, double S2) {
+        const double d = S1 / (double)M;
         double var = S2 / (double)M - d * d;
         if (var < 0.0) var = 0.0;
-        double mu = (double)to_f32(z[c]) + d;
+        const double mu = (double)to_f32(z[c]) + d;
         mean[c] = (float)mu;
         inv_std[c] = (float)(1.0 / sqrt(var + (double)eps));
         if (run_mean) {
             run_mean[c] = (float)((1.0 - (double)momentum) * (double)run_mean[c] + (double)momentum * mu);
             run_var[c] = (float)((1.0 - (double)momentum) * (double)run_var[c] + (double)momentum * var);
         }
-    }
+    });
+}
+
+// Batch-norm backward, first launch: slab partials of A = sum dno and B = sum dno*zhat.
+template <typename T, int VEC, int ACT>
+__global__ __launch_bounds__(kThreads) void bn_bwd_partials(const T* __restrict__ z, const T* __restrict__ dy,
+                                                            int64_t M, int C, int tpr, int rpi, int64_t rows_per_block,
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta,
+                                                            const float* __restrict__ mean,
+                                                            const float* __restrict__ inv_std,
+                                                            float* __restrict__ part) {
+    extern __shared__ float red[];
+    BwdAcc<T, VEC, ACT> acc{gamma, beta, mean, inv_std, {}, {}, {}, {}};
+    slab_partials<T, VEC>(z, dy, M, C, tpr, rpi, rows_per_block, acc, part, red);
+}
+
+// Second launch: dgamma (+)= B, dbeta (+)= A and the coefficients of
+// dz = gamma*inv_std*(dno - A/M - zhat*B/M) into coef[c][3].
+__global__ __launch_bounds__(kThreads) void bn_bwd_finalize(const float* __restrict__ part, int slabs, int C, int64_t M,
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ inv_std,
+                                                            float* __restrict__ dgamma, float* __restrict__ dbeta,
+                                                            int accumulate, float* __restrict__ coef) {
+    __shared__ double dred[2 * kThreads];
+    merge_slabs(part, slabs, C, dred, [&](int c, double A, double B) {
+        if (dgamma) dgamma[c] = accumulate ? (float)((double)dgamma[c] + B) : (float)B;
+        if (dbeta) dbeta[c] = accumulate ? (float)((double)dbeta[c] + A) : (float)A;
+        coef[3 * c + 0] = gamma[c] * inv_std[c];
+        coef[3 * c + 1] = (float)(A / (double)M);
+        coef[3 * c + 2] = (float)(B / (double)M);
+    });
 }
 
 // y = act(a) with a = z or the batch-norm affine; grid-stride over 16-byte vectors.
@@ -160,20 +268,37 @@ __global__ __launch_bounds__(kThreads) void apply_act(const T* __restrict__ z, T
                                                       const float* __restrict__ beta,
                                                       const float* __restrict__ mean,
                                                       const float* __restrict__ inv_std) {
-    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    // channel of the first element, stepped by the grid stride (the per-channel
+    // parameters are reloaded only when it changes: never, when C divides the stride)
+    int c0 = (int)((v * VEC) % C), cached = -1;
+    const int step = (int)((stride * VEC) % C);
+    float mu[VEC], is[VEC], g[VEC], bt[VEC];
+    for (; v < nvec; v += stride) {
         float a[VEC];
         Vec<T, VEC>::load(z + v * VEC, a);
-        const int c0 = (int)((v * VEC) % C);
+        if constexpr (BN) {
+            if (c0 != cached) {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    mu[j] = mean[c0 + j]; is[j] = inv_std[c0 + j]; g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j];
+                }
+                cached = c0;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
             float in = a[j];
             if constexpr (BN) {
                 float zh;
-                in = bn_affine(in, mean[c0 + j], inv_std[c0 + j], gamma[c0 + j], beta[c0 + j], &zh);
+                in = bn_affine(in, mu[j], is[j], g[j], bt[j], &zh);
             }
             a[j] = act_fwd<ACT>(in);
         }
         Vec<T, VEC>::store(y + v * VEC, a);
+        c0 += step;
+        if (c0 >= C) c0 -= C;
     }
 }
 
@@ -190,80 +315,7 @@ __global__ __launch_bounds__(kThreads) void act_bwd(const T* __restrict__ z, con
     }
 }
 
-// Batch-norm backward, pass 1: per-slab sums of dno and dno*zhat, where
-// zhat = (z-mean)*inv_std, a = gamma*zhat + beta, dno = act'(a)*dy.
-template <typename T, int VEC, int ACT>
-__global__ __launch_bounds__(kThreads) void bn_bwd_partials(const T* __restrict__ z, const T* __restrict__ dy,
-                                                            int64_t M, int C, int tpr, int rpi,
-                                                            int64_t rows_per_block, const float* __restrict__ gamma,
-                                                            const float* __restrict__ beta,
-                                                            const float* __restrict__ mean,
-                                                            const float* __restrict__ inv_std,
-                                                            float* __restrict__ part) {
-    extern __shared__ float red[];
-    const int t = threadIdx.x, cv = t % tpr, r = t / tpr;
-    const int c0 = (blockIdx.y * tpr + cv) * VEC;
-    const bool active = r < rpi && c0 < C;
-    const int64_t m0 = (int64_t)blockIdx.x * rows_per_block;
-    const int64_t m1 = m0 + rows_per_block < M ? m0 + rows_per_block : M;
-    float sa[VEC], sb[VEC], g[VEC], bt[VEC], mu[VEC], is[VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) sa[j] = sb[j] = 0.0f;
-    if (active) {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j]; mu[j] = mean[c0 + j]; is[j] = inv_std[c0 + j];
-        }
-        for (int64_t m = m0 + r; m < m1; m += rpi) {
-            float zv[VEC], gv[VEC];
-            Vec<T, VEC>::load(z + m * C + c0, zv);
-            Vec<T, VEC>::load(dy + m * C + c0, gv);
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                float zh, a = bn_affine(zv[j], mu[j], is[j], g[j], bt[j], &zh);
-                float dno = act_slope<ACT>(a) * gv[j];
-                sa[j] += dno;
-                sb[j] = __builtin_fmaf(dno, zh, sb[j]);
-            }
-        }
-    }
-    const int width = tpr * VEC * 2, slot = cv * VEC * 2;
-    if (active)
-        for (int j = 0; j < VEC; ++j) {
-            red[r * width + slot + 2 * j] = sa[j];
-            red[r * width + slot + 2 * j + 1] = sb[j];
-        }
-    __syncthreads();
-    merge_rows(red, rpi, width, r, slot, VEC * 2, active);
-    if (active && r == 0)
-        for (int j = 0; j < VEC; ++j) {
-            int c = c0 + j;
-            part[((int64_t)c * 2 + 0) * gridDim.x + blockIdx.x] = red[slot + 2 * j];
-            part[((int64_t)c * 2 + 1) * gridDim.x + blockIdx.x] = red[slot + 2 * j + 1];
-        }
-}
-
-// Pass 2: per channel A = sum dno, B = sum dno*zhat; dgamma (+)= B, dbeta (+)= A;
-// coefficients for dz = gamma*inv_std*(dno - A/M - zhat*B/M) into coef[c][3].
-__global__ __launch_bounds__(kThreads) void bn_bwd_finalize(const float* __restrict__ part, int blocks, int64_t M,
-                                                            const float* __restrict__ gamma,
-                                                            const float* __restrict__ inv_std,
-                                                            float* __restrict__ dgamma, float* __restrict__ dbeta,
-                                                            int accumulate, float* __restrict__ coef) {
-    __shared__ double red[kThreads];
-    const int c = blockIdx.x;
-    double A = block_sum_f64(part + (int64_t)c * 2 * blocks, blocks, red);
-    double B = block_sum_f64(part + ((int64_t)c * 2 + 1) * blocks, blocks, red);
-    if (threadIdx.x == 0) {
-        if (dgamma) dgamma[c] = accumulate ? (float)((double)dgamma[c] + B) : (float)B;
-        if (dbeta) dbeta[c] = accumulate ? (float)((double)dbeta[c] + A) : (float)A;
-        coef[3 * c + 0] = gamma[c] * inv_std[c];
-        coef[3 * c + 1] = (float)(A / (double)M);
-        coef[3 * c + 2] = (float)(B / (double)M);
-    }
-}
-
-// Pass 3: dz = k0*(dno - k1 - zhat*k2) elementwise.
+// Third launch: dz = k0*(dno - k1 - zhat*k2) elementwise.
 template <typename T, int VEC, int ACT>
 __global__ __launch_bounds__(kThreads) void bn_bwd_apply(const T* __restrict__ z, const T* dy, T* dz, int64_t nvec,
                                                          int C, const float* __restrict__ gamma,
@@ -271,19 +323,33 @@ __global__ __launch_bounds__(kThreads) void bn_bwd_apply(const T* __restrict__ z
                                                          const float* __restrict__ mean,
                                                          const float* __restrict__ inv_std,
                                                          const float* __restrict__ coef) {
-    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    int c0 = (int)((v * VEC) % C), cached = -1;
+    const int step = (int)((stride * VEC) % C);
+    float mu[VEC], is[VEC], g[VEC], bt[VEC], k0[VEC], k1[VEC], k2[VEC];
+    for (; v < nvec; v += stride) {
         float zv[VEC], gv[VEC];
         Vec<T, VEC>::load(z + v * VEC, zv);
         Vec<T, VEC>::load(dy + v * VEC, gv);
-        const int c0 = (int)((v * VEC) % C);
+        if (c0 != cached) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const int c = c0 + j;
+                mu[j] = mean[c]; is[j] = inv_std[c]; g[j] = gamma[c]; bt[j] = beta[c];
+                k0[j] = coef[3 * c]; k1[j] = coef[3 * c + 1]; k2[j] = coef[3 * c + 2];
+            }
+            cached = c0;
+        }
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
-            const int c = c0 + j;
-            float zh, a = bn_affine(zv[j], mean[c], inv_std[c], gamma[c], beta[c], &zh);
+            float zh, a = bn_affine(zv[j], mu[j], is[j], g[j], bt[j], &zh);
             float dno = act_slope<ACT>(a) * gv[j];
-            gv[j] = coef[3 * c] * (dno - coef[3 * c + 1] - zh * coef[3 * c + 2]);
+            gv[j] = k0[j] * (dno - k1[j] - zh * k2[j]);
         }
         Vec<T, VEC>::store(dz + v * VEC, gv);
+        c0 += step;
+        if (c0 >= C) c0 -= C;
     }
 }
 
@@ -295,6 +361,14 @@ int elementwise_grid(int64_t nvec) {
 }
 
 size_t partial_bytes(const RowPlan& p, int C) { return align_up((size_t)C * 2 * p.blocks * sizeof(float), 256); }
+
+// Workgroups for the per-channel merge: up to 64 channels each, at least 64 workgroups
+// when there are that many channels.
+int merge_grid(int C) {
+    int g = (int)ceil_div(C, 64);
+    const int g2 = C < 64 ? C : 64;
+    return g > g2 ? g : g2;
+}
 
 }  // namespace
 
@@ -343,11 +417,11 @@ hipError_t launch_bn_stats(int dt, const void* z, int64_t M, int C, float moment
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dt == DT_BF16)
-        bn_stats_finalize<bf16><<<C, kThreads, 0, s>>>(part, p.blocks, (const bf16*)z, M, momentum, eps, mean,
-                                                       inv_std, run_mean, run_var);
+        bn_stats_finalize<bf16><<<merge_grid(C), block, 0, s>>>(part, p.blocks, C, (const bf16*)z, M, momentum, eps,
+                                                                mean, inv_std, run_mean, run_var);
     else
-        bn_stats_finalize<float><<<C, kThreads, 0, s>>>(part, p.blocks, (const float*)z, M, momentum, eps, mean,
-                                                        inv_std, run_mean, run_var);
+        bn_stats_finalize<float><<<merge_grid(C), block, 0, s>>>(part, p.blocks, C, (const float*)z, M, momentum,
+                                                                 eps, mean, inv_std, run_mean, run_var);
     return hipGetLastError();
 }
 
@@ -392,7 +466,8 @@ hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_
                                                                       part))));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    bn_bwd_finalize<<<C, kThreads, 0, s>>>(part, p.blocks, M, gamma, inv_std, dgamma, dbeta, accumulate, coef);
+    bn_bwd_finalize<<<merge_grid(C), block, 0, s>>>(part, p.blocks, C, M, gamma, inv_std, dgamma, dbeta, accumulate,
+                                                    coef);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nvec = M * C / p.vec;
