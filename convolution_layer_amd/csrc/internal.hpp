@@ -73,4 +73,19 @@ hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, cons
 hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, float* db, int accumulate,
                            const ConvDims& d, void* ws, hipStream_t s);
 
+// ---------------------------------------------------------------- stride-1 input-tile reuse
+// Forward and input gradient of stride-1 layers whose gathered channels fill 128-byte
+// chunks: each input tile + halo is copied to LDS once per chunk and shared by all taps.
+// bf16 rearranges the weights into MFMA fragment order in the workspace first (ws bytes
+// below); fp32 reads w (forward) or the rearranged input-gradient weights of the generic
+// path (backward, passed as w) directly.
+bool halo_fwd_supported(int dt, const ConvDims& d);
+bool halo_dx_supported(int dt, const ConvDims& d);
+size_t halo_fwd_ws_bytes(int dt, const ConvDims& d);
+size_t halo_dx_ws_bytes(int dt, const ConvDims& d);
+hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
+                           const ConvDims& d, int act, void* ws, hipStream_t s);
+hipError_t launch_halo_dx(int dt, const void* dz, const void* w, void* dx, const ConvDims& d, void* ws,
+                          hipStream_t s);
+
 }  // namespace convmi

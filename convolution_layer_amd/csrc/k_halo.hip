@@ -1,0 +1,845 @@
+// k_halo.hip -- stride-1 convolution forward and input gradient with input-tile reuse.
+//
+// For a stride-1 layer the implicit-GEMM operand A of every tap (kh, kw) is one input
+// rectangle shifted by (kh, kw).  The per-tap gather of the generic MFMA kernel reads that
+// rectangle KH*KW times.  Here an output tile is an R x Q rectangle of one image; for each
+// 128-byte channel chunk the tile's input rectangle plus its halo, (R + KH - 1) x
+// (Q + KW - 1) positions, is copied into LDS once, and every tap reads its MFMA fragments
+// from it at shifted positions.  Only the weights stream per tap.  With four whole
+// 56-pixel rows per tile this loads about a third of the bytes per FLOP of the per-tap
+// gather; on gfx950 the vector-memory address path, not the MFMA or the LDS, is what the
+// gather saturates first.
+//
+// Forward: out(n, oh, ow, oc) = sum_{kh,kw,ic} w[oc, kh, kw, ic] x[n, oh - ph + kh, ow - pw + kw, ic]
+//   halo origin (oh0 - ph, ow0 - pw); tap (kh, kw) sits at halo offset (kh, kw).
+// Input gradient: dx(n, ih, iw, ic) = sum_{kh,kw,oc} w[oc, kh, kw, ic] dz[n, ih + ph - kh, iw + pw - kw, oc]
+//   halo origin (ih0 + ph - KH + 1, iw0 + pw - KW + 1); tap (kh, kw) sits at offset
+//   (KH - 1 - kh, KW - 1 - kw); the weight operand is the rearranged copy
+//   Bt[ic][(kh, kw, oc)] = w[oc, kh, kw, ic] that the generic input-gradient path builds.
+// Definitions: rl_tools conv2d listings "operations_generic.h" (forward, backward_input)
+// and "operations_cuda.h" (forward with bias and activation; backward_input).
+//
+// Pipeline: steps (chunk c, tap t), c outer.  Weight tiles (BN rows x 128 bytes) go
+// through a two-slot LDS ring, one step ahead.  With two halo buffers the halo of chunk
+// c + 1 is copied during chunk c; with one it is copied after the last tap of chunk c and
+// a second workgroup on the CU covers the gap.  All copies are 16-byte LDS-DMA with
+// XOR-swizzled 16-byte chunks; each wave counts the copies it has issued and waits for
+// exactly the ones the next step reads.  The epilogue stages the tile in LDS in the
+// storage type (the activation reads the stored pre-activation, so staging the rounded
+// value loses nothing) and writes 16-byte vectors.
+#include "internal.hpp"
+#include "lds_dma.hpp"
+
+namespace convmi {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// MFMA flavours.  MF = rows (and columns) of one output fragment.  A lane of group
+// lg = lane / MF holds row lane % MF of its operand fragments, one 16-byte chunk of k;
+// the 128-byte k chunk of a step is covered in 8 / (64 / MF) MFMA k-steps.
+//   MF = 16: fp32, 4 x v_mfma_f32_16x16x4_f32 per 16-byte vector (the four k of a lane's
+//            vector go to four MFMAs; A and B use the same order); accumulator element e
+//            of lane group lg is output row 4*lg + e.
+//   MF = 32: v_mfma_f32_32x32x16_bf16; accumulator element e of lane group lg is output
+//            row 8*(e/4) + 4*lg + e%4.
+template <typename T, int MF> struct HMma;
+template <> struct HMma<float, 16> {
+    typedef floatx4 Acc;
+    static constexpr int NE = 4;
+    static __device__ __forceinline__ void run(Acc& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int lg, int e) { return 4 * lg + e; }
+};
+template <> struct HMma<bf16, 32> {
+    typedef floatx16 Acc;
+    static constexpr int NE = 16;
+    static __device__ __forceinline__ void run(Acc& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                    0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int lg, int e) { return 8 * (e >> 2) + 4 * lg + (e & 3); }
+};
+
+// 16-byte chunk swizzle of a 128-byte LDS row: rows 2j and 2j+1 fall in different bank
+// halves, so any 16 consecutive rows read at one logical chunk hit distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+struct HaloGeom {
+    int Hin, Win, Cin;     // gathered tensor: x (forward) or dz (input gradient)
+    int KH, KW;
+    int Hout, Wout, Nn;    // output image size and output channels
+    int R, Q;              // output tile: R rows x Q columns
+    int HQ, HP, GH;        // halo row length (Q + KW - 1), positions, 8-position copy groups
+    int org_r, org_c;      // halo origin relative to the tile origin
+    int tiles_r, tiles_c;  // tiles per image
+    int nchunks;           // Cin / channels per 128-byte chunk
+    int Kb;                // weight row length KH*KW*Cin
+    int sign;              // +1 forward (tap at (kh, kw)), -1 input gradient (flipped)
+    int hb;                // halo buffers (1 or 2)
+    int64_t img_stride;    // Hin*Win*Cin
+    FastDiv fQ, fHQ, fTR, fTC;
+};
+
+template <typename T> __device__ __forceinline__ void put16(T* p, const float* v);
+template <> __device__ __forceinline__ void put16<float>(float* p, const float* v) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void put16<bf16>(bf16* p, const float* v) {
+    *(uint4*)p = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7]));
+}
+
+// z = stored(acc + bias), y = act(z).  `raw` holds 16 bytes of stored z of one pixel.
+struct HFwdOut {
+    void* z;            // nullable
+    void* y;            // nullable
+    const float* bias;  // nullable
+    int OC;
+    __device__ __forceinline__ float colbias(int col) const { return (bias && col < OC) ? bias[col] : 0.0f; }
+    template <typename T, int ACT>
+    __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv) const {
+        constexpr int VEC = 16 / (int)sizeof(T);
+        T v[VEC];
+        __builtin_memcpy(v, &raw, 16);
+        const int64_t off = pix * OC + col;
+        if (nv == VEC && OC % VEC == 0) {
+            if (z) *(uint4*)((T*)z + off) = raw;
+            if (y) {
+                float yr[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) yr[j] = act_fwd<ACT>(to_f32(v[j]));
+                put16<T>((T*)y + off, yr);
+            }
+        } else {
+            for (int j = 0; j < nv; ++j) {
+                if (z) ((T*)z)[off + j] = v[j];
+                if (y) ((T*)y)[off + j] = from_f32<T>(act_fwd<ACT>(to_f32(v[j])));
+            }
+        }
+    }
+};
+
+struct HDxOut {
+    void* dx;
+    int IC;
+    __device__ __forceinline__ float colbias(int) const { return 0.0f; }
+    template <typename T, int ACT>
+    __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv) const {
+        constexpr int VEC = 16 / (int)sizeof(T);
+        const int64_t off = pix * IC + col;
+        if (nv == VEC && IC % VEC == 0) {
+            *(uint4*)((T*)dx + off) = raw;
+        } else {
+            T v[VEC];
+            __builtin_memcpy(v, &raw, 16);
+            for (int j = 0; j < nv; ++j) ((T*)dx)[off + j] = v[j];
+        }
+    }
+};
+
+constexpr int kThreadsH = 256;  // four waves, WM x WN
+
+// Two workgroups per CU must fit the register file: at most 256 registers per lane.
+template <typename T, int MF, int BM, int BN, int WM, int WN, int ACT, class Out>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_kernel(
+    const T* __restrict__ A, HaloGeom g, const T* __restrict__ B, Out out, int tiles_n) {
+    using MM = HMma<T, MF>;
+    using Acc = typename MM::Acc;
+    constexpr int NWAVE = WM * WN, NTH = kThreadsH;
+    static_assert(NWAVE * 64 == NTH, "four waves");
+    constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+    constexpr int CK = 8 * VEC;               // channels per 128-byte chunk
+    constexpr int LG = 64 / MF;               // lane groups (16-byte k chunks per MFMA)
+    constexpr int KST = 8 / LG;               // MFMA k-steps per 128-byte chunk
+    constexpr int TM = BM / (WM * MF), TN = BN / (WN * MF);
+    static_assert(TM * WM * MF == BM && TN * WN * MF == BN, "tile shape");
+    static_assert(BN % 8 == 0, "8-row copy groups");
+    constexpr int GB = BN / 8;  // 1-KB weight copies per step
+    extern __shared__ __align__(1024) unsigned char smem[];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int halo_bytes = g.GH * 1024;
+    const bool two = g.hb == 2;
+    const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    const uint32_t w_base = smem_base + g.hb * halo_bytes;
+
+    // tile -> (image, tile row, tile column, column tile); consecutive tiles share an XCD
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int tn = tile % tiles_n;
+    const int sp = tile / tiles_n;
+    const int qsp = fdiv(sp, g.fTC);
+    const int tc = sp - qsp * g.tiles_c;
+    const int n = fdiv(qsp, g.fTR);
+    const int tr = qsp - n * g.tiles_r;
+    const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
+    const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
+    const T* Aimg = A + (int64_t)n * g.img_stride;
+    const int nsteps = g.nchunks * g.KH * g.KW;
+
+    // Copy group grp covers 8 LDS rows (halo positions or weight rows) 8*grp .. 8*grp+7;
+    // lane l copies 16-byte chunk l%8 of row 8*grp + l/8.  Each returns this wave's copies.
+    const int rg = lane >> 3, pc = lane & 7;
+    auto issue_halo = [&](int c) -> int {
+        const uint32_t dstb = smem_base + (uint32_t)((two ? (c & 1) : 0) * halo_bytes);
+        int cnt = 0;
+        for (int grp = wid; grp < g.GH; grp += NWAVE, ++cnt) {
+            const int p = grp * 8 + rg;
+            const void* src = &kZero16;
+            if (p < g.HP) {
+                const int hr = fdiv(p, g.fHQ);
+                const int ih = hr0 + hr, iw = hc0 + (p - hr * g.HQ);
+                if ((unsigned)ih < (unsigned)g.Hin && (unsigned)iw < (unsigned)g.Win)
+                    src = Aimg + ((int64_t)ih * g.Win + iw) * g.Cin + c * CK + (pc ^ swz(p)) * VEC;
+            }
+            dma16(src, __builtin_amdgcn_readfirstlane(dstb + grp * 1024));
+        }
+        return cnt;
+    };
+    // weight tiles are issued strictly in step order; (wc, wkh, wkw) is the next one
+    int wst = 0, wc = 0, wtap = 0;
+    const int taps = g.KH * g.KW;
+    auto issue_w = [&]() -> int {
+        const int kofs = wtap * g.Cin + wc * CK;
+        const uint32_t dstb = w_base + (uint32_t)((wst & 1) * BN * 128);
+        int cnt = 0;
+        for (int grp = wid; grp < GB; grp += NWAVE, ++cnt) {
+            const int r = grp * 8 + rg;
+            const int nr = n0 + r;
+            const void* src = nr < g.Nn ? (const void*)(B + (int64_t)nr * g.Kb + kofs + (pc ^ swz(r)) * VEC)
+                                        : (const void*)&kZero16;
+            dma16(src, __builtin_amdgcn_readfirstlane(dstb + grp * 1024));
+        }
+        ++wst;
+        if (++wtap == taps) {
+            wtap = 0;
+            ++wc;
+        }
+        return cnt;
+    };
+
+    // LDS fragment sources of this lane: A rows are output pixels m = rr*Q + qq of the
+    // tile (halo position rr*HQ + qq before the tap shift), B rows are output channels.
+    const int wm = wid / WN, wn = wid % WN;
+    const int lr = lane % MF, lg = lane / MF;
+    int hpos[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        int m = wm * TM * MF + i * MF + lr;
+        if (m >= g.R * g.Q) m = 0;  // rows past the tile read a valid position; never stored
+        const int rr = fdiv(m, g.fQ);
+        hpos[i] = rr * g.HQ + (m - rr * g.Q);
+    }
+    int boff[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * MF + j * MF + lr;
+        boff[j] = r * 128 + (swz(r) << 4);  // xor-able: swz(r) << 4 < 128
+    }
+
+    Acc acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < MM::NE; ++e) acc[i][j][e] = 0.0f;
+
+    // Fragment reads are software-pipelined: the reads of k-step kk + 1 are issued before
+    // the MFMAs of kk, and the reads of the next step's first k-step before the MFMAs of
+    // the current step's last one.  The barrier that hands over a weight slot sits just
+    // before those last MFMAs, so its wait overlaps MFMAs already in flight.
+    uint4 fa[2][TM], fb[2][TN];
+    auto tap_off = [&](int kh_, int kw_) {
+        return g.sign > 0 ? kh_ * g.HQ + kw_ : (g.KH - 1 - kh_) * g.HQ + (g.KW - 1 - kw_);
+    };
+    auto read_frags = [&](const unsigned char* Hs, const unsigned char* Ws, int toff, int lc, uint4 (&a)[TM],
+                          uint4 (&b)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int p = hpos[i] + toff;
+            a[i] = *(const uint4*)(Hs + p * 128 + ((lc ^ swz(p)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = *(const uint4*)(Ws + (boff[j] ^ (lc << 4)));
+    };
+    auto mfmas = [&](const uint4 (&a)[TM], const uint4 (&b)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) MM::run(acc[i][j], a[i], b[j]);
+    };
+    auto halo_at = [&](int c_) { return smem + (two ? (c_ & 1) : 0) * halo_bytes; };
+    auto slot_at = [&](int st_) { return smem + g.hb * halo_bytes + (st_ & 1) * BN * 128; };
+
+    // Wave-local copy accounting: `issued` copies so far; e1 the count right after the
+    // next step's weight tile, eh_next right after the next chunk's halo.
+    int issued = issue_halo(0);
+    int eh_next = issued;
+    issued += issue_w();
+    const int e0 = issued;
+    int e1 = issued;
+    if (nsteps > 1) {
+        issued += issue_w();
+        e1 = issued;
+    }
+    if (two && g.nchunks > 1) {
+        issued += issue_halo(1);
+        eh_next = issued;
+    }
+    wait_dma(issued - e0);
+    __syncthreads();
+    read_frags(halo_at(0), slot_at(0), tap_off(0, 0), lg, fa[0], fb[0]);
+
+    int c = 0, kh = 0, kw = 0;
+    for (int st = 0; st < nsteps; ++st) {
+        const unsigned char* Hs = halo_at(c);
+        const unsigned char* Ws = slot_at(st);
+        const int toff = tap_off(kh, kw);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KST; ++kk) {
+            read_frags(Hs, Ws, toff, (kk + 1) * LG + lg, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(fa[kk & 1], fb[kk & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // next step (c, kh, kw) -> (c2, kh2, kw2)
+        int c2 = c, kh2 = kh, kw2 = kw + 1;
+        if (kw2 == g.KW) {
+            kw2 = 0;
+            if (++kh2 == g.KH) {
+                kh2 = 0;
+                ++c2;
+            }
+        }
+        if (st + 1 < nsteps) {
+            const bool boundary = c2 != c;
+            if (boundary && !two) {
+                // one halo buffer: every wave is done with chunk c's halo, reload it in place
+                wait_dma(issued - e1);
+                __syncthreads();
+                if (st + 2 < nsteps) issued += issue_w();
+                issued += issue_halo(c2);
+                wait_dma(0);
+                __syncthreads();
+                e1 = issued;
+            } else {
+                const int need = boundary && eh_next > e1 ? eh_next : e1;
+                wait_dma(issued - need);
+                __syncthreads();  // weight slot st and, at a boundary, halo c are free again
+                if (st + 2 < nsteps) issued += issue_w();
+                e1 = issued;
+                if (boundary && two && c2 + 1 < g.nchunks) {
+                    issued += issue_halo(c2 + 1);
+                    eh_next = issued;
+                }
+            }
+            read_frags(halo_at(c2), slot_at(st + 1), tap_off(kh2, kw2), lg, fa[KST & 1], fb[KST & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa[(KST - 1) & 1], fb[(KST - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        c = c2;
+        kh = kh2;
+        kw = kw2;
+    }
+    __syncthreads();
+
+    // epilogue: stored values -> LDS (rows of BN + 16 bytes) -> 16-byte vectors
+    constexpr int LDC = BN + VEC;
+    T* Cs = (T*)smem;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int cl = wn * TN * MF + j * MF + lr;
+        const float bj = out.colbias(n0 + cl);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < MM::NE; ++e)
+                Cs[(wm * TM * MF + i * MF + MM::row(lg, e)) * LDC + cl] = from_f32<T>(acc[i][j][e] + bj);
+    }
+    __syncthreads();
+    constexpr int OVR = BN / VEC;
+    static_assert(NTH % OVR == 0, "each thread keeps one column range");
+    const int cv = t % OVR, col = n0 + cv * VEC;
+    if (col >= g.Nn) return;
+    const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
+    const int RQ = g.R * g.Q;
+    for (int m = t / OVR; m < RQ; m += NTH / OVR) {
+        const int rr = fdiv(m, g.fQ);
+        const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
+        if (oh >= g.Hout || ow >= g.Wout) continue;
+        const int64_t pix = ((int64_t)n * g.Hout + oh) * g.Wout + ow;
+        const uint4 raw = *(const uint4*)(Cs + m * LDC + cv * VEC);
+        out.template put<T, ACT>(pix, col, raw, nv);
+    }
+}
+
+// bf16 variant without a per-step barrier.  The weights are first laid out in MFMA
+// fragment order (frag_weights below): the B fragment of 32 rows x 16 k that a wave needs
+// for one MFMA k-step is 1 KB contiguous, so every weight load instruction reads whole
+// cache lines.  Each wave loads its own B fragments straight into registers one step
+// ahead; LDS holds only the input halo, whose next chunk is copied in slices during the
+// current one (two buffers) or after it (one buffer).  Waves therefore only meet at chunk
+// boundaries, where each waits for all of its outstanding vector-memory operations:
+// LDS-DMA copies and register loads need not complete in issue order with respect to
+// each other, so a count that mixes the two kinds proves nothing.
+template <int BM, int BN, int WM, int WN, int ACT, class Out>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_rb_kernel(
+    const bf16* __restrict__ A, HaloGeom g, const uint4* __restrict__ Bf, Out out, int tiles_n) {
+    using MM = HMma<bf16, 32>;
+    using Acc = MM::Acc;
+    constexpr int MF = 32, NWAVE = 4, NTH = kThreadsH;
+    static_assert(WM * WN == NWAVE, "four waves");
+    constexpr int TM = BM / (WM * MF), TN = BN / (WN * MF);
+    static_assert(TM * WM * MF == BM && TN * WN * MF == BN, "tile shape");
+    constexpr int VEC = 8, CK = 64, KST = 4;  // 16-byte chunk = 8 bf16; 128-byte chunk = 4 MFMA k-steps
+    extern __shared__ __align__(1024) unsigned char smem[];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int halo_bytes = g.GH * 1024;
+    const bool two = g.hb == 2;
+    const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int tn = tile % tiles_n;
+    const int sp = tile / tiles_n;
+    const int qsp = fdiv(sp, g.fTC);
+    const int tc = sp - qsp * g.tiles_c;
+    const int n = fdiv(qsp, g.fTR);
+    const int tr = qsp - n * g.tiles_r;
+    const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
+    const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
+    const bf16* Aimg = A + (int64_t)n * g.img_stride;
+    const int taps = g.KH * g.KW;
+    const int nsteps = g.nchunks * taps;
+
+    // Halo copy: a chunk's halo is JH copy instructions per wave; instruction j of this
+    // wave covers halo positions 8*(wid + 4j) .. +7, lane l chunk l%8 of position l/8.
+    const int rg = lane >> 3, pc = lane & 7;
+    const int JH = (g.GH + NWAVE - 1) / NWAVE;
+    auto issue_halo = [&](int c, int j0, int j1) {
+        const uint32_t dstb = smem_base + (uint32_t)((two ? (c & 1) : 0) * halo_bytes);
+        for (int j = j0; j < j1; ++j) {
+            const int grp = wid + NWAVE * j;
+            if (grp >= g.GH) break;
+            const int p = grp * 8 + rg;
+            const void* src = &kZero16;
+            if (p < g.HP) {
+                const int hr = fdiv(p, g.fHQ);
+                const int ih = hr0 + hr, iw = hc0 + (p - hr * g.HQ);
+                if ((unsigned)ih < (unsigned)g.Hin && (unsigned)iw < (unsigned)g.Win)
+                    src = Aimg + ((int64_t)ih * g.Win + iw) * g.Cin + c * CK + (pc ^ swz(p)) * VEC;
+            }
+            dma16(src, __builtin_amdgcn_readfirstlane(dstb + grp * 1024));
+        }
+    };
+    const int parts = taps > 1 ? taps - 1 : 1;  // slices of the next halo per chunk
+
+    const int wm = wid / WN, wn = wid % WN;
+    const int lr = lane & 31, lg = lane >> 5;
+    int hpos[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        int m = wm * TM * MF + i * MF + lr;
+        if (m >= g.R * g.Q) m = 0;  // rows past the tile read a valid position; never stored
+        const int rr = fdiv(m, g.fQ);
+        hpos[i] = rr * g.HQ + (m - rr * g.Q);
+    }
+    // B fragments: 32-row group (n0 + wn*TN*32)/32 + j, step st, k-step kk at
+    // ((group * nsteps + st) * 4 + kk) * 64 + lane
+    const uint4* bq = Bf + (int64_t)((n0 + wn * TN * MF) / MF) * nsteps * (KST * 64) + lane;
+    const int64_t gstride = (int64_t)nsteps * (KST * 64);
+    auto load_b = [&](int st, uint4 (&dst)[TN][KST]) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int kk = 0; kk < KST; ++kk) dst[j][kk] = bq[j * gstride + (st * KST + kk) * 64];
+    };
+
+    Acc acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < MM::NE; ++e) acc[i][j][e] = 0.0f;
+
+    uint4 bA[TN][KST], bB[TN][KST];
+    issue_halo(0, 0, JH);
+    load_b(0, bA);
+    wait_dma(0);
+    __syncthreads();
+
+    auto step = [&](int st, const uint4 (&cur)[TN][KST], uint4 (&nxt)[TN][KST]) {
+        const int c = st / taps, tap = st - c * taps;
+        if (st + 1 < nsteps) load_b(st + 1, nxt);
+        const int kh = tap / g.KW, kw = tap - kh * g.KW;
+        const int toff = g.sign > 0 ? kh * g.HQ + kw : (g.KH - 1 - kh) * g.HQ + (g.KW - 1 - kw);
+        const unsigned char* Hs = smem + (two ? (c & 1) : 0) * halo_bytes;
+        int pa[TM], ps[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int p = hpos[i] + toff;
+            pa[i] = p * 128;
+            ps[i] = swz(p);
+        }
+        uint4 fa[2][TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[0][i] = *(const uint4*)(Hs + pa[i] + ((lg ^ ps[i]) << 4));
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk) {
+            if (kk + 1 < KST) {
+                const int lc = (kk + 1) * 2 + lg;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    fa[(kk + 1) & 1][i] = *(const uint4*)(Hs + pa[i] + ((lc ^ ps[i]) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) MM::run(acc[i][j], fa[kk & 1][i], cur[j][kk]);
+            // A slice of the next chunk's halo, issued after this step's first use of `cur`:
+            // the next wait for a weight load lies a full step ahead.
+            if (kk == 0 && two && c + 1 < g.nchunks && tap < parts)
+                issue_halo(c + 1, tap * JH / parts, (tap + 1) * JH / parts);
+        }
+        if (tap == taps - 1 && c + 1 < g.nchunks) {
+            if (two) {
+                wait_dma(0);      // this wave's slices of the next halo have landed
+                __syncthreads();  // ... and every wave's; the old halo is free again
+            } else {
+                __syncthreads();  // every wave is done with the halo of chunk c
+                issue_halo(c + 1, 0, JH);
+                wait_dma(0);
+                __syncthreads();
+            }
+        }
+    };
+    for (int st = 0; st < nsteps; st += 2) {
+        step(st, bA, bB);
+        if (st + 1 < nsteps) step(st + 1, bB, bA);
+    }
+    __syncthreads();
+
+    // epilogue: stored values -> LDS (rows of BN + 16 bytes) -> 16-byte vectors
+    constexpr int LDC = BN + VEC;
+    bf16* Cs = (bf16*)smem;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int cl = wn * TN * MF + j * MF + lr;
+        const float bj = out.colbias(n0 + cl);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < MM::NE; ++e)
+                Cs[(wm * TM * MF + i * MF + MM::row(lg, e)) * LDC + cl] = from_f32<bf16>(acc[i][j][e] + bj);
+    }
+    __syncthreads();
+    constexpr int OVR = BN / VEC;
+    static_assert(NTH % OVR == 0, "each thread keeps one column range");
+    const int cv = t % OVR, col = n0 + cv * VEC;
+    if (col >= g.Nn) return;
+    const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
+    const int RQ = g.R * g.Q;
+    for (int m = t / OVR; m < RQ; m += NTH / OVR) {
+        const int rr = fdiv(m, g.fQ);
+        const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
+        if (oh >= g.Hout || ow >= g.Wout) continue;
+        const int64_t pix = ((int64_t)n * g.Hout + oh) * g.Wout + ow;
+        const uint4 raw = *(const uint4*)(Cs + m * LDC + cv * VEC);
+        out.template put<bf16, ACT>(pix, col, raw, nv);
+    }
+}
+
+// Weights in B-fragment order for halo_rb_kernel.  Output 16-byte unit
+//   ((group * nsteps + st) * 4 + kk) * 64 + lane,  st = chunk * KH*KW + tap
+// holds, for row = 32*group + lane%32, the 8 consecutive k of channel chunk
+// chunk*64 + kk*16 + (lane/32)*8 at tap.  Forward rows are output channels:
+// w[row, tap, ch]; input-gradient rows are input channels: w[ch, tap, row].  Rows past
+// the matrix are zero.
+__global__ __launch_bounds__(256) void frag_weights(const bf16* __restrict__ w, uint4* __restrict__ dst, int Nn,
+                                                    int taps, int Cin, int nsteps, int groups, int fwd) {
+    const int64_t total = (int64_t)groups * nsteps * 4 * 64;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
+        const int l = (int)(u & 63);
+        const int64_t q = u >> 6;
+        const int kk = (int)(q & 3);
+        const int64_t q2 = q >> 2;
+        const int st = (int)(q2 % nsteps);
+        const int grp = (int)(q2 / nsteps);
+        const int row = grp * 32 + (l & 31);
+        const int chunk = st / taps, tap = st - chunk * taps;
+        const int ch0 = chunk * 64 + kk * 16 + (l >> 5) * 8;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (row < Nn) {
+            if (fwd) {
+                v = *(const uint4*)(w + ((int64_t)row * taps + tap) * Cin + ch0);
+            } else {
+                bf16 e[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) e[k] = w[((int64_t)(ch0 + k) * taps + tap) * Nn + row];
+                __builtin_memcpy(&v, e, 16);
+            }
+        }
+        dst[u] = v;
+    }
+}
+
+// ------------------------------------------------------------------ host side
+constexpr int kLdsMax = 160 * 1024;
+constexpr int kCUs = 256;
+
+struct HaloPlan {
+    int bm, bn, hb;
+    int R, Q;
+    int lds;  // dynamic LDS bytes per workgroup
+};
+
+int halo_groups(int R, int Q, int KH, int KW) { return ((R + KH - 1) * (Q + KW - 1) + 7) / 8; }
+
+// bf16 tiles keep only the halo in LDS (weights go to registers); fp32 tiles also hold a
+// two-slot weight ring.  The epilogue reuses the same bytes.
+int plan_lds(int bm, int bn, int hb, int gh, int esize) {
+    const int ring = hb * gh * 1024 + (esize == 2 ? 0 : 2 * bn * 128);
+    const int epi = bm * (bn + 16 / esize) * esize;
+    return ring > epi ? ring : epi;
+}
+
+struct Sides {
+    int Hout, Wout, Cin, Nn;
+};
+
+// Estimated time of a tile layout: rounds of workgroups times the slower of the bytes a
+// CU loads (16-byte loads of whole cache lines run at about 34-60 B/clk per CU) and its
+// MFMA work (about 3700 bf16 flop/clk per CU measured for 32x32x16 fed from LDS; 256
+// fp32 flop/clk peak).  A single halo buffer exposes the copy of every later chunk's
+// halo, half hidden when a second workgroup shares the CU.  Only the ranking matters.
+double plan_cost(int dt, const ConvDims& d, const Sides& sd, int bm, int bn, int hb, int R, int Q, int occ) {
+    const int64_t tiles = (int64_t)d.N * ceil_div(sd.Hout, R) * ceil_div(sd.Wout, Q) * ceil_div(sd.Nn, bn);
+    const double rounds = fmax(1.0, (double)tiles / ((double)kCUs * occ));
+    const int chunks = sd.Cin * (int)dtype_size(dt) / 128;
+    const double halo = halo_groups(R, Q, d.KH, d.KW) * 1024.0;
+    const double copy = chunks * (halo + (double)d.KH * d.KW * bn * 128) / 34.0;
+    const double mfma = 2.0 * bm * bn * d.KH * d.KW * sd.Cin / (dt == DT_BF16 ? 3700.0 : 256.0);
+    double clk = fmax(copy, mfma) + 0.05 * (copy + mfma);  // the smaller one still costs a little
+    if (hb == 1 && chunks > 1) clk += (chunks - 1) * halo / 34.0 * (occ == 1 ? 1.0 : 0.5);
+    if (occ == 1) clk *= 1.6;  // a lone workgroup per CU leaves every stall exposed (measured)
+    return rounds * occ * clk;
+}
+
+// Output tiles are R x Q rectangles: Q is the whole row or an even split of it, and the
+// R*Q pixels fill at least three quarters of the block's MFMA rows.  Block heights are
+// tried largest first (a taller block loads each weight fragment for more pixels): bf16
+// 256 or 128 rows for 128 output channels, 512, 256 or 128 rows for 64; fp32 256 or 224.
+// Within the first height that fits, the layout with the lowest estimated time wins.
+bool pick_halo(int dt, const ConvDims& d, const Sides& sd, HaloPlan* best) {
+    const int es = (int)dtype_size(dt);
+    if ((sd.Cin * es) % 128) return false;
+    const int chunks = sd.Cin * es / 128;
+    const int bn = sd.Nn <= 64 ? 64 : 128;
+    static const int bms_b128[] = {256, 128, 0}, bms_b64[] = {512, 256, 128, 0}, bms_f32[] = {256, 224, 0};
+    const int* bms = dt == DT_BF16 ? (bn == 128 ? bms_b128 : bms_b64) : bms_f32;
+    for (; *bms; ++bms) {
+        const int bm = *bms;
+        bool found = false;
+        double best_cost = 0.0;
+        for (int R = 1; R <= bm && R <= sd.Hout; ++R) {
+            int Q = bm / R;
+            if (Q > sd.Wout) Q = sd.Wout;
+            const int nseg = (int)ceil_div(sd.Wout, Q);
+            Q = (int)ceil_div(sd.Wout, nseg);
+            if (R * Q * 4 < bm * 3) continue;
+            const int gh = halo_groups(R, Q, d.KH, d.KW);
+            for (int hb = 1; hb <= (chunks > 1 ? 2 : 1); ++hb) {
+                const int lds = plan_lds(bm, bn, hb, gh, es);
+                if (lds > kLdsMax) continue;
+                const int occ = lds <= kLdsMax / 2 ? 2 : 1;
+                const double cost = plan_cost(dt, d, sd, bm, bn, hb, R, Q, occ);
+                if (!found || cost < best_cost) {
+                    *best = HaloPlan{bm, bn, hb, R, Q, lds};
+                    best_cost = cost;
+                    found = true;
+                }
+            }
+        }
+        if (found) return true;
+    }
+    return false;
+}
+
+HaloGeom make_geom(const ConvDims& d, const Sides& sd, const HaloPlan& p, int dt, bool fwd) {
+    HaloGeom g;
+    g.Hin = fwd ? d.H : d.OH;
+    g.Win = fwd ? d.W : d.OW;
+    g.Cin = sd.Cin;
+    g.KH = d.KH;
+    g.KW = d.KW;
+    g.Hout = sd.Hout;
+    g.Wout = sd.Wout;
+    g.Nn = sd.Nn;
+    g.R = p.R;
+    g.Q = p.Q;
+    g.HQ = p.Q + d.KW - 1;
+    g.HP = (p.R + d.KH - 1) * g.HQ;
+    g.GH = (g.HP + 7) / 8;
+    g.org_r = fwd ? -d.ph : d.ph - d.KH + 1;
+    g.org_c = fwd ? -d.pw : d.pw - d.KW + 1;
+    g.tiles_r = (int)ceil_div(sd.Hout, p.R);
+    g.tiles_c = (int)ceil_div(sd.Wout, p.Q);
+    g.nchunks = sd.Cin * (int)dtype_size(dt) / 128;
+    g.Kb = d.KH * d.KW * sd.Cin;
+    g.sign = fwd ? 1 : -1;
+    g.hb = p.hb;
+    g.img_stride = (int64_t)g.Hin * g.Win * g.Cin;
+    g.fQ = make_fastdiv(p.Q);
+    g.fHQ = make_fastdiv(g.HQ);
+    g.fTR = make_fastdiv(g.tiles_r);
+    g.fTC = make_fastdiv(g.tiles_c);
+    return g;
+}
+
+template <class K> hipError_t raise_lds(K kern, bool& raised) {
+    if (raised) return hipSuccess;  // the dynamic LDS limit is raised once per instantiation
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    if (e == hipSuccess) raised = true;
+    return e;
+}
+
+template <int MF, int BM, int BN, int WM, int WN, int ACT, class Out>
+hipError_t launch_f32(const float* A, const HaloGeom& g, const float* B, const Out& out, int images, int lds,
+                      hipStream_t s) {
+    auto kern = halo_kernel<float, MF, BM, BN, WM, WN, ACT, Out>;
+    static bool raised = false;
+    const hipError_t e = raise_lds(kern, raised);
+    if (e != hipSuccess) return e;
+    const int tiles_n = (int)ceil_div(g.Nn, BN);
+    const int64_t grid = (int64_t)images * g.tiles_r * g.tiles_c * tiles_n;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreadsH), lds, s, A, g, B, out, tiles_n);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int ACT, class Out>
+hipError_t launch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, const Out& out, int images, int lds,
+                       hipStream_t s) {
+    auto kern = halo_rb_kernel<BM, BN, WM, WN, ACT, Out>;
+    static bool raised = false;
+    const hipError_t e = raise_lds(kern, raised);
+    if (e != hipSuccess) return e;
+    const int tiles_n = (int)ceil_div(g.Nn, BN);
+    const int64_t grid = (int64_t)images * g.tiles_r * g.tiles_c * tiles_n;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreadsH), lds, s, A, g, Bf, out, tiles_n);
+    return hipGetLastError();
+}
+
+template <int ACT, class Out>
+hipError_t dispatch_f32(const float* A, const HaloGeom& g, const float* B, const Out& out, const HaloPlan& p,
+                        int images, hipStream_t s) {
+#define CONVMI_HP(BM_, BN_)                                                                                 \
+    if (p.bm == BM_ && p.bn == BN_) return launch_f32<16, BM_, BN_, 2, 2, ACT, Out>(A, g, B, out, images, p.lds, s);
+    CONVMI_HP(224, 128) CONVMI_HP(224, 64) CONVMI_HP(256, 128) CONVMI_HP(256, 64)
+#undef CONVMI_HP
+    return hipErrorInvalidValue;
+}
+
+// bf16 wave layouts: 128 output channels as 2 x 64 (TN = 2 fragments per wave, waves 2 x 2);
+// 64 output channels as 1 x 64 (waves 4 x 1).
+template <int ACT, class Out>
+hipError_t dispatch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, const Out& out, const HaloPlan& p,
+                         int images, hipStream_t s) {
+#define CONVMI_RB(BM_, BN_, WM_, WN_)                                                                       \
+    if (p.bm == BM_ && p.bn == BN_) return launch_bf16<BM_, BN_, WM_, WN_, ACT, Out>(A, g, Bf, out, images, p.lds, s);
+    CONVMI_RB(256, 128, 2, 2) CONVMI_RB(128, 128, 2, 2)
+    CONVMI_RB(512, 64, 4, 1) CONVMI_RB(256, 64, 4, 1) CONVMI_RB(128, 64, 4, 1)
+#undef CONVMI_RB
+    return hipErrorInvalidValue;
+}
+
+Sides fwd_sides(const ConvDims& d) { return Sides{d.OH, d.OW, d.IC, d.OC}; }
+Sides dx_sides(const ConvDims& d) { return Sides{d.H, d.W, d.OC, d.IC}; }
+
+// Fragment-ordered weights: 32-row groups covering every column tile, KH*KW*Cin k each.
+size_t frag_bytes(const ConvDims& d, const Sides& sd, const HaloPlan& p) {
+    const int64_t groups = ceil_div(sd.Nn, p.bn) * (p.bn / 32);
+    return align_up((size_t)groups * 32 * d.KH * d.KW * sd.Cin * 2, 256);
+}
+
+hipError_t launch_frag_weights(const bf16* w, uint4* dst, const ConvDims& d, const Sides& sd, const HaloPlan& p,
+                               bool fwd, hipStream_t s) {
+    const int taps = d.KH * d.KW;
+    const int nsteps = (sd.Cin / 64) * taps;
+    const int groups = (int)(ceil_div(sd.Nn, p.bn) * (p.bn / 32));
+    const int64_t units = (int64_t)groups * nsteps * 256;
+    const int grid = (int)(ceil_div(units, 256) < 2048 ? ceil_div(units, 256) : 2048);
+    frag_weights<<<grid, 256, 0, s>>>(w, dst, sd.Nn, taps, sd.Cin, nsteps, groups, fwd ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool halo_fwd_supported(int dt, const ConvDims& d) {
+    HaloPlan p;
+    return d.sh == 1 && d.sw == 1 && pick_halo(dt, d, fwd_sides(d), &p);
+}
+
+bool halo_dx_supported(int dt, const ConvDims& d) {
+    HaloPlan p;
+    return d.sh == 1 && d.sw == 1 && pick_halo(dt, d, dx_sides(d), &p);
+}
+
+size_t halo_fwd_ws_bytes(int dt, const ConvDims& d) {
+    HaloPlan p;
+    if (dt != DT_BF16 || !halo_fwd_supported(dt, d) || !pick_halo(dt, d, fwd_sides(d), &p)) return 0;
+    return frag_bytes(d, fwd_sides(d), p);
+}
+
+size_t halo_dx_ws_bytes(int dt, const ConvDims& d) {
+    HaloPlan p;
+    if (dt != DT_BF16 || !halo_dx_supported(dt, d) || !pick_halo(dt, d, dx_sides(d), &p)) return 0;
+    return frag_bytes(d, dx_sides(d), p);
+}
+
+hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
+                           const ConvDims& d, int act, void* ws, hipStream_t s) {
+    const Sides sd = fwd_sides(d);
+    HaloPlan p;
+    if (d.sh != 1 || d.sw != 1 || !pick_halo(dt, d, sd, &p)) return hipErrorInvalidValue;
+    const HaloGeom g = make_geom(d, sd, p, dt, true);
+    const HFwdOut o{z, y, bias, d.OC};
+    if (dt == DT_BF16) {
+        const hipError_t e = launch_frag_weights((const bf16*)w, (uint4*)ws, d, sd, p, true, s);
+        if (e != hipSuccess) return e;
+        CONVMI_ACT_SWITCH(act, A_, return (dispatch_bf16<A_, HFwdOut>((const bf16*)x, g, (const uint4*)ws, o, p,
+                                                                      d.N, s)));
+    } else {
+        CONVMI_ACT_SWITCH(act, A_, return (dispatch_f32<A_, HFwdOut>((const float*)x, g, (const float*)w, o, p,
+                                                                     d.N, s)));
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_halo_dx(int dt, const void* dz, const void* w, void* dx, const ConvDims& d, void* ws,
+                          hipStream_t s) {
+    const Sides sd = dx_sides(d);
+    HaloPlan p;
+    if (d.sh != 1 || d.sw != 1 || !pick_halo(dt, d, sd, &p)) return hipErrorInvalidValue;
+    const HaloGeom g = make_geom(d, sd, p, dt, false);
+    const HDxOut o{dx, d.IC};
+    if (dt == DT_BF16) {
+        const hipError_t e = launch_frag_weights((const bf16*)w, (uint4*)ws, d, sd, p, false, s);
+        if (e != hipSuccess) return e;
+        return dispatch_bf16<ACT_IDENTITY, HDxOut>((const bf16*)dz, g, (const uint4*)ws, o, p, d.N, s);
+    }
+    return dispatch_f32<ACT_IDENTITY, HDxOut>((const float*)dz, g, (const float*)w, o, p, d.N, s);
+}
+
+}  // namespace convmi

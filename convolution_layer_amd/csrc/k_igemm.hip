@@ -591,15 +591,17 @@ bool igemm_dx_supported(int dt, const ConvDims& d) {
     return pick_bk(dt, d.OC, dx_kws(d)) != 0;
 }
 
-size_t igemm_fwd_ws_bytes(int, const ConvDims&) { return 0; }
+size_t igemm_fwd_ws_bytes(int dt, const ConvDims& d) { return halo_fwd_ws_bytes(dt, d); }
 
 size_t igemm_dx_ws_bytes(int dt, const ConvDims& d) {
     const size_t n = (size_t)d.sh * d.sw * d.IC * dx_khs(d) * dx_kws(d) * d.OC;
-    return align_up(n * dtype_size(dt), 256);
+    const size_t bt = align_up(n * dtype_size(dt), 256), frag = halo_dx_ws_bytes(dt, d);
+    return bt > frag ? bt : frag;
 }
 
 hipError_t launch_igemm_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
-                            const ConvDims& d, int act, void*, hipStream_t s) {
+                            const ConvDims& d, int act, void* ws, hipStream_t s) {
+    if (halo_fwd_supported(dt, d)) return launch_halo_fwd(dt, x, w, bias, z, y, d, act, ws, s);
     GatherGeom g;
     g.Hin = d.H; g.Win = d.W; g.Cin = d.IC; g.KWk = d.KW;
     g.R1 = d.OH; g.R2 = d.OW; g.rs1 = d.sh; g.ro1 = -d.ph; g.rs2 = d.sw; g.ro2 = -d.pw;
@@ -621,6 +623,8 @@ hipError_t launch_igemm_fwd(int dt, const void* x, const void* w, const float* b
 
 hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, const ConvDims& d, void* ws,
                            hipStream_t s) {
+    // bf16 stride-1: the tile-reuse kernel reads the weights in its own fragment order
+    if (dt == DT_BF16 && halo_dx_supported(dt, d)) return launch_halo_dx(dt, dz, w, dx, d, ws, s);
     const int KHs = dx_khs(d), KWs = dx_kws(d);
     const int Ncol = d.sh * d.sw * d.IC, Kb = KHs * KWs * d.OC;
     // rearranged weights into the workspace
@@ -634,6 +638,7 @@ hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, cons
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (halo_dx_supported(dt, d)) return launch_halo_dx(dt, dz, ws, dx, d, nullptr, s);
     // rows: phase blocks (qh, qw) that touch the image
     const int qh0 = d.ph / d.sh, qh1 = (d.H - 1 + d.ph) / d.sh;
     const int qw0 = d.pw / d.sw, qw1 = (d.W - 1 + d.pw) / d.sw;

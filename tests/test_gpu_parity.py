@@ -47,6 +47,17 @@ MEDIUM = [
     ((2, 11, 11, 16, 16, 3, 3, 2, 2, 1, 1), WL.BF16, WL.ACT_SIGMOID),
     ((3, 12, 10, 32, 96, 5, 5, 1, 1, 2, 2), WL.F32, WL.ACT_TANH),
     ((2, 30, 30, 64, 32, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+    # stride-1 shapes for the input-tile-reuse kernels: rows split into segments,
+    # KH != KW, asymmetric padding, ragged output channels (vector and scalar stores),
+    # one and two halo buffers
+    ((2, 21, 300, 64, 72, 3, 5, 1, 1, 0, 2), WL.BF16, WL.ACT_RELU),
+    ((2, 19, 250, 36, 64, 5, 3, 1, 1, 2, 0), WL.BF16, WL.ACT_SIGMOID),
+    ((2, 16, 40, 32, 30, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_TANH),
+    ((2, 18, 33, 20, 64, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_IDENTITY),
+    ((3, 12, 12, 64, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH),
+    # two-row images: the halo only fits LDS once, so later chunks reload it in place
+    ((2, 2, 256, 128, 64, 7, 7, 1, 1, 3, 3), WL.BF16, WL.ACT_RELU),
+    ((2, 2, 256, 64, 128, 7, 7, 1, 1, 3, 3), WL.BF16, WL.ACT_IDENTITY),
 ]
 
 
