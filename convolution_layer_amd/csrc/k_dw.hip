@@ -19,6 +19,8 @@
 // existing gradient when accumulating).  No atomics: results are bitwise reproducible.
 // The bias gradient comes from the same dz loads: workgroups of the first k tile keep
 // per-channel sums of their dz block and write them beside the partial tile.
+#include <type_traits>
+
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
@@ -26,6 +28,7 @@ namespace convmi {
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NT = 256;
@@ -288,7 +291,7 @@ __device__ __forceinline__ int dswz(int row) { return (row & 3) << 1; }
 typedef short dw_short4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) dw_short4* dw_lds4_t;
 
-template <typename T, int BM, int BN, int WM, int WN>
+template <typename T, int BM, int BN, int WM, int WN, int MF>
 __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const T* __restrict__ dz, DwGeom g,
                                                  FastDiv fOW, FastDiv fOH, FastDiv fIC, FastDiv fKW,
                                                  float* __restrict__ part, float* __restrict__ part_db,
@@ -304,8 +307,11 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
     static_assert((IA + IB) % 4 == 0, "copies split evenly over the four waves");
     constexpr int IPW = (IA + IB) / 4;
     constexpr int STAGE = BK * (RA + RB);
-    constexpr int TM = BM / (WM * 16), TN = BN / (WN * 16);
-    static_assert(TM * WM * 16 == BM && TN * WN * 16 == BN, "tile shape");
+    constexpr int TM = BM / (WM * MF), TN = BN / (WN * MF);
+    static_assert(TM * WM * MF == BM && TN * WN * MF == BN, "tile shape");
+    static_assert(MF == 16 || (MF == 32 && sizeof(T) == 2), "32x32 fragments are bf16 only");
+    using Acc = typename std::conditional<MF == 32, floatx16, floatx4>::type;
+    constexpr int NE = MF == 32 ? 16 : 4;
     __shared__ __align__(1024) unsigned char smem[2 * STAGE];
 
     const int t = threadIdx.x, lane = t & 63;
@@ -382,11 +388,13 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
 
     const int wm = wid / WN, wn = wid % WN;
     const int lr = lane & 15, lg = lane >> 4;
-    floatx4 acc[TM][TN];
+    Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < NE; ++e) acc[i][j][e] = 0.0f;
 
     // operand vector of 16 consecutive-in-position bytes for column c (tile-local) at
     // positions kb.. of a tile with row bytes R
@@ -416,9 +424,45 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
             return make_uint4(r[0], r[1], r[2], r[3]);
         }
     };
+    // 32x32x16 operand: lane l holds column c + l%32 at positions kb + 8*(l/32) .. +7.  In
+    // each 16-lane group the transposing read gives lane i the column (group's first) + i,
+    // so lane i addresses position kb + 4*half + i/4, columns 4*(i%4) .. +3 of the group.
+    auto frag32 = [&](const unsigned char* base, int R, int kk, int c) -> uint4 {
+        const int l16 = lane & 15, hi = (lane >> 4) & 1, kb = kk + 8 * (lane >> 5);
+        uint4 v;
+        dw_short4 h[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int row = kb + 4 * half + (l16 >> 2);
+            const int cb = 2 * (c + 16 * hi + 4 * (l16 & 3));
+            const int off = row * R + ((((cb >> 4) ^ dswz(row)) << 4) | (cb & 15));
+            h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(base + off));
+        }
+        v.x = __builtin_bit_cast(uint2, h[0]).x; v.y = __builtin_bit_cast(uint2, h[0]).y;
+        v.z = __builtin_bit_cast(uint2, h[1]).x; v.w = __builtin_bit_cast(uint2, h[1]).y;
+        return v;
+    };
     auto compute = [&](int st) {
         const unsigned char* As = smem + (st & 1) * STAGE;
         const unsigned char* Bs = As + BK * RA;
+        if constexpr (MF == 32) {
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 16) {
+                uint4 af[TM], bfr[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) af[i] = frag32(As, RA, kk, wm * TM * 32 + i * 32);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) bfr[j] = frag32(Bs, RB, kk, wn * TN * 32 + j * 32);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                                            __builtin_bit_cast(bf16x8, bfr[j]),
+                                                                            acc[i][j], 0, 0, 0);
+            }
+            return;
+        }
         constexpr int KM = MM::KM;
 #pragma unroll
         for (int kk = 0; kk < BK; kk += KM) {
@@ -432,7 +476,9 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) MM::run(acc[i][j], af[i], bfr[j]);
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (MF == 16) MM::run(acc[i][j], af[i], bfr[j]);
+                }
         }
     };
 
@@ -458,15 +504,18 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
         compute(k);
     }
 
+    // accumulator element e of a lane: row (oc) 4*(lane/16) + e (16x16) or
+    // 8*(e/4) + 4*(lane/32) + e%4 (32x32), column lane % MF
     float* dst = part + (int64_t)slab * g.OC * g.Kdim;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int oc = oc0 + wm * TM * 16 + i * 16 + lg * 4 + e;
-                const int k = k0 + wn * TN * 16 + j * 16 + lr;
+            for (int e = 0; e < NE; ++e) {
+                const int row = MF == 32 ? 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) : lg * 4 + e;
+                const int oc = oc0 + wm * TM * MF + i * MF + row;
+                const int k = k0 + wn * TN * MF + j * MF + lane % MF;
                 if (oc < g.OC && k < g.Kdim) dst[(int64_t)oc * g.Kdim + k] = acc[i][j][e];
             }
     if (do_db) {  // uniform per workgroup
@@ -483,39 +532,359 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
     }
 }
 
+// ------------------------------------------------------------------ stride-1 bf16 kernel
+// For stride 1 the KW taps of one kernel row read the same input row shifted by one
+// position each.  A workgroup owns a whole kernel row kh: 128 output channels x (KW taps
+// x 128 input channels).  It streams stages of RS output-row segments of SEG positions:
+// the dz rows (positions x 128 oc) and, once, the input rows they touch (SEG + KW - 1
+// positions x 128 ic); tap kw reads the input tile at a row offset of kw.  That loads
+// about a third of the bytes per FLOP of the per-tap gather above.  Operands are read
+// with transposing LDS reads into 32x32x16 MFMA fragments (lane l: column l%32,
+// positions 8*(l/32) .. +7 of the k-step).  One workgroup per CU (the stage ring is
+// ~115 KB), so each wave may hold 2*KW accumulator fragments per operand row pair.
+struct Dw3Geom {
+    int N, H, W, IC, OC, KH, KW, OH, OW, ph, pw;
+    int SEG, RS, nseg;  // stage: RS segments of SEG positions of output rows
+    int SPp;            // positions per stage, padded to a multiple of 16
+    int XW, XR;         // input positions per segment (SEG + KW - 1), input rows per stage
+    int G;              // segments in all (N*OH*nseg)
+    int nst;            // stages in all (ceil(G / RS))
+    int spb;            // stages per slab
+    int S, tiles, ict, oct;
+    int Kdim;           // KH*KW*IC
+    FastDiv fnseg, fOH;
+};
+
+// 16-byte chunk swizzle of a 256-byte LDS row: 4 consecutive rows read at the same
+// 32-byte column piece by one transposing read land in 4 different quarters of the banks.
+__device__ __forceinline__ int sw3(int row) { return (row & 3) << 2; }
+
+template <int KW_>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void dw3_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ dz, Dw3Geom g, float* __restrict__ part,
+    float* __restrict__ part_db, int want_db) {
+    constexpr int TM = 2, TN = 2 * KW_;  // wave tile 64 oc x KW*64 columns (waves 2 x 2)
+    extern __shared__ __align__(1024) unsigned char smem[];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int stage_bytes = (g.SPp + g.XR) * 256;
+    const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+    // (slab, tile); the tiles of one slab share its dz rows and stay on one XCD
+    const int lin = xcd_tile(blockIdx.x, gridDim.x);
+    const int slab = lin / g.tiles, tile = lin - slab * g.tiles;
+    const int oct_i = tile % g.oct, r1 = tile / g.oct;
+    const int ict_i = r1 % g.ict, kh = r1 / g.ict;
+    const int oc0 = oct_i * 128, ic0 = ict_i * 128;
+    const int s_begin = slab * g.spb;
+    const int s_end = min(g.nst, s_begin + g.spb);
+    const int KT = s_end - s_begin;
+    // every kernel row's workgroup sums every KH-th dz row of a stage for the bias gradient
+    const bool do_db = want_db && ict_i == 0;
+
+    // Copy instructions of a stage: NA for dz (4 rows of 256 bytes each), then NB for the
+    // input rows; this wave issues instructions wid, wid + 4, ...  Lane l copies 16-byte
+    // chunk l%16 of row 4j + l/16; the swizzle of that row depends on l/16 only.
+    const int NA = g.SPp / 4, NB = g.XR / 4;
+    const int rsub = lane >> 4;
+    const int choff = ((lane & 15) ^ sw3(rsub)) * 16;  // source byte offset of the chunk
+    const int nmine = (NA + NB - wid + 3) / 4;          // instructions of this wave per stage
+    // Segment data of the stage being copied: uniform per workgroup.
+    struct Segs {
+        const char* dzb[2];  // first dz pixel of segment r (+ oc0), bytes
+        const char* xb[2];   // input row of segment r at iw = 0 (+ ic0), bytes; null if outside
+        int len[2];          // valid positions of segment r (0 if none)
+        int w0[2];
+        uint32_t slot;
+    };
+    auto segs_of = [&](int st) {
+        Segs sg;
+        const int sidx = s_begin + st;
+        sg.slot = smem_base + (uint32_t)((st & 1) * stage_bytes);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int gr = sidx * g.RS + r;
+            sg.len[r] = 0;
+            sg.w0[r] = 0;
+            sg.dzb[r] = (const char*)dz;
+            sg.xb[r] = nullptr;
+            if (r < g.RS && gr < g.G) {
+                const int f = fdiv(gr, g.fnseg);
+                const int sgi = gr - f * g.nseg;
+                const int n = fdiv(f, g.fOH), oh = f - n * g.OH;
+                sg.w0[r] = sgi * g.SEG;
+                sg.len[r] = min(g.SEG, g.OW - sg.w0[r]);
+                sg.dzb[r] = (const char*)(dz + ((int64_t)f * g.OW + sg.w0[r]) * g.OC + oc0);
+                const int ih = oh + kh - g.ph;
+                if ((unsigned)ih < (unsigned)g.H)
+                    sg.xb[r] = (const char*)(x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0);
+            }
+        }
+        return sg;
+    };
+    // issue this wave's copy instructions i0 .. i1-1 of a stage
+    auto issue = [&](const Segs& sg, int i0, int i1) {
+        for (int i = i0; i < i1; ++i) {
+            const int j = wid + 4 * i;
+            const void* src = &kZero16;
+            uint32_t dst;
+            if (j < NA) {
+                const int p = 4 * j + rsub;
+                const bool r = p >= g.SEG;
+                const int q = r ? p - g.SEG : p;
+                if (q < (r ? sg.len[1] : sg.len[0]))
+                    src = (r ? sg.dzb[1] : sg.dzb[0]) + q * (g.OC * 2) + choff;
+                dst = sg.slot + j * 1024;
+            } else {
+                const int jb = j - NA;
+                const int xr = 4 * jb + rsub;
+                const bool r = xr >= g.XW;
+                const int qq = r ? xr - g.XW : xr;
+                const char* xb = r ? sg.xb[1] : sg.xb[0];
+                const int iw = (r ? sg.w0[1] : sg.w0[0]) + qq - g.pw;
+                if (xb != nullptr && qq < g.XW && (r ? sg.len[1] : sg.len[0]) > 0 && (unsigned)iw < (unsigned)g.W)
+                    src = xb + iw * (g.IC * 2) + choff;
+                dst = sg.slot + g.SPp * 256 + jb * 1024;
+            }
+            dma16(src, __builtin_amdgcn_readfirstlane(dst));
+        }
+    };
+
+    const int wm = wid >> 1, wn = wid & 1;
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // Transposing fragment read: lane l gets column c + l%32 at positions
+    // kk + 8*(l/32) .. +7; in each 16-lane group lane i addresses position +i/4 of a
+    // half and the 8-byte piece 4*(i%4) of the group's 16 columns.  Input rows of tap kw
+    // sit kw rows further, and the second segment of a stage starts XW - SEG rows later.
+    // k-steps start at multiples of 16, so the swizzle of a lane's row does not depend on
+    // the k-step: every offset is kk*256 plus a per-lane constant (two constants for the
+    // input rows, with and without the second segment's shift).
+    const int l16 = lane & 15, hi = (lane >> 4) & 1, kb8 = 8 * (lane >> 5);
+    auto lds_off = [&](int row, int c) {
+        const int cb = 2 * (c + 16 * hi + 4 * (l16 & 3));
+        return row * 256 + ((((cb >> 4) ^ sw3(row)) << 4) | (cb & 15));
+    };
+    int a_off[TM][2], b_off[TN][2][2];
+    int prow[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        prow[half] = kb8 + 4 * half + (l16 >> 2);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a_off[i][half] = lds_off(prow[half], wm * 64 + i * 32);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = wn * KW_ * 64 + j * 32;  // tap col/128, input channel col%128
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh)
+                b_off[j][half][sh] = lds_off(prow[half] + (col >> 7) + sh * (g.XW - g.SEG), col & 127);
+        }
+    }
+    auto read_frags = [&](const unsigned char* As, const unsigned char* Xs, int kk, uint4 (&af)[TM],
+                          uint4 (&bf)[TN]) {
+        dw_short4 h[2];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(As + kk * 256 + a_off[i][half]));
+            af[i] = make_uint4(__builtin_bit_cast(uint2, h[0]).x, __builtin_bit_cast(uint2, h[0]).y,
+                               __builtin_bit_cast(uint2, h[1]).x, __builtin_bit_cast(uint2, h[1]).y);
+        }
+        bool second[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) second[half] = kk + prow[half] >= g.SEG;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int off = second[half] ? b_off[j][half][1] : b_off[j][half][0];
+                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Xs + kk * 256 + off));
+            }
+            bf[j] = make_uint4(__builtin_bit_cast(uint2, h[0]).x, __builtin_bit_cast(uint2, h[0]).y,
+                               __builtin_bit_cast(uint2, h[1]).x, __builtin_bit_cast(uint2, h[1]).y);
+        }
+    };
+    auto mfmas = [&](const uint4 (&af)[TM], const uint4 (&bf)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                                    __builtin_bit_cast(bf16x8, bf[j]), acc[i][j],
+                                                                    0, 0, 0);
+    };
+
+    // Column sums of dz for the bias gradient: thread t owns chunk t%16 (8 channels) of
+    // rows kh + KH*(t/16), kh + KH*(t/16 + 16), ...
+    float dbs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dbs[j] = 0.0f;
+    auto db_sum = [&](const unsigned char* As) {
+        for (int row = kh + g.KH * (t >> 4); row < g.SPp; row += 16 * g.KH) {
+            const uint4 v = *(const uint4*)(As + row * 256 + (((t & 15) ^ sw3(row)) << 4));
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                dbs[2 * d] += __uint_as_float(u[d] << 16);
+                dbs[2 * d + 1] += __uint_as_float(u[d] & 0xffff0000u);
+            }
+        }
+    };
+
+    // Stage k: the copies of stage k + 1 go out in slices over the first k-steps of stage
+    // k, between MFMA groups, so their address arithmetic overlaps the MFMAs; the reads
+    // of k-step kk + 1 are issued before the MFMAs of kk.
+    const int nk = g.SPp / 16;
+    const int spread = nk > 2 ? 2 : 1;  // k-steps that carry copies: early, to leave time for them to land
+    if (KT > 0) issue(segs_of(0), 0, nmine);
+    for (int k = 0; k < KT; ++k) {
+        wait_dma(0);
+        __syncthreads();
+        const bool next = k + 1 < KT;
+        const Segs sg = segs_of(next ? k + 1 : k);
+        const unsigned char* As = smem + (k & 1) * stage_bytes;
+        const unsigned char* Xs = As + g.SPp * 256;
+        if (do_db) db_sum(As);
+        uint4 a0[TM], b0[TN], a1[TM], b1[TN];
+        read_frags(As, Xs, 0, a0, b0);
+        int kk = 0;
+        for (; kk + 1 < nk; kk += 2) {
+            read_frags(As, Xs, (kk + 1) * 16, a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (next && kk < spread) issue(sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+            if (kk + 2 < nk) read_frags(As, Xs, (kk + 2) * 16, a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (next && kk + 1 < spread) issue(sg, (kk + 1) * nmine / spread, (kk + 2) * nmine / spread);
+        }
+        if (kk < nk) {
+            mfmas(a0, b0);
+            if (next && kk < spread) issue(sg, kk * nmine / spread, nmine);
+        }
+    }
+
+    // partial tile: row (oc) 8*(e/4) + 4*(lane/32) + e%4 of fragment i, column lane%32
+    float* dst = part + (int64_t)slab * g.OC * g.Kdim;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = wn * KW_ * 64 + j * 32;
+            const int k = (kh * g.KW + (col >> 7)) * g.IC + ic0 + (col & 127) + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int oc = oc0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                dst[(int64_t)oc * g.Kdim + k] = acc[i][j][e];
+            }
+        }
+    if (do_db) {  // uniform per workgroup
+        __syncthreads();
+        float* red = (float*)smem;  // [16][128]; the ring is no longer needed
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[(t >> 4) * 128 + (t & 15) * 8 + j] = dbs[j];
+        __syncthreads();
+        if (t < 128) {
+            float s_ = 0.0f;
+            for (int q = 0; q < 16; ++q) s_ += red[q * 128 + t];
+            part_db[((int64_t)slab * g.KH + kh) * g.OC + oc0 + t] = s_;
+        }
+    }
+}
+
 // dw = (accumulate ? dw : 0) + sum over slabs; four slab groups (s = q mod 4) per output
 // vector are summed in slab order and then merged in group order: fixed order, so
-// bitwise reproducible.  Block 0 also finishes db.  count is a multiple of 4.
+// bitwise reproducible.  Loads go out eight at a time before their in-order adds, so a
+// thread keeps eight loads in flight.  Blocks past the dw blocks finish db the same way
+// (64 channels each).  count is a multiple of 4.
+template <int U>
+__device__ __forceinline__ float4 sum_strided(const float4* __restrict__ p, int64_t stride4, int first, int S) {
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = first;
+    for (; s + 4 * (U - 1) < S; s += 4 * U) {
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = p[(int64_t)(s + 4 * u) * stride4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            r.x += v[u].x; r.y += v[u].y; r.z += v[u].z; r.w += v[u].w;
+        }
+    }
+    for (; s < S; s += 4) {
+        const float4 v = p[(int64_t)s * stride4];
+        r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+    }
+    return r;
+}
+
 __global__ __launch_bounds__(NT) void dw_reduce4(const float* __restrict__ part, const float* __restrict__ part_db,
                                                  float* __restrict__ dw, float* __restrict__ db, int64_t count,
-                                                 int OC, int S, int accumulate) {
+                                                 int OC, int S, int Sdb, int accumulate) {
     __shared__ float4 red[4][64];
     const int q = threadIdx.x >> 6, o = threadIdx.x & 63;
-    const int64_t i4 = (int64_t)blockIdx.x * 64 + o, n4 = count >> 2;
+    const int64_t n4 = count >> 2;
+    const int nb_dw = (int)((n4 + 63) / 64);
+    if ((int)blockIdx.x < nb_dw) {
+        const int64_t i4 = (int64_t)blockIdx.x * 64 + o;
+        float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i4 < n4) r = sum_strided<8>((const float4*)part + i4, n4, q, S);
+        red[q][o] = r;
+        __syncthreads();
+        if (q == 0 && i4 < n4) {
+            float4 a = red[0][o];
+#pragma unroll
+            for (int k = 1; k < 4; ++k) { a.x += red[k][o].x; a.y += red[k][o].y; a.z += red[k][o].z; a.w += red[k][o].w; }
+            if (accumulate) {
+                const float4 d = ((const float4*)dw)[i4];
+                a.x += d.x; a.y += d.y; a.z += d.z; a.w += d.w;
+            }
+            ((float4*)dw)[i4] = a;
+        }
+        return;
+    }
+    // bias: block nb_dw + b sums channels 64b .. 64b+63 (as 16 float4 of 4 channels)
+    if (db == nullptr) return;
+    const int c4 = ((int)blockIdx.x - nb_dw) * 16 + (o & 15), sub = o >> 4;
+    const int oc4 = OC >> 2;
+    // 16 thread groups (q, sub) split the slabs: group g = 4q + sub takes s = g mod 16
     float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i4 < n4)
-        for (int s = q; s < S; s += 4) {
-            const float4 v = ((const float4*)(part + (int64_t)s * count))[i4];
+    const int grp = q * 4 + sub;
+    if (c4 < oc4)
+        for (int s = grp; s < Sdb; s += 16) {
+            const float4 v = ((const float4*)part_db)[(int64_t)s * oc4 + c4];
             r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
         }
-    red[q][o] = r;
+    __shared__ float4 rdb[16][16];
+    rdb[grp][o & 15] = r;
     __syncthreads();
-    if (q == 0 && i4 < n4) {
-        float4 a = red[0][o];
+    if (threadIdx.x < 16 && c4 - (o & 15) + (int)threadIdx.x < oc4) {
+        const int cc = ((int)blockIdx.x - nb_dw) * 16 + (int)threadIdx.x;
+        float4 a = rdb[0][threadIdx.x];
+        for (int k = 1; k < 16; ++k) {
+            a.x += rdb[k][threadIdx.x].x; a.y += rdb[k][threadIdx.x].y;
+            a.z += rdb[k][threadIdx.x].z; a.w += rdb[k][threadIdx.x].w;
+        }
+        // db is only 4-byte aligned: scalar accesses
+        float* o4 = db + 4 * cc;
+        const float v4[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-        for (int k = 1; k < 4; ++k) { a.x += red[k][o].x; a.y += red[k][o].y; a.z += red[k][o].z; a.w += red[k][o].w; }
-        if (accumulate) {
-            const float4 d = ((const float4*)dw)[i4];
-            a.x += d.x; a.y += d.y; a.z += d.z; a.w += d.w;
-        }
-        ((float4*)dw)[i4] = a;
+        for (int k = 0; k < 4; ++k) o4[k] = accumulate ? o4[k] + v4[k] : v4[k];
     }
-    if (db && blockIdx.x == 0)
-        for (int c = threadIdx.x; c < OC; c += NT) {
-            float v = 0.0f;
-            for (int k = 0; k < S; ++k) v += part_db[(int64_t)k * OC + c];
-            db[c] = accumulate ? db[c] + v : v;
-        }
+}
+
+// grid of the reduction: dw blocks, then one block per 64 bias channels
+unsigned reduce_grid(int64_t count, int OC, bool with_db) {
+    const int64_t nb_dw = ceil_div(count / 4, 64);
+    return (unsigned)(nb_dw + (with_db ? ceil_div(OC, 64) : 0));
 }
 
 struct Plan {
@@ -544,13 +913,15 @@ Plan plan(int dt, const ConvDims& d) {
     return p;
 }
 
+// bf16 uses 32x32x16 MFMA fragments (waves 2 x 2), fp32 16x16x4.
 template <typename T, int BM, int BN>
 hipError_t launch_dw2(const T* x, const T* dz, const DwGeom& g, const ConvDims& d, const Plan& p, float* part,
                       float* part_db, int want_db, hipStream_t s) {
-    constexpr int WN = (BM == 128 || BN == 64) ? 2 : 4;
+    constexpr int MF = sizeof(T) == 2 ? 32 : 16;
+    constexpr int WN = MF == 32 ? 2 : ((BM == 128 || BN == 64) ? 2 : 4);
     constexpr int WM = 4 / WN;
     dim3 grid(p.tiles_m * p.tiles_n * p.S);
-    dw2_kernel<T, BM, BN, WM, WN><<<grid, NT, 0, s>>>(x, dz, g, make_fastdiv(d.OW), make_fastdiv(d.OH),
+    dw2_kernel<T, BM, BN, WM, WN, MF><<<grid, NT, 0, s>>>(x, dz, g, make_fastdiv(d.OW), make_fastdiv(d.OH),
                                                       make_fastdiv(d.IC), make_fastdiv(d.KW), part, part_db,
                                                       want_db);
     return hipGetLastError();
@@ -566,6 +937,65 @@ hipError_t launch_cfg(const T* x, const T* dz, const DwGeom& g, const Plan& p, f
     return hipGetLastError();
 }
 
+// Stride-1 bf16 layers with 128-channel multiples and kernels at most 3 wide.
+bool dw3_ok(int dt, const ConvDims& d) {
+    return dt == DT_BF16 && d.sh == 1 && d.sw == 1 && d.OC % 128 == 0 && d.IC % 128 == 0 && d.KW >= 1 &&
+           d.KW <= 3;
+}
+
+// Stage geometry: two whole output rows when they fit in 128 positions, else one row
+// split into equal segments of at most 128.  About one workgroup per CU.
+Dw3Geom plan3(const ConvDims& d) {
+    Dw3Geom g;
+    g.N = d.N; g.H = d.H; g.W = d.W; g.IC = d.IC; g.OC = d.OC; g.KH = d.KH; g.KW = d.KW;
+    g.OH = d.OH; g.OW = d.OW; g.ph = d.ph; g.pw = d.pw;
+    if (2 * d.OW <= 128) {
+        g.RS = 2;
+        g.nseg = 1;
+        g.SEG = d.OW;
+    } else {
+        g.RS = 1;
+        g.nseg = (int)ceil_div(d.OW, 128);
+        g.SEG = (int)ceil_div(d.OW, g.nseg);
+    }
+    g.SPp = (int)ceil_div(g.RS * g.SEG, 16) * 16;
+    g.XW = g.SEG + d.KW - 1;
+    const int xr = g.RS * g.XW > g.SPp + 2 * (d.KW - 1) ? g.RS * g.XW : g.SPp + 2 * (d.KW - 1);
+    g.XR = (int)ceil_div(xr, 4) * 4;
+    g.G = d.N * d.OH * g.nseg;
+    g.nst = (int)ceil_div(g.G, g.RS);
+    g.ict = d.IC / 128;
+    g.oct = d.OC / 128;
+    g.tiles = d.KH * g.ict * g.oct;
+    int S = 256 / g.tiles;
+    if (S < 1) S = 1;
+    if (S > g.nst) S = g.nst;
+    g.spb = (int)ceil_div(g.nst, S);
+    g.S = (int)ceil_div(g.nst, g.spb);
+    g.Kdim = d.KH * d.KW * d.IC;
+    g.fnseg = make_fastdiv(g.nseg);
+    g.fOH = make_fastdiv(d.OH);
+    return g;
+}
+
+size_t dw3_lds(const Dw3Geom& g) { return (size_t)2 * (g.SPp + g.XR) * 256; }
+
+template <int KW_>
+hipError_t launch_dw3_kw(const bf16* x, const bf16* dz, const Dw3Geom& g, float* part, float* part_db, int want_db,
+                         hipStream_t s) {
+    auto kern = dw3_kernel<KW_>;
+    static bool raised = false;  // the dynamic LDS limit is raised once per instantiation
+    if (!raised) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 160 * 1024);
+        if (e != hipSuccess) return e;
+        raised = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(g.S * g.tiles)), dim3(NT), dw3_lds(g), s, x, dz, g, part, part_db,
+                       want_db);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool igemm_dw_supported(int dt, const ConvDims& d) {
@@ -574,13 +1004,31 @@ bool igemm_dw_supported(int dt, const ConvDims& d) {
 }
 
 size_t igemm_dw_ws_bytes(int dt, const ConvDims& d) {
-    const Plan p = plan(dt, d);
+    const bool s1 = dw3_ok(dt, d);
+    const int S = s1 ? plan3(d).S : plan(dt, d).S;
+    const int Sdb = s1 ? S * d.KH : S;  // bias partials: one per slab (and kernel row)
     const size_t Kdim = (size_t)d.KH * d.KW * d.IC;
-    return align_up((size_t)p.S * d.OC * Kdim * 4, 256) + align_up((size_t)p.S * d.OC * 4, 256);
+    return align_up((size_t)S * d.OC * Kdim * 4, 256) + align_up((size_t)Sdb * d.OC * 4, 256);
 }
 
 hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, float* db, int accumulate,
                            const ConvDims& d, void* ws, hipStream_t s) {
+    if (dw3_ok(dt, d)) {
+        const Dw3Geom g = plan3(d);
+        float* part = (float*)ws;
+        float* part_db = (float*)((char*)ws + align_up((size_t)g.S * d.OC * g.Kdim * 4, 256));
+        const int want_db = db != nullptr;
+        const bf16 *xb = (const bf16*)x, *zb = (const bf16*)dz;
+        hipError_t e = hipErrorInvalidValue;
+        if (d.KW == 3) e = launch_dw3_kw<3>(xb, zb, g, part, part_db, want_db, s);
+        else if (d.KW == 2) e = launch_dw3_kw<2>(xb, zb, g, part, part_db, want_db, s);
+        else e = launch_dw3_kw<1>(xb, zb, g, part, part_db, want_db, s);
+        if (e != hipSuccess) return e;
+        const int64_t count = (int64_t)d.OC * g.Kdim;
+        dw_reduce4<<<reduce_grid(count, d.OC, db != nullptr), NT, 0, s>>>(part, part_db, dw, db, count, d.OC, g.S,
+                                                                          g.S * g.KH, accumulate);
+        return hipGetLastError();
+    }
     const Plan p = plan(dt, d);
     DwGeom g{d.N, d.H, d.W, d.IC, d.OC, d.KW, d.sh, d.sw, d.ph, d.pw, d.OH, d.OW,
              d.KH * d.KW * d.IC, d.N * d.OH * d.OW, p.Pc, p.tiles_n, p.S};
@@ -614,8 +1062,8 @@ hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, flo
     }
     if (e != hipSuccess) return e;
     const int64_t count = (int64_t)d.OC * g.Kdim;
-    dw_reduce4<<<(unsigned)ceil_div(count / 4, 64), NT, 0, s>>>(part, part_db, dw, db, count, d.OC, p.S,
-                                                                accumulate);
+    dw_reduce4<<<reduce_grid(count, d.OC, db != nullptr), NT, 0, s>>>(part, part_db, dw, db, count, d.OC, p.S, p.S,
+                                                                      accumulate);
     return hipGetLastError();
 }
 

@@ -387,8 +387,8 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 // fragment order (frag_weights below): the B fragment of 32 rows x 16 k that a wave needs
 // for one MFMA k-step is 1 KB contiguous, so every weight load instruction reads whole
 // cache lines.  Each wave loads its own B fragments straight into registers one step
-// ahead; LDS holds only the input halo, whose next chunk is copied in slices during the
-// current one (two buffers) or after it (one buffer).  Waves therefore only meet at chunk
+// ahead; LDS holds only the input halo, whose next chunk is copied during the current one
+// (two buffers) or after it (one buffer).  Waves therefore only meet at chunk
 // boundaries, where each waits for all of its outstanding vector-memory operations:
 // LDS-DMA copies and register loads need not complete in issue order with respect to
 // each other, so a count that mixes the two kinds proves nothing.
@@ -443,8 +443,6 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
             dma16(src, __builtin_amdgcn_readfirstlane(dstb + grp * 1024));
         }
     };
-    const int parts = taps > 1 ? taps - 1 : 1;  // slices of the next halo per chunk
-
     const int wm = wid / WN, wn = wid % WN;
     const int lr = lane & 31, lg = lane >> 5;
     int hpos[TM];
@@ -507,11 +505,9 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) MM::run(acc[i][j], fa[kk & 1][i], cur[j][kk]);
-            // A slice of the next chunk's halo, issued after this step's first use of `cur`:
-            // the next wait for a weight load lies a full step ahead.
-            if (kk == 0 && two && c + 1 < g.nchunks && tap < parts)
-                issue_halo(c + 1, tap * JH / parts, (tap + 1) * JH / parts);
+                for (int j = 0; j < TN; ++j) MM::run(acc[i][j], cur[j][kk], fa[kk & 1][i]);
+            // The next chunk's halo, issued once this chunk's first MFMAs are under way.
+            if (kk == 0 && two && c + 1 < g.nchunks && tap == 0) issue_halo(c + 1, 0, JH);
         }
         if (tap == taps - 1 && c + 1 < g.nchunks) {
             if (two) {
@@ -531,18 +527,27 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     }
     __syncthreads();
 
-    // epilogue: stored values -> LDS (rows of BN + 16 bytes) -> 16-byte vectors
+    // epilogue: stored values -> LDS (rows of BN + 16 bytes) -> 16-byte vectors.  The
+    // accumulators hold the transposed tile (MFMA rows are channels, columns pixels), so
+    // a lane owns 4 consecutive channels of one pixel per row group: one 8-byte write.
     constexpr int LDC = BN + VEC;
     bf16* Cs = (bf16*)smem;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int cl = wn * TN * MF + j * MF + lr;
-        const float bj = out.colbias(n0 + cl);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int g4 = 0; g4 < MM::NE / 4; ++g4) {
+            const int cl = wn * TN * MF + j * MF + MM::row(lg, 4 * g4);  // 4 consecutive channels
+            float bj[4];
 #pragma unroll
-            for (int e = 0; e < MM::NE; ++e)
-                Cs[(wm * TM * MF + i * MF + MM::row(lg, e)) * LDC + cl] = from_f32<bf16>(acc[i][j][e] + bj);
+            for (int q = 0; q < 4; ++q) bj[q] = out.colbias(n0 + cl + q);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int m = wm * TM * MF + i * MF + lr;
+                const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * g4] + bj[0], acc[i][j][4 * g4 + 1] + bj[1]),
+                                           pack_bf16x2(acc[i][j][4 * g4 + 2] + bj[2], acc[i][j][4 * g4 + 3] + bj[3]));
+                *(uint2*)(Cs + m * LDC + cl) = v;
+            }
+        }
     }
     __syncthreads();
     constexpr int OVR = BN / VEC;

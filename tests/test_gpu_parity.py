@@ -58,6 +58,12 @@ MEDIUM = [
     # two-row images: the halo only fits LDS once, so later chunks reload it in place
     ((2, 2, 256, 128, 64, 7, 7, 1, 1, 3, 3), WL.BF16, WL.ACT_RELU),
     ((2, 2, 256, 64, 128, 7, 7, 1, 1, 3, 3), WL.BF16, WL.ACT_IDENTITY),
+    # stride-1 bf16 weight gradient with shared input rows: one- and two-row stages,
+    # segmented rows, padded stages, 1-3 taps wide, several channel tiles
+    ((2, 9, 70, 128, 256, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+    ((1, 5, 300, 128, 128, 2, 3, 1, 1, 0, 1), WL.BF16, WL.ACT_IDENTITY),
+    ((3, 7, 40, 256, 128, 3, 1, 1, 1, 1, 0), WL.BF16, WL.ACT_TANH),
+    ((2, 11, 33, 128, 128, 1, 2, 1, 1, 0, 0), WL.BF16, WL.ACT_SIGMOID),
 ]
 
 
