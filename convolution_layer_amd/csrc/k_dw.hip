@@ -540,8 +540,8 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
 // positions x 128 ic); tap kw reads the input tile at a row offset of kw.  That loads
 // about a third of the bytes per FLOP of the per-tap gather above.  Operands are read
 // with transposing LDS reads into 32x32x16 MFMA fragments (lane l: column l%32,
-// positions 8*(l/32) .. +7 of the k-step).  One workgroup per CU (the stage ring is
-// ~115 KB), so each wave may hold 2*KW accumulator fragments per operand row pair.
+// positions 8*(l/32) .. +7 of the k-step).  One workgroup of eight waves per CU (the
+// stage ring is ~115 KB); each wave holds 2 x KW accumulator fragments.
 struct Dw3Geom {
     int N, H, W, IC, OC, KH, KW, OH, OW, ph, pw;
     int SEG, RS, nseg;  // stage: RS segments of SEG positions of output rows
@@ -559,11 +559,14 @@ struct Dw3Geom {
 // 32-byte column piece by one transposing read land in 4 different quarters of the banks.
 __device__ __forceinline__ int sw3(int row) { return (row & 3) << 2; }
 
+constexpr int kDw3Threads = 512;  // eight waves: two per SIMD, so one wave's address work overlaps the other's MFMAs
+
 template <int KW_>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void dw3_kernel(
+__global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw3_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ dz, Dw3Geom g, float* __restrict__ part,
     float* __restrict__ part_db, int want_db) {
-    constexpr int TM = 2, TN = 2 * KW_;  // wave tile 64 oc x KW*64 columns (waves 2 x 2)
+    constexpr int NW = kDw3Threads / 64;
+    constexpr int TM = 2, TN = KW_;  // wave tile 64 oc x KW*32 columns (waves 2 x 4)
     extern __shared__ __align__(1024) unsigned char smem[];
     const int t = threadIdx.x, lane = t & 63;
     const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -583,12 +586,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const bool do_db = want_db && ict_i == 0;
 
     // Copy instructions of a stage: NA for dz (4 rows of 256 bytes each), then NB for the
-    // input rows; this wave issues instructions wid, wid + 4, ...  Lane l copies 16-byte
+    // input rows; this wave issues instructions wid, wid + NW, ...  Lane l copies 16-byte
     // chunk l%16 of row 4j + l/16; the swizzle of that row depends on l/16 only.
     const int NA = g.SPp / 4, NB = g.XR / 4;
     const int rsub = lane >> 4;
     const int choff = ((lane & 15) ^ sw3(rsub)) * 16;  // source byte offset of the chunk
-    const int nmine = (NA + NB - wid + 3) / 4;          // instructions of this wave per stage
+    const int nmine = (NA + NB - wid + NW - 1) / NW;    // instructions of this wave per stage
     // Segment data of the stage being copied: uniform per workgroup.
     struct Segs {
         const char* dzb[2];  // first dz pixel of segment r (+ oc0), bytes
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // issue this wave's copy instructions i0 .. i1-1 of a stage
     auto issue = [&](const Segs& sg, int i0, int i1) {
         for (int i = i0; i < i1; ++i) {
-            const int j = wid + 4 * i;
+            const int j = wid + NW * i;
             const void* src = &kZero16;
             uint32_t dst;
             if (j < NA) {
@@ -650,7 +653,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
     };
 
-    const int wm = wid >> 1, wn = wid & 1;
+    const int wm = wid >> 2, wn = wid & 3;
     floatx16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         for (int i = 0; i < TM; ++i) a_off[i][half] = lds_off(prow[half], wm * 64 + i * 32);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = wn * KW_ * 64 + j * 32;  // tap col/128, input channel col%128
+            const int col = wn * KW_ * 32 + j * 32;  // tap col/128, input channel col%128
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh)
                 b_off[j][half][sh] = lds_off(prow[half] + (col >> 7) + sh * (g.XW - g.SEG), col & 127);
@@ -722,12 +725,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     };
 
     // Column sums of dz for the bias gradient: thread t owns chunk t%16 (8 channels) of
-    // rows kh + KH*(t/16), kh + KH*(t/16 + 16), ...
+    // rows kh + KH*(t/16), kh + KH*(t/16 + 32), ...
+    constexpr int RG = kDw3Threads / 16;  // row groups
     float dbs[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) dbs[j] = 0.0f;
     auto db_sum = [&](const unsigned char* As) {
-        for (int row = kh + g.KH * (t >> 4); row < g.SPp; row += 16 * g.KH) {
+        for (int row = kh + g.KH * (t >> 4); row < g.SPp; row += RG * g.KH) {
             const uint4 v = *(const uint4*)(As + row * 256 + (((t & 15) ^ sw3(row)) << 4));
             const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -779,7 +783,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = wn * KW_ * 64 + j * 32;
+            const int col = wn * KW_ * 32 + j * 32;
             const int k = (kh * g.KW + (col >> 7)) * g.IC + ic0 + (col & 127) + (lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -789,13 +793,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
     if (do_db) {  // uniform per workgroup
         __syncthreads();
-        float* red = (float*)smem;  // [16][128]; the ring is no longer needed
+        float* red = (float*)smem;  // [RG][128]; the ring is no longer needed
 #pragma unroll
         for (int j = 0; j < 8; ++j) red[(t >> 4) * 128 + (t & 15) * 8 + j] = dbs[j];
         __syncthreads();
         if (t < 128) {
             float s_ = 0.0f;
-            for (int q = 0; q < 16; ++q) s_ += red[q * 128 + t];
+            for (int q = 0; q < RG; ++q) s_ += red[q * 128 + t];
             part_db[((int64_t)slab * g.KH + kh) * g.OC + oc0 + t] = s_;
         }
     }
@@ -991,8 +995,8 @@ hipError_t launch_dw3_kw(const bf16* x, const bf16* dz, const Dw3Geom& g, float*
         if (e != hipSuccess) return e;
         raised = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(g.S * g.tiles)), dim3(NT), dw3_lds(g), s, x, dz, g, part, part_db,
-                       want_db);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(g.S * g.tiles)), dim3(kDw3Threads), dw3_lds(g), s, x, dz, g, part,
+                       part_db, want_db);
     return hipGetLastError();
 }
 
