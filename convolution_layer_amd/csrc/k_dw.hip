@@ -547,6 +547,7 @@ struct Dw3Geom {
     int SEG, RS, nseg;  // stage: RS segments of SEG positions of output rows
     int SPp;            // positions per stage, padded to a multiple of 16
     int XW, XR;         // input positions per segment (SEG + KW - 1), input rows per stage
+    int XWp;            // LDS row of the second segment's first input row (SEG + a multiple of 4)
     int G;              // segments in all (N*OH*nseg)
     int nst;            // stages in all (ceil(G / RS))
     int spb;            // stages per slab
@@ -561,7 +562,9 @@ __device__ __forceinline__ int sw3(int row) { return (row & 3) << 2; }
 
 constexpr int kDw3Threads = 512;  // eight waves: two per SIMD, so one wave's address work overlaps the other's MFMAs
 
-template <int KW_>
+// NK: k-steps per stage when known at compile time (0: read from the geometry); with a
+// fixed count every LDS offset of a k-step is an immediate.
+template <int KW_, int NK>
 __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw3_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ dz, Dw3Geom g, float* __restrict__ part,
     float* __restrict__ part_db, int want_db) {
@@ -641,8 +644,8 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
             } else {
                 const int jb = j - NA;
                 const int xr = 4 * jb + rsub;
-                const bool r = xr >= g.XW;
-                const int qq = r ? xr - g.XW : xr;
+                const bool r = xr >= g.XWp;
+                const int qq = r ? xr - g.XWp : xr;
                 const char* xb = r ? sg.xb[1] : sg.xb[0];
                 const int iw = (r ? sg.w0[1] : sg.w0[0]) + qq - g.pw;
                 if (xb != nullptr && qq < g.XW && (r ? sg.len[1] : sg.len[0]) > 0 && (unsigned)iw < (unsigned)g.W)
@@ -665,16 +668,16 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
     // Transposing fragment read: lane l gets column c + l%32 at positions
     // kk + 8*(l/32) .. +7; in each 16-lane group lane i addresses position +i/4 of a
     // half and the 8-byte piece 4*(i%4) of the group's 16 columns.  Input rows of tap kw
-    // sit kw rows further, and the second segment of a stage starts XW - SEG rows later.
-    // k-steps start at multiples of 16, so the swizzle of a lane's row does not depend on
-    // the k-step: every offset is kk*256 plus a per-lane constant (two constants for the
-    // input rows, with and without the second segment's shift).
+    // sit kw rows further; the second segment's rows start XWp - SEG rows later, a
+    // multiple of 4, so the swizzle is unchanged.  k-steps start at multiples of 16, so
+    // every offset is a per-lane constant plus kk*256 (plus the second-segment shift).
+    typedef short dw_short8 __attribute__((ext_vector_type(8)));
     const int l16 = lane & 15, hi = (lane >> 4) & 1, kb8 = 8 * (lane >> 5);
     auto lds_off = [&](int row, int c) {
         const int cb = 2 * (c + 16 * hi + 4 * (l16 & 3));
         return row * 256 + ((((cb >> 4) ^ sw3(row)) << 4) | (cb & 15));
     };
-    int a_off[TM][2], b_off[TN][2][2];
+    int a_off[TM][2], b_off[TN][2];
     int prow[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -684,37 +687,30 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int col = wn * KW_ * 32 + j * 32;  // tap col/128, input channel col%128
-#pragma unroll
-            for (int sh = 0; sh < 2; ++sh)
-                b_off[j][half][sh] = lds_off(prow[half] + (col >> 7) + sh * (g.XW - g.SEG), col & 127);
+            b_off[j][half] = lds_off(prow[half] + (col >> 7), col & 127);
         }
     }
-    auto read_frags = [&](const unsigned char* As, const unsigned char* Xs, int kk, uint4 (&af)[TM],
-                          uint4 (&bf)[TN]) {
-        dw_short4 h[2];
+    const int seg_shift = (g.XWp - g.SEG) * 256;
+    auto read_frags = [&](const unsigned char* As, const unsigned char* Xs, int kk, dw_short8 (&af)[TM],
+                          dw_short8 (&bf)[TN]) {
+        const unsigned char* Ak = As + kk * 256;
+        const unsigned char* Xk = Xs + kk * 256;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(As + kk * 256 + a_off[i][half]));
-            af[i] = make_uint4(__builtin_bit_cast(uint2, h[0]).x, __builtin_bit_cast(uint2, h[0]).y,
-                               __builtin_bit_cast(uint2, h[1]).x, __builtin_bit_cast(uint2, h[1]).y);
+            const dw_short4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Ak + a_off[i][0]));
+            const dw_short4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Ak + a_off[i][1]));
+            af[i] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        bool second[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) second[half] = kk + prow[half] >= g.SEG;
+        const int sh0 = kk + prow[0] >= g.SEG ? seg_shift : 0;
+        const int sh1 = kk + prow[1] >= g.SEG ? seg_shift : 0;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int off = second[half] ? b_off[j][half][1] : b_off[j][half][0];
-                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Xs + kk * 256 + off));
-            }
-            bf[j] = make_uint4(__builtin_bit_cast(uint2, h[0]).x, __builtin_bit_cast(uint2, h[0]).y,
-                               __builtin_bit_cast(uint2, h[1]).x, __builtin_bit_cast(uint2, h[1]).y);
+            const dw_short4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Xk + b_off[j][0] + sh0));
+            const dw_short4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Xk + b_off[j][1] + sh1));
+            bf[j] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    auto mfmas = [&](const uint4 (&af)[TM], const uint4 (&bf)[TN]) {
+    auto mfmas = [&](const dw_short8 (&af)[TM], const dw_short8 (&bf)[TN]) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -745,7 +741,7 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
     // Stage k: the copies of stage k + 1 go out in slices over the first k-steps of stage
     // k, between MFMA groups, so their address arithmetic overlaps the MFMAs; the reads
     // of k-step kk + 1 are issued before the MFMAs of kk.
-    const int nk = g.SPp / 16;
+    const int nk = NK > 0 ? NK : g.SPp / 16;
     const int spread = nk > 2 ? 2 : 1;  // k-steps that carry copies: early, to leave time for them to land
     if (KT > 0) issue(segs_of(0), 0, nmine);
     for (int k = 0; k < KT; ++k) {
@@ -756,24 +752,29 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
         const unsigned char* As = smem + (k & 1) * stage_bytes;
         const unsigned char* Xs = As + g.SPp * 256;
         if (do_db) db_sum(As);
-        uint4 a0[TM], b0[TN], a1[TM], b1[TN];
-        read_frags(As, Xs, 0, a0, b0);
-        int kk = 0;
-        for (; kk + 1 < nk; kk += 2) {
-            read_frags(As, Xs, (kk + 1) * 16, a1, b1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(a0, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (next && kk < spread) issue(sg, kk * nmine / spread, (kk + 1) * nmine / spread);
-            if (kk + 2 < nk) read_frags(As, Xs, (kk + 2) * 16, a0, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(a1, b1);
-            __builtin_amdgcn_sched_barrier(0);
-            if (next && kk + 1 < spread) issue(sg, (kk + 1) * nmine / spread, (kk + 2) * nmine / spread);
-        }
-        if (kk < nk) {
-            mfmas(a0, b0);
-            if (next && kk < spread) issue(sg, kk * nmine / spread, nmine);
+        dw_short8 fa[2][TM], fb[2][TN];
+        read_frags(As, Xs, 0, fa[0], fb[0]);
+        if constexpr (NK > 0) {
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                if (kk + 1 < NK) read_frags(As, Xs, (kk + 1) * 16, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                mfmas(fa[kk & 1], fb[kk & 1]);
+                if (next && kk < spread) issue(sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+            }
+        } else {
+            int kk = 0;
+            for (; kk + 1 < nk; kk += 2) {
+                read_frags(As, Xs, (kk + 1) * 16, fa[1], fb[1]);
+                mfmas(fa[0], fb[0]);
+                if (next && kk < spread) issue(sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+                if (kk + 2 < nk) read_frags(As, Xs, (kk + 2) * 16, fa[0], fb[0]);
+                mfmas(fa[1], fb[1]);
+                if (next && kk + 1 < spread) issue(sg, (kk + 1) * nmine / spread, (kk + 2) * nmine / spread);
+            }
+            if (kk < nk) {
+                mfmas(fa[0], fb[0]);
+                if (next && kk < spread) issue(sg, kk * nmine / spread, nmine);
+            }
         }
     }
 
@@ -964,8 +965,10 @@ Dw3Geom plan3(const ConvDims& d) {
     }
     g.SPp = (int)ceil_div(g.RS * g.SEG, 16) * 16;
     g.XW = g.SEG + d.KW - 1;
-    const int xr = g.RS * g.XW > g.SPp + 2 * (d.KW - 1) ? g.RS * g.XW : g.SPp + 2 * (d.KW - 1);
-    g.XR = (int)ceil_div(xr, 4) * 4;
+    g.XWp = g.SEG + (int)ceil_div(d.KW - 1, 4) * 4;  // same swizzle phase as the first segment
+    const int need_rows = g.RS == 2 ? g.XWp + g.XW : g.XW;
+    const int read_rows = g.SPp + (g.XWp - g.SEG) + d.KW - 1;  // padded positions included
+    g.XR = (int)ceil_div(need_rows > read_rows ? need_rows : read_rows, 4) * 4;
     g.G = d.N * d.OH * g.nseg;
     g.nst = (int)ceil_div(g.G, g.RS);
     g.ict = d.IC / 128;
@@ -984,10 +987,10 @@ Dw3Geom plan3(const ConvDims& d) {
 
 size_t dw3_lds(const Dw3Geom& g) { return (size_t)2 * (g.SPp + g.XR) * 256; }
 
-template <int KW_>
+template <int KW_, int NK>
 hipError_t launch_dw3_kw(const bf16* x, const bf16* dz, const Dw3Geom& g, float* part, float* part_db, int want_db,
                          hipStream_t s) {
-    auto kern = dw3_kernel<KW_>;
+    auto kern = dw3_kernel<KW_, NK>;
     static bool raised = false;  // the dynamic LDS limit is raised once per instantiation
     if (!raised) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1024,9 +1027,12 @@ hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, flo
         const int want_db = db != nullptr;
         const bf16 *xb = (const bf16*)x, *zb = (const bf16*)dz;
         hipError_t e = hipErrorInvalidValue;
-        if (d.KW == 3) e = launch_dw3_kw<3>(xb, zb, g, part, part_db, want_db, s);
-        else if (d.KW == 2) e = launch_dw3_kw<2>(xb, zb, g, part, part_db, want_db, s);
-        else e = launch_dw3_kw<1>(xb, zb, g, part, part_db, want_db, s);
+        const int nk = g.SPp / 16;
+        if (d.KW == 3 && nk == 7) e = launch_dw3_kw<3, 7>(xb, zb, g, part, part_db, want_db, s);
+        else if (d.KW == 3 && nk == 8) e = launch_dw3_kw<3, 8>(xb, zb, g, part, part_db, want_db, s);
+        else if (d.KW == 3) e = launch_dw3_kw<3, 0>(xb, zb, g, part, part_db, want_db, s);
+        else if (d.KW == 2) e = launch_dw3_kw<2, 0>(xb, zb, g, part, part_db, want_db, s);
+        else e = launch_dw3_kw<1, 0>(xb, zb, g, part, part_db, want_db, s);
         if (e != hipSuccess) return e;
         const int64_t count = (int64_t)d.OC * g.Kdim;
         dw_reduce4<<<reduce_grid(count, d.OC, db != nullptr), NT, 0, s>>>(part, part_db, dw, db, count, d.OC, g.S,

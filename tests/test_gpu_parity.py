@@ -64,6 +64,8 @@ MEDIUM = [
     ((1, 5, 300, 128, 128, 2, 3, 1, 1, 0, 1), WL.BF16, WL.ACT_IDENTITY),
     ((3, 7, 40, 256, 128, 3, 1, 1, 1, 1, 0), WL.BF16, WL.ACT_TANH),
     ((2, 11, 33, 128, 128, 1, 2, 1, 1, 0, 0), WL.BF16, WL.ACT_SIGMOID),
+    ((1, 6, 50, 128, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),      # 7 k-steps, padded
+    ((1, 4, 60, 128, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_IDENTITY),  # 8 k-steps, padded
 ]
 
 
