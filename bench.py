@@ -63,7 +63,7 @@ def source_hash() -> str:
 class Layer:
     """Device buffers and the four library calls of one training step."""
 
-    def __init__(self, wl: WL.Workload):
+    def __init__(self, wl: WL.Workload, x=None):
         import torch
 
         import convolution_layer_amd as cm
@@ -73,7 +73,8 @@ class Layer:
         d = WL.make_inputs(wl)
         self.desc = G.desc_for(wl)
         dev = lambda a, t=None: G.dev(a, t)
-        self.x, self.w = dev(d["x"], dt), dev(d["w"], dt)
+        self.x = x if x is not None else dev(d["x"], dt)  # a chained layer takes the previous y
+        self.w = dev(d["w"], dt)
         self.b = dev(d.get("b"))
         self.dy = dev(d["dy"], dt)
         self.bn = wl.norm == WL.NORM_BATCH
@@ -174,6 +175,123 @@ def time_graph(f, calls=20, replays=10):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / (calls * replays), g
+
+
+REPORT_ORDER = ("c1", "c2a", "c2b", "c2c", "c3", "c4", "c5")
+
+
+def call_bytes(wl: WL.Workload, call: str) -> int:
+    """Algorithmic HBM bytes of one call: what the operation itself must read and write."""
+    s = wl.shape
+    e = 2 if wl.dtype == WL.BF16 else 4
+    x, w, y = s.N * s.H * s.W * s.IC, s.OC * s.KH * s.KW * s.IC, s.P * s.OC
+    if call == "forward":  # x, w, bias, z and y (batch norm: + the statistics pass over z)
+        return (x + w + 2 * y) * e + 4 * s.OC + (y * e if wl.norm == WL.NORM_BATCH else 0)
+    if call == "bn_stats":
+        return y * e
+    if call == "activation_backward":  # z, dy -> dz
+        return 3 * y * e
+    if call == "backward_data":  # dz, w -> dx
+        return (y + w + x) * e
+    if call == "backward_weight":  # x, dz -> dw (fp32), db
+        return (x + y) * e + 4 * w + 4 * s.OC
+    raise ValueError(call)
+
+
+def graph_ms(fs, k, replays):
+    """Per-replay device times (ms) of a HIP graph holding k rounds of the calls fs."""
+    import torch
+    for f in fs:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(k):
+            for f in fs:
+                f()
+    g.replay()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    del g
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def cold_warm_ms(f, replays=10):
+    """Device time of one call, warm and cold.  Warm: K calls in one HIP graph, per-call
+    time = replay time / K.  Cold: K rounds of (write 512 MB, call) minus K rounds of the
+    write alone, / K; the write evicts L2 and the 256 MB MALL, so the call reads HBM.
+    Returns (warm per-replay array, cold per-replay array, K), all per call in ms."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    state = {"v": 0}
+
+    def evict():
+        state["v"] = state["v"] % 250 + 1  # non-zero fill: a kernel, not a memset node
+        flush.fill_(state["v"])
+
+    est = time_call(f, 3)  # ms, host gaps included: only sizes the graphs
+    k = int(max(1, min(50, round(0.5 / max(est, 1e-3)))))
+    warm = graph_ms([f], k, replays) / k
+    both = graph_ms([evict, f], k, replays)
+    alone = graph_ms([evict], k, replays)
+    cold = (both - np.median(alone)) / k
+    del flush
+    return warm, cold, k
+
+
+def report(replays=10):
+    """Every configuration, every call: device time warm and cold (see cold_warm_ms),
+    median / p10 / p90 over the replays."""
+    import torch
+    prev_y, out = None, []
+    for name in REPORT_ORDER:
+        wl = WL.WORKLOADS[name]
+        layer = Layer(wl, x=prev_y if wl.x_dist[0] == "chain" else None)
+        layer.forward()
+        torch.cuda.synchronize()
+        prev_y = layer.y.clone() if name in ("c2a", "c2b") else None
+        calls = [("forward", layer.forward)]
+        if layer.bn:
+            calls.append(("bn_stats", layer.bn_stats))
+        calls += [("activation_backward", layer.act_bwd), ("backward_data", layer.bwd_data),
+                  ("backward_weight", layer.bwd_weight)]
+        for cname, f in calls:
+            warm, cold, k = cold_warm_ms(f, replays)
+            row = {"config": name, "call": cname, "dtype": wl.dtype, "graph_calls": k,
+                   "warm_ms": {q: round(float(np.percentile(warm, p)), 5) for q, p in (("p10", 10), ("median", 50), ("p90", 90))},
+                   "cold_ms": {q: round(float(np.percentile(cold, p)), 5) for q, p in (("p10", 10), ("median", 50), ("p90", 90))}}
+            med = row["warm_ms"]["median"]
+            by = call_bytes(wl, cname)
+            row["GB/s"] = round(by / (med * 1e-3) / 1e9, 1)
+            row["hbm_frac"] = round(row["GB/s"] / PEAK_HBM_GBS, 4)
+            row["cold_GB/s"] = round(by / (row["cold_ms"]["median"] * 1e-3) / 1e9, 1)
+            row["cold_hbm_frac"] = round(row["cold_GB/s"] / PEAK_HBM_GBS, 4)
+            if cname in ("forward", "backward_data", "backward_weight"):
+                tf = wl.shape.flops() / (med * 1e-3) / 1e12
+                row["TFLOP/s"] = round(tf, 3)
+                row["mfma_frac"] = round(tf / PEAK_TFLOPS[wl.dtype], 4)
+            out.append(row)
+            print(json.dumps(row), flush=True)
+        del layer
+        torch.cuda.empty_cache()
+    print()
+    print("warm: K calls per HIP graph replay (inputs may sit in the 256 MB MALL); cold: after a 512 MB write")
+    print("TFLOP/s and %MFMA from the warm median; GB/s = algorithmic bytes / median time")
+    print(f"{'cfg':5} {'call':20} {'dtype':5} {'warm us':>9} {'p10':>8} {'p90':>8} {'cold us':>9} {'p10':>8} "
+          f"{'p90':>8} {'TFLOP/s':>9} {'%MFMA':>7} {'warm GB/s':>10} {'cold GB/s':>10} {'%HBM cold':>9}")
+    for r in out:
+        w, c = r["warm_ms"], r["cold_ms"]
+        tf = f"{r['TFLOP/s']:9.2f} {100 * r['mfma_frac']:6.1f}%" if "TFLOP/s" in r else f"{'':9} {'':7}"
+        print(f"{r['config']:5} {r['call']:20} {r['dtype']:5} {1e3 * w['median']:9.2f} {1e3 * w['p10']:8.2f} "
+              f"{1e3 * w['p90']:8.2f} {1e3 * c['median']:9.2f} {1e3 * c['p10']:8.2f} {1e3 * c['p90']:8.2f} {tf} "
+              f"{r['GB/s']:10.1f} {r['cold_GB/s']:10.1f} {100 * r['cold_hbm_frac']:8.1f}%")
 
 
 def cpu_baseline(wl: WL.Workload, n_images: int):
@@ -295,9 +413,14 @@ def main():
     ap.add_argument("--only", choices=("forward", "activation_backward", "backward_data", "backward_weight"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--report", action="store_true",
+                    help="time every call of every configuration (warm and cold) instead of the bench step")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.report:
+        report()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is not built.",
@@ -345,15 +468,19 @@ def main():
         torch.cuda.synchronize()
         ref = (bn_layer.sm.clone(), bn_layer.si.clone())
         eager_ms = time_call(bn_layer.bn_stats, 50)
-        bn_ms, graph = time_graph(bn_layer.bn_stats)
+        warm, cold, k = cold_warm_ms(bn_layer.bn_stats)
         # every replay recomputes the same statistics (the call is deterministic)
         if not (torch.equal(ref[0], bn_layer.sm) and torch.equal(ref[1], bn_layer.si)):
             raise RuntimeError("graph replay of bn_stats_training differs from the eager call")
-        del graph
+        bn_ms, cold_ms = float(np.median(warm)), float(np.median(cold))
         zbytes = bn_wl.shape.P * bn_wl.shape.OC * 4
         bn_gbs = zbytes / (bn_ms * 1e-3) / 1e9
+        cold_gbs = zbytes / (cold_ms * 1e-3) / 1e9
         bn = {"workload": "c3", "bytes": zbytes, "ms": round(bn_ms, 5), "GB/s": round(bn_gbs, 1),
-              "frac": round(bn_gbs / PEAK_HBM_GBS, 4), "timing": "HIP graph of 20 calls, 10 replays",
+              "frac": round(bn_gbs / PEAK_HBM_GBS, 4), "cold_ms": round(cold_ms, 5),
+              "cold_GB/s": round(cold_gbs, 1), "cold_frac": round(cold_gbs / PEAK_HBM_GBS, 4),
+              "timing": f"HIP graph of {k} calls, median of 10 replays; cold = after a 512 MB write that "
+                        "evicts L2 and MALL (write time subtracted)",
               "eager_ms_per_call": round(eager_ms, 5)}
         log(f"bench: bn_stats {bn}")
         del bn_layer
