@@ -46,6 +46,8 @@ def _load(path: str, rebuild: bool = False):
     L.oracle_apply_activation.argtypes = [_D, _i, _i, C.c_int, C.c_int, _D, _D, _D, _D, _D]
     L.oracle_activation_backward.argtypes = [_D, _D, _i, _i, C.c_int, C.c_int, _D, _D, _D, _D,
                                              _D, _D, _D]
+    L.oracle_bn_eval_stats.argtypes = [_D, _D, _i, C.c_double, _D, _D]
+    L.oracle_activation_backward_eval.argtypes = [_D, _D, _i, _i, C.c_int, _D, _D, _D, _D, _D, _D, _D]
     L.oracle_conv2d_backward_data.argtypes = [_D, _D, _D] + dims
     L.oracle_conv2d_backward_data_at.argtypes = [_D, _D, _L, _i, _D] + dims
     L.oracle_conv2d_backward_weight.argtypes = [_D, _D, _D, _D] + dims
@@ -136,6 +138,14 @@ def bn_stats(z, momentum=0.1, eps=1e-5, running_mean=None, running_var=None):
     return mean, var, inv, rm, rv
 
 
+def bn_eval_stats(running_mean, running_var, eps=1e-5):
+    """Evaluation-mode statistics: (mean, inv_std) from the running pair."""
+    rm, rv = _f64(running_mean), _f64(running_var)
+    mean, inv = np.zeros(rm.size), np.zeros(rm.size)
+    lib().oracle_bn_eval_stats(_p(rm), _p(rv), rm.size, eps, _p(mean), _p(inv))
+    return mean, inv
+
+
 def apply_activation(z, act, norm=NORM_NONE, gamma=None, beta=None, mean=None, inv_std=None):
     z = _f64(z)
     C_ = z.shape[-1]
@@ -145,14 +155,21 @@ def apply_activation(z, act, norm=NORM_NONE, gamma=None, beta=None, mean=None, i
     return y
 
 
-def activation_backward(z, dy, act, norm=NORM_NONE, gamma=None, beta=None, mean=None, inv_std=None):
-    """Returns (dz, dgamma, dbeta); dgamma/dbeta are None without batch norm."""
+def activation_backward(z, dy, act, norm=NORM_NONE, gamma=None, beta=None, mean=None, inv_std=None,
+                        evaluation=False):
+    """Returns (dz, dgamma, dbeta); dgamma/dbeta are None without batch norm.
+    evaluation=True takes the batch-norm statistics as constants (evaluation mode)."""
     z, dy = _f64(z), _f64(dy)
     assert z.shape == dy.shape
     C_ = z.shape[-1]
     dz = np.zeros_like(z)
     dg = np.zeros(C_) if norm == NORM_BATCH else None
     dbt = np.zeros(C_) if norm == NORM_BATCH else None
+    if evaluation and norm == NORM_BATCH:
+        lib().oracle_activation_backward_eval(_p(z), _p(dy), z.size // C_, C_, act, _p(_f64(gamma)),
+                                              _p(_f64(beta)), _p(_f64(mean)), _p(_f64(inv_std)), _p(dz),
+                                              _p(dg), _p(dbt))
+        return dz, dg, dbt
     lib().oracle_activation_backward(_p(z), _p(dy), z.size // C_, C_, act, norm, _p(_f64(gamma)),
                                      _p(_f64(beta)), _p(_f64(mean)), _p(_f64(inv_std)), _p(dz),
                                      _p(dg), _p(dbt))

@@ -158,6 +158,17 @@ void oracle_bn_stats(const double* z, i64 M, i64 C, double momentum, double eps,
     }
 }
 
+/* Evaluation mode: the running statistics stand in for the batch ones.
+ *   mean = running_mean,  inv_std = 1 / sqrt(running_var + eps);  nothing is updated.
+ * [generic] forward, evaluation-mode branch of the batch-norm statistics. */
+void oracle_bn_eval_stats(const double* running_mean, const double* running_var, i64 C, double eps,
+                          double* mean, double* inv_std) {
+    for (i64 c = 0; c < C; ++c) {
+        mean[c] = running_mean[c];
+        inv_std[c] = 1.0 / sqrt(running_var[c] + eps);
+    }
+}
+
 /* ------------------------------------------------------- a3 normalise + activate ---- */
 /* a = z (no norm) or gamma*(z-mean)*inv_std + beta (batch norm); y = act(a).
  * [generic] forward phase 3 and the no-norm branch; [cuda] bn_forward_affine. */
@@ -226,6 +237,36 @@ void oracle_activation_backward(const double* z, const double* dy, i64 M, i64 C,
                                              : act_slope(act, a);
             double dzh = slope * dy[i] * g;
             dz[i] = is / (double)M * ((double)M * dzh - s1 - zh * s2);
+        }
+        if (dgamma) dgamma[c] = sg;
+        if (dbeta) dbeta[c] = sb;
+    }
+}
+
+/* Evaluation-mode batch-norm backward: the statistics are constants, so each element
+ * stands alone:
+ *   zhat = (z - mean) * inv_std,  a = gamma*zhat + beta,  dno = act'(a) * dy,
+ *   dz = dno * gamma * inv_std;   per channel dgamma = sum dno*zhat, dbeta = sum dno
+ * (written, not accumulated).  [generic] backward_input and backward, evaluation-mode
+ * branches.  dgamma/dbeta may be NULL. */
+void oracle_activation_backward_eval(const double* z, const double* dy, i64 M, i64 C, int act,
+                                     const double* gamma, const double* beta,
+                                     const double* mean, const double* inv_std,
+                                     double* dz, double* dgamma, double* dbeta) {
+#pragma omp parallel for schedule(static)
+    for (i64 c = 0; c < C; ++c) {
+        double g = gamma[c], mu = mean[c], is = inv_std[c];
+        double sg = 0.0, sb = 0.0;
+        for (i64 m = 0; m < M; ++m) {
+            i64 i = m * C + c;
+            double zh = (z[i] - mu) * is;
+            double a = g * zh + beta[c];
+            double slope = (act == ACT_RELU) ? (double)relu_mask_bn_f32(z[i], mu, is, g, beta[c])
+                                             : act_slope(act, a);
+            double dno = slope * dy[i];
+            dz[i] = dno * g * is;
+            sg += dno * zh;
+            sb += dno;
         }
         if (dgamma) dgamma[c] = sg;
         if (dbeta) dbeta[c] = sb;

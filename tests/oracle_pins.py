@@ -387,4 +387,83 @@ def pin_bn_bias_invariance():
     _close(dz, dz0, 1e-10, "bias invariance dz")
 
 
+def _eval_running(C, seed):
+    r = _rng(seed)
+    return r.normal(0, 0.5, C), r.uniform(0.2, 3.0, C)
+
+
+def pin_bn_eval_stats_closed_form():
+    """Evaluation-mode statistics: mean passes the running mean through; running_var =
+    1 - eps gives inv_std = 1 exactly, running_var = 4 - eps gives 1/2, and in general
+    inv_std**2 * (running_var + eps) = 1."""
+    eps = 1e-5
+    rm = np.array([0.25, -3.0, 7.5, 0.0])
+    rv = np.array([1.0 - eps, 4.0 - eps, 0.5, 9.0])
+    mean, inv = O.bn_eval_stats(rm, rv, eps)
+    np.testing.assert_array_equal(mean, rm)
+    assert inv[0] == 1.0 and inv[1] == 0.5
+    _close(inv ** 2 * (rv + eps), np.ones(4), 1e-15, "inv_std^2 (var + eps)")
+
+
+def pin_bn_eval_forward_matches_training_forward():
+    """With running statistics equal to the batch statistics of z (var biased, as the
+    training statistics), the evaluation forward reproduces the training forward."""
+    z, g, bt, _ = _bn_problem(31)
+    mean, var, inv, *_ = O.bn_stats(z, 0.1, 1e-5)
+    em, ei = O.bn_eval_stats(mean, var, 1e-5)
+    for act in (O.ACT_IDENTITY, O.ACT_RELU, O.ACT_TANH, O.ACT_SIGMOID):
+        yt = O.apply_activation(z, act, O.NORM_BATCH, g, bt, mean, inv)
+        ye = O.apply_activation(z, act, O.NORM_BATCH, g, bt, em, ei)
+        _close(ye, yt, 1e-14, f"eval forward act {act}")
+
+
+def pin_bn_eval_backward_vs_torch_autograd():
+    """Evaluation-mode BN + act backward: dz, dgamma, dbeta against torch fp64 autograd
+    through batch_norm(training=False) with the running statistics."""
+    for act, fn in ((O.ACT_IDENTITY, lambda t: t), (O.ACT_RELU, torch.relu), (O.ACT_TANH, torch.tanh),
+                    (O.ACT_SIGMOID, torch.sigmoid)):
+        z, g, bt, dy = _bn_problem(41 + act)
+        rm, rv = _eval_running(z.shape[-1], 45 + act)
+        mean, inv = O.bn_eval_stats(rm, rv, 1e-5)
+        dz, dg, dbt = O.activation_backward(z, dy, act, O.NORM_BATCH, g, bt, mean, inv, evaluation=True)
+        zt = torch.from_numpy(z).permute(0, 3, 1, 2).clone().requires_grad_(True)
+        gt = torch.from_numpy(g).clone().requires_grad_(True)
+        btt = torch.from_numpy(bt).clone().requires_grad_(True)
+        y = fn(F.batch_norm(zt, torch.from_numpy(rm), torch.from_numpy(rv), gt, btt, training=False, eps=1e-5))
+        y.backward(torch.from_numpy(dy).permute(0, 3, 1, 2))
+        _close(dz, zt.grad.permute(0, 2, 3, 1).numpy(), 1e-11, f"eval dz act {act}")
+        _close(dg, gt.grad.numpy(), 1e-11, f"eval dgamma act {act}")
+        _close(dbt, btt.grad.numpy(), 1e-11, f"eval dbeta act {act}")
+
+
+def pin_bn_eval_backward_fd_and_closed_form():
+    """Central differences of L(z, gamma, beta) = <act(gamma*(z - m)*s + beta), dy> with
+    fixed (m, s) match dz, dgamma, dbeta; with gamma = 1, identity activation and s = 1
+    the backward passes dy through: dz = dy, dbeta = sum dy, dgamma = sum dy*(z - m)."""
+    act = O.ACT_TANH
+    z, g, bt, dy = _bn_problem(51, (2, 3, 3, 3))
+    rm, rv = _eval_running(3, 52)
+    mean, inv = O.bn_eval_stats(rm, rv, 1e-5)
+    dz, dg, dbt = O.activation_backward(z, dy, act, O.NORM_BATCH, g, bt, mean, inv, evaluation=True)
+
+    def L(z_, g_, b_):
+        return float(np.sum(O.apply_activation(z_, act, O.NORM_BATCH, g_, b_, mean, inv) * dy))
+
+    h = 1e-6
+    for idx in np.ndindex(*z.shape):
+        e = np.zeros_like(z); e[idx] = h
+        fd = (L(z + e, g, bt) - L(z - e, g, bt)) / (2 * h)
+        assert abs(fd - dz[idx]) < 1e-7, ("eval dz", idx, fd, dz[idx])
+    for c in range(3):
+        e = np.zeros(3); e[c] = h
+        assert abs((L(z, g + e, bt) - L(z, g - e, bt)) / (2 * h) - dg[c]) < 1e-7, ("eval dgamma", c)
+        assert abs((L(z, g, bt + e) - L(z, g, bt - e)) / (2 * h) - dbt[c]) < 1e-7, ("eval dbeta", c)
+    ones, one_inv = np.ones(3), np.ones(3)
+    dz1, dg1, db1 = O.activation_backward(z, dy, O.ACT_IDENTITY, O.NORM_BATCH, ones, bt, rm, one_inv,
+                                          evaluation=True)
+    np.testing.assert_array_equal(dz1, dy)
+    _close(db1, dy.reshape(-1, 3).sum(0), 1e-14, "eval dbeta closed form")
+    _close(dg1, (dy * (z - rm)).reshape(-1, 3).sum(0), 1e-13, "eval dgamma closed form")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -49,6 +49,10 @@ MUTANTS = [
     ("dw_at_tap_sign", "i64 ih = oh * sh - ph + kh;", "i64 ih = oh * sh - ph - kh;", 3),
     ("bias_grad_square", "for (i64 m = 0; m < M; ++m) s += dz[m * C + c];",
      "for (i64 m = 0; m < M; ++m) s += dz[m * C + c] * dz[m * C + c];", 0),
+    ("bneval_eps_dropped", "inv_std[c] = 1.0 / sqrt(running_var[c] + eps);",
+     "inv_std[c] = 1.0 / sqrt(running_var[c]);", 0),
+    ("bneval_inv_std_missing", "dz[i] = dno * g * is;", "dz[i] = dno * g;", 0),
+    ("bneval_dgamma_no_zhat", "sg += dno * zh;", "sg += dno;", 1),
 ]
 
 
