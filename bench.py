@@ -63,7 +63,7 @@ def source_hash() -> str:
 class Layer:
     """Device buffers and the four library calls of one training step."""
 
-    def __init__(self, wl: WL.Workload, x=None):
+    def __init__(self, wl: WL.Workload, x=None, evaluation=False):
         import torch
 
         import convolution_layer_amd as cm
@@ -72,6 +72,8 @@ class Layer:
         s, dt = wl.shape, wl.dtype
         d = WL.make_inputs(wl)
         self.desc = G.desc_for(wl)
+        if evaluation:
+            self.desc.mode = cm.MODE_EVAL
         dev = lambda a, t=None: G.dev(a, t)
         self.x = x if x is not None else dev(d["x"], dt)  # a chained layer takes the previous y
         self.w = dev(d["w"], dt)
@@ -180,13 +182,13 @@ def time_graph(f, calls=20, replays=10):
 REPORT_ORDER = ("c1", "c2a", "c2b", "c2c", "c3", "c4", "c5")
 
 
-def call_bytes(wl: WL.Workload, call: str) -> int:
+def call_bytes(wl: WL.Workload, call: str, evaluation: bool = False) -> int:
     """Algorithmic HBM bytes of one call: what the operation itself must read and write."""
     s = wl.shape
     e = 2 if wl.dtype == WL.BF16 else 4
     x, w, y = s.N * s.H * s.W * s.IC, s.OC * s.KH * s.KW * s.IC, s.P * s.OC
-    if call == "forward":  # x, w, bias, z and y (batch norm: + the statistics pass over z)
-        return (x + w + 2 * y) * e + 4 * s.OC + (y * e if wl.norm == WL.NORM_BATCH else 0)
+    if call == "forward":  # x, w, bias, z and y (training batch norm: + the statistics pass over z)
+        return (x + w + 2 * y) * e + 4 * s.OC + (y * e if wl.norm == WL.NORM_BATCH and not evaluation else 0)
     if call == "bn_stats":
         return y * e
     if call == "activation_backward":  # z, dy -> dz
@@ -262,18 +264,22 @@ def report(replays=10):
             calls.append(("bn_stats", layer.bn_stats))
         calls += [("activation_backward", layer.act_bwd), ("backward_data", layer.bwd_data),
                   ("backward_weight", layer.bwd_weight)]
+        if layer.bn:  # evaluation-mode batch norm: running statistics, constant in the backward
+            ev = Layer(wl, x=layer.x, evaluation=True)
+            ev.forward()
+            calls += [("forward[eval]", ev.forward), ("activation_backward[eval]", ev.act_bwd)]
         for cname, f in calls:
             warm, cold, k = cold_warm_ms(f, replays)
             row = {"config": name, "call": cname, "dtype": wl.dtype, "graph_calls": k,
                    "warm_ms": {q: round(float(np.percentile(warm, p)), 5) for q, p in (("p10", 10), ("median", 50), ("p90", 90))},
                    "cold_ms": {q: round(float(np.percentile(cold, p)), 5) for q, p in (("p10", 10), ("median", 50), ("p90", 90))}}
             med = row["warm_ms"]["median"]
-            by = call_bytes(wl, cname)
+            by = call_bytes(wl, cname.split("[")[0], evaluation=cname.endswith("[eval]"))
             row["GB/s"] = round(by / (med * 1e-3) / 1e9, 1)
             row["hbm_frac"] = round(row["GB/s"] / PEAK_HBM_GBS, 4)
             row["cold_GB/s"] = round(by / (row["cold_ms"]["median"] * 1e-3) / 1e9, 1)
             row["cold_hbm_frac"] = round(row["cold_GB/s"] / PEAK_HBM_GBS, 4)
-            if cname in ("forward", "backward_data", "backward_weight"):
+            if cname in ("forward", "forward[eval]", "backward_data", "backward_weight"):
                 tf = wl.shape.flops() / (med * 1e-3) / 1e12
                 row["TFLOP/s"] = round(tf, 3)
                 row["mfma_frac"] = round(tf / PEAK_TFLOPS[wl.dtype], 4)

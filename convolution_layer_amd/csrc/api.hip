@@ -52,9 +52,8 @@ convmi_status check_desc(const convmi_desc* d, ConvDims* out) {
         return fail(CONVMI_ERR_INVALID_ARG, "unknown activation %d", d->activation);
     if (d->normalization != CONVMI_NORM_NONE && d->normalization != CONVMI_NORM_BATCH)
         return fail(CONVMI_ERR_INVALID_ARG, "unknown normalization %d", d->normalization);
-    if (d->mode == CONVMI_MODE_EVAL)
-        return fail(CONVMI_ERR_UNSUPPORTED, "evaluation mode (running statistics) is not implemented");
-    if (d->mode != CONVMI_MODE_TRAIN) return fail(CONVMI_ERR_INVALID_ARG, "unknown mode %d", d->mode);
+    if (d->mode != CONVMI_MODE_TRAIN && d->mode != CONVMI_MODE_EVAL)
+        return fail(CONVMI_ERR_INVALID_ARG, "unknown mode %d", d->mode);
     if (d->normalization == CONVMI_NORM_BATCH) {
         if (!(d->momentum >= 0.0f && d->momentum <= 1.0f))
             return fail(CONVMI_ERR_INVALID_ARG, "momentum must be in [0, 1]");
@@ -188,6 +187,8 @@ CONVMI_API convmi_status conv2d_forward(const convmi_desc* desc, const void* x, 
         CHECK(need_vec(save_inv_std, "save_inv_std"));
         if ((running_mean == nullptr) != (running_var == nullptr))
             return fail(CONVMI_ERR_INVALID_ARG, "running_mean and running_var must be both given or both NULL");
+        if (desc->mode == CONVMI_MODE_EVAL && running_mean == nullptr)
+            return fail(CONVMI_ERR_INVALID_ARG, "evaluation mode normalises with running_mean/running_var: both required");
         if (running_mean) {
             CHECK(need_vec(running_mean, "running_mean"));
             CHECK(need_vec(running_var, "running_var"));
@@ -210,8 +211,11 @@ CONVMI_API convmi_status conv2d_forward(const convmi_desc* desc, const void* x, 
         e = launch_conv_fwd_direct(desc->dtype, x, w, bias, z, conv_y, d, act, s);
     if (e != hipSuccess) return hip_fail(e, "conv2d_forward: convolution launch");
     if (bn) {
-        e = launch_bn_stats(desc->dtype, z, rows_of(d), d.OC, desc->momentum, desc->eps, save_mean, save_inv_std,
-                            running_mean, running_var, workspace, s);
+        if (desc->mode == CONVMI_MODE_EVAL)  // running statistics, left unchanged
+            e = launch_bn_eval_stats(running_mean, running_var, d.OC, desc->eps, save_mean, save_inv_std, s);
+        else
+            e = launch_bn_stats(desc->dtype, z, rows_of(d), d.OC, desc->momentum, desc->eps, save_mean,
+                                save_inv_std, running_mean, running_var, workspace, s);
         if (e != hipSuccess) return hip_fail(e, "conv2d_forward: batch-norm statistics launch");
         e = launch_apply_act(desc->dtype, z, y, rows_of(d), d.OC, act, 1, gamma, beta, save_mean, save_inv_std, s);
         if (e != hipSuccess) return hip_fail(e, "conv2d_forward: normalise/activate launch");
@@ -265,6 +269,10 @@ CONVMI_API convmi_status bn_stats_training(const convmi_desc* desc, const void* 
     CHECK(check_desc(desc, &d));
     if (desc->normalization != CONVMI_NORM_BATCH)
         return fail(CONVMI_ERR_INVALID_ARG, "bn_stats_training needs normalization = BATCH");
+    if (desc->mode != CONVMI_MODE_TRAIN)
+        return fail(CONVMI_ERR_INVALID_ARG,
+                    "bn_stats_training computes training statistics; in evaluation mode conv2d_forward uses the "
+                    "running statistics");
     CHECK(need(z, "z"));
     CHECK(need_vec(save_mean, "save_mean"));
     CHECK(need_vec(save_inv_std, "save_inv_std"));
@@ -306,7 +314,8 @@ CONVMI_API convmi_status activation_backward(const convmi_desc* desc, const void
         if (dbeta) CHECK(need_vec(dbeta, "dbeta"));
         CHECK(check_ws(workspace, workspace_bytes, ws_act_bwd(desc, d), "activation_backward"));
         e = launch_bn_bwd(desc->dtype, z, dy, dz, rows_of(d), d.OC, desc->activation, gamma, beta, save_mean,
-                          save_inv_std, dgamma, dbeta, accumulate, workspace, s);
+                          save_inv_std, dgamma, dbeta, accumulate, desc->mode == CONVMI_MODE_EVAL ? 1 : 0,
+                          workspace, s);
     } else {
         e = launch_act_bwd(desc->dtype, z, dy, dz, rows_of(d), d.OC, desc->activation, s);
     }

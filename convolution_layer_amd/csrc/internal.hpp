@@ -55,7 +55,9 @@ hipError_t launch_act_bwd(int dt, const void* z, const void* dy, void* dz, int64
 // Batch-norm training backward (+ activation derivative), dgamma/dbeta optional.
 hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_t M, int C, int act,
                          const float* gamma, const float* beta, const float* mean, const float* inv_std,
-                         float* dgamma, float* dbeta, int accumulate, void* ws, hipStream_t s);
+                         float* dgamma, float* dbeta, int accumulate, int evaluation, void* ws, hipStream_t s);
+hipError_t launch_bn_eval_stats(const float* run_mean, const float* run_var, int C, float eps, float* mean,
+                                float* inv_std, hipStream_t s);
 
 // ---------------------------------------------------------------- MFMA implicit GEMM
 // Returns false (and launches nothing) when the shape is outside what the tiled

@@ -245,20 +245,33 @@ __global__ __launch_bounds__(kThreads) void bn_bwd_partials(const T* __restrict_
 }
 
 // Second launch: dgamma (+)= B, dbeta (+)= A and the coefficients of
-// dz = gamma*inv_std*(dno - A/M - zhat*B/M) into coef[c][3].
+// dz = gamma*inv_std*(dno - A/M - zhat*B/M) into coef[c][3].  In evaluation mode the
+// statistics are constants and dz = gamma*inv_std*dno: the two mean terms are zero.
 __global__ __launch_bounds__(kThreads) void bn_bwd_finalize(const float* __restrict__ part, int slabs, int C, int64_t M,
                                                             const float* __restrict__ gamma,
                                                             const float* __restrict__ inv_std,
                                                             float* __restrict__ dgamma, float* __restrict__ dbeta,
-                                                            int accumulate, float* __restrict__ coef) {
+                                                            int accumulate, int evaluation,
+                                                            float* __restrict__ coef) {
     __shared__ double dred[2 * kThreads];
     merge_slabs(part, slabs, C, dred, [&](int c, double A, double B) {
         if (dgamma) dgamma[c] = accumulate ? (float)((double)dgamma[c] + B) : (float)B;
         if (dbeta) dbeta[c] = accumulate ? (float)((double)dbeta[c] + A) : (float)A;
         coef[3 * c + 0] = gamma[c] * inv_std[c];
-        coef[3 * c + 1] = (float)(A / (double)M);
-        coef[3 * c + 2] = (float)(B / (double)M);
+        coef[3 * c + 1] = evaluation ? 0.0f : (float)(A / (double)M);
+        coef[3 * c + 2] = evaluation ? 0.0f : (float)(B / (double)M);
     });
+}
+
+// Evaluation-mode statistics: mean = running_mean, inv_std = 1/sqrt(running_var + eps)
+// (in fp64, then stored in fp32); the running statistics are left unchanged.
+__global__ __launch_bounds__(kThreads) void bn_eval_stats(const float* __restrict__ run_mean,
+                                                          const float* __restrict__ run_var, int C, float eps,
+                                                          float* __restrict__ mean, float* __restrict__ inv_std) {
+    const int c = blockIdx.x * kThreads + threadIdx.x;
+    if (c >= C) return;
+    mean[c] = run_mean[c];
+    inv_std[c] = (float)(1.0 / sqrt((double)run_var[c] + (double)eps));
 }
 
 // y = act(a) with a = z or the batch-norm affine; grid-stride over 16-byte vectors.
@@ -452,9 +465,15 @@ hipError_t launch_act_bwd(int dt, const void* z, const void* dy, void* dz, int64
     return hipGetLastError();
 }
 
+hipError_t launch_bn_eval_stats(const float* run_mean, const float* run_var, int C, float eps, float* mean,
+                                float* inv_std, hipStream_t s) {
+    bn_eval_stats<<<(C + kThreads - 1) / kThreads, kThreads, 0, s>>>(run_mean, run_var, C, eps, mean, inv_std);
+    return hipGetLastError();
+}
+
 hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_t M, int C, int act,
                          const float* gamma, const float* beta, const float* mean, const float* inv_std,
-                         float* dgamma, float* dbeta, int accumulate, void* ws, hipStream_t s) {
+                         float* dgamma, float* dbeta, int accumulate, int evaluation, void* ws, hipStream_t s) {
     RowPlan p = row_plan(M, C, dt);
     float* part = (float*)ws;
     float* coef = (float*)((char*)ws + partial_bytes(p, C));
@@ -467,7 +486,7 @@ hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     bn_bwd_finalize<<<merge_grid(C), block, 0, s>>>(part, p.blocks, C, M, gamma, inv_std, dgamma, dbeta, accumulate,
-                                                    coef);
+                                                    evaluation, coef);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nvec = M * C / p.vec;

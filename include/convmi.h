@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
     CONVMI_OK = 0,
     CONVMI_ERR_INVALID_ARG = 1, /* bad size, stride, pad, enum value, NULL pointer, aliasing */
-    CONVMI_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (e.g. eval mode) */
+    CONVMI_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
     CONVMI_ERR_WORKSPACE = 3,   /* workspace smaller than convmi_workspace_size() */
     CONVMI_ERR_MISALIGNED = 4,  /* a pointer violates the alignment rule above */
     CONVMI_ERR_HIP = 5          /* a HIP launch or runtime call failed */
@@ -75,7 +75,11 @@ typedef enum {
 
 typedef enum { CONVMI_NORM_NONE = 0, CONVMI_NORM_BATCH = 1 } convmi_norm;
 
-/* Only training mode is implemented; CONVMI_MODE_EVAL returns CONVMI_ERR_UNSUPPORTED. */
+/* Batch-norm mode.  TRAIN: batch statistics, running statistics updated.  EVAL: the
+ * running statistics normalise (mean = running_mean, inv_std = 1/sqrt(running_var +
+ * eps)), nothing is updated, and the backward treats the statistics as constants
+ * ([generic] forward and backward_input / backward, evaluation-mode branches).  Without
+ * batch norm the two modes compute the same thing. */
 typedef enum { CONVMI_MODE_TRAIN = 0, CONVMI_MODE_EVAL = 1 } convmi_mode;
 
 typedef enum {
@@ -117,9 +121,11 @@ convmi_status convmi_workspace_size(const convmi_desc* desc, int32_t op, size_t*
  * forward (conv, add bias, bn_stats_training, bn_forward_affine, activation).
  *   x, w: inputs.  bias: fp32 [OC] or NULL (no bias).
  *   gamma, beta, running_mean, running_var, save_mean, save_inv_std: batch norm only
- *     (NULL otherwise).  running_* are updated in place with the biased batch variance
- *     (as on the pages); save_mean / save_inv_std receive the batch mean and
- *     1/sqrt(var+eps) for the backward pass.
+ *     (NULL otherwise).  TRAIN: running_* (optional, both or neither) are updated in
+ *     place with the biased batch variance (as on the pages); save_mean / save_inv_std
+ *     receive the batch mean and 1/sqrt(var+eps) for the backward pass.  EVAL:
+ *     running_* are required and only read; save_mean / save_inv_std receive
+ *     running_mean and 1/sqrt(running_var+eps).
  *   z: pre-activation output (conv + bias).  Required with batch norm; may be NULL
  *     without it.  y: the layer output act(a).  Both overwritten. */
 convmi_status conv2d_forward(const convmi_desc* desc, const void* x, const void* w, const float* bias,
@@ -147,7 +153,8 @@ convmi_status conv2d_backward_weight(const convmi_desc* desc, const void* x, con
 /* a2: per-channel training statistics of z over the N*OH*OW rows: mean, biased var,
  * save_inv_std = 1/sqrt(var+eps); running_mean/var (nullable, both or neither)
  * updated with momentum.  [generic] forward, batch-norm training statistics; [cuda]
- * bn_stats_training. */
+ * bn_stats_training.  TRAIN mode only (INVALID_ARG in EVAL mode, where
+ * conv2d_forward takes the running statistics). */
 convmi_status bn_stats_training(const convmi_desc* desc, const void* z, float* save_mean, float* save_inv_std,
                                 float* running_mean, float* running_var,
                                 void* workspace, size_t workspace_bytes, void* stream);
@@ -160,8 +167,11 @@ convmi_status bn_stats_training(const convmi_desc* desc, const void* z, float* s
  *     dz = inv_std/M * (M*dno*gamma - S1 - zhat*S2), dgamma (+)= sum dno*zhat,
  *     dbeta (+)= sum dno.  gamma, beta, save_mean, save_inv_std are required and
  *     dgamma, dbeta optional (NULL skips them); `accumulate` as for dw.
+ *   Batch norm, EVAL mode (constant statistics): dz = dno * gamma * inv_std, with
+ *     dgamma, dbeta as above.
  * dz may equal dy (in place).  [generic] backward_input / backward (training-mode
- * two-phase normalisation backward); [cuda] activation_backward, bn_training_backward. */
+ * two-phase normalisation backward, evaluation-mode branch); [cuda]
+ * activation_backward, bn_training_backward. */
 convmi_status activation_backward(const convmi_desc* desc, const void* z, const void* dy,
                                   const float* gamma, const float* beta,
                                   const float* save_mean, const float* save_inv_std,

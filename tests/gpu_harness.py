@@ -72,11 +72,11 @@ def desc_for(wl: WL.Workload):
                         cm.MODE_TRAIN, cdtype(wl.dtype), wl.momentum, wl.eps)
 
 
-def shape_desc(shape: WL.ConvShape, dt: str, act=0, norm=0, momentum=0.1, eps=1e-5):
+def shape_desc(shape: WL.ConvShape, dt: str, act=0, norm=0, momentum=0.1, eps=1e-5, evaluation=False):
     import convolution_layer_amd as cm
     s = shape
     return cm.make_desc(s.N, s.H, s.W, s.IC, s.OC, s.KH, s.KW, (s.sh, s.sw), (s.ph, s.pw), act, norm,
-                        cm.MODE_TRAIN, cdtype(dt), momentum, eps)
+                        cm.MODE_EVAL if evaluation else cm.MODE_TRAIN, cdtype(dt), momentum, eps)
 
 
 def sample_indices(shape4, count: int, seed: int) -> np.ndarray:

@@ -76,7 +76,7 @@ def _good(cm, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(N=0), 1), (dict(IC=-1), 1), (dict(KH=0), 1), (dict(stride=(0, 1)), 1), (dict(pad=(-1, 0)), 1),
     (dict(KH=11, pad=(0, 0)), 1), (dict(dtype=7), 1), (dict(activation=9), 1), (dict(normalization=3), 1),
-    (dict(mode=1), 2), (dict(mode=5), 1), (dict(normalization=1, eps=0.0), 1),
+    (dict(mode=5), 1), (dict(normalization=1, eps=0.0), 1),
     (dict(normalization=1, momentum=1.5), 1), (dict(N=1 << 40), 2),
 ])
 def test_bad_descriptor(cm, kw, status):
@@ -85,6 +85,23 @@ def test_bad_descriptor(cm, kw, status):
     st = cm.lib.convmi_output_dims(C.byref(d), C.byref(oh), C.byref(ow))
     assert st == status, cm.lib.convmi_last_error()
     assert cm.lib.convmi_last_error().decode()
+
+
+def test_evaluation_mode_checks(cm):
+    """Evaluation mode is a valid descriptor; with batch norm the forward needs the
+    running statistics, and the training-statistics call refuses it."""
+    d = _good(cm, mode=1, normalization=1)
+    oh, ow = C.c_int64(), C.c_int64()
+    assert cm.lib.convmi_output_dims(C.byref(d), C.byref(oh), C.byref(ow)) == cm.OK
+    f = cm.lib.conv2d_forward
+    vec = [A + 0x300000 + 0x1000 * i for i in range(6)]  # gamma, beta, rm, rv, save_mean, save_inv_std
+    args = [C.byref(d), A, A + 0x100000, None, vec[0], vec[1], None, None, vec[4], vec[5], A + 0x400000,
+            A + 0x200000, None, 0, None]
+    assert f(*args) == cm.ERR_INVALID_ARG  # running statistics missing
+    assert "running" in cm.lib.convmi_last_error().decode()
+    st = cm.lib.bn_stats_training(C.byref(d), A, vec[4], vec[5], None, None, None, 0, None)
+    assert st == cm.ERR_INVALID_ARG
+    assert "evaluation" in cm.lib.convmi_last_error().decode()
 
 
 def test_null_desc(cm):

@@ -173,6 +173,65 @@ def test_medium_batchnorm_layer(case):
     G.assert_close(G.host(dbt), db_r, dt, "dbeta")
 
 
+@pytest.mark.parametrize("case", BN_MEDIUM, ids=_mid_id)
+def test_medium_batchnorm_evaluation(case):
+    """Evaluation mode: the forward normalises with the running statistics (left
+    unchanged; save_mean/save_inv_std receive them) and the backward treats them as
+    constants (dz = dno*gamma*inv_std, dgamma, dbeta), against the oracle."""
+    shape, dt, act, x, w, b, dy = _problem(case, 60)
+    r = np.random.default_rng(61)
+    gamma = WL.round_to(WL.F32, r.uniform(0.5, 1.5, shape.OC))
+    beta = WL.round_to(WL.F32, r.normal(0.0, 0.1, shape.OC))
+    rm0 = WL.round_to(WL.F32, r.normal(0.0, 0.5, shape.OC))
+    rv0 = WL.round_to(WL.F32, r.uniform(0.2, 3.0, shape.OC))
+    eps = 1e-5
+    desc = G.shape_desc(shape, dt, act, WL.NORM_BATCH, 0.1, eps, evaluation=True)
+    rm_d, rv_d = G.dev(rm0), G.dev(rv0)
+    out = G.run_forward(desc, dt, G.dev(x, dt), G.dev(w, dt), G.dev(b), G.dev(gamma), G.dev(beta), rm_d, rv_d)
+    z_r = O.conv2d_forward(x, w, b, (shape.sh, shape.sw), (shape.ph, shape.pw))
+    G.assert_close(G.host(out["z"]), z_r, dt, "z")
+    mean_r, inv_r = O.bn_eval_stats(rm0, rv0, eps)
+    G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, rv0, inv_r, eps, "eval fwd")
+    np.testing.assert_array_equal(G.host(rm_d), rm0)  # running statistics untouched
+    np.testing.assert_array_equal(G.host(rv_d), rv0)
+    zs = WL.round_to(dt, z_r)
+    m32, i32 = WL.round_to(WL.F32, mean_r), WL.round_to(WL.F32, inv_r)
+    y_r = O.apply_activation(zs, act, WL.NORM_BATCH, gamma, beta, m32, i32)
+    G.assert_close(G.host(out["y"]), y_r, dt, "y")
+    dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(zs, dt), G.dev(dy, dt), G.dev(gamma), G.dev(beta), G.dev(m32),
+                                G.dev(i32))
+    dz_r, dg_r, db_r = O.activation_backward(zs, dy, act, WL.NORM_BATCH, gamma, beta, m32, i32, evaluation=True)
+    G.assert_close(G.host(dz), dz_r, dt, "dz")
+    G.assert_close(G.host(dg), dg_r, dt, "dgamma")
+    G.assert_close(G.host(dbt), db_r, dt, "dbeta")
+
+
+def test_full_batchnorm_evaluation_c3():
+    """c3 at full size in evaluation mode (running statistics drawn per channel): y and
+    the backward dz, dgamma, dbeta against the oracle on the same z."""
+    wl = WL.WORKLOADS["c3"]
+    s, dt = wl.shape, wl.dtype
+    d = _inputs("c3")
+    r = np.random.default_rng(62)
+    rm0 = WL.round_to(WL.F32, r.normal(0.0, 0.5, s.OC))
+    rv0 = WL.round_to(WL.F32, r.uniform(0.2, 3.0, s.OC))
+    desc = G.shape_desc(s, dt, wl.act, WL.NORM_BATCH, wl.momentum, wl.eps, evaluation=True)
+    out = G.run_forward(desc, dt, G.dev(d["x"], dt), G.dev(d["w"], dt), G.dev(d["b"]), G.dev(d["gamma"]),
+                        G.dev(d["beta"]), G.dev(rm0), G.dev(rv0))
+    zg = G.host(out["z"])  # the oracle takes the library's stored z (identical inputs)
+    mean_r, inv_r = O.bn_eval_stats(rm0, rv0, wl.eps)
+    m32, i32 = WL.round_to(WL.F32, mean_r), WL.round_to(WL.F32, inv_r)
+    y_r = O.apply_activation(zg, wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32)
+    G.assert_close(G.host(out["y"]), y_r, dt, "y")
+    dz, dg, dbt = G.run_act_bwd(desc, dt, out["z"], G.dev(d["dy"], dt), G.dev(d["gamma"]), G.dev(d["beta"]),
+                                G.dev(m32), G.dev(i32))
+    dz_r, dg_r, db_r = O.activation_backward(zg, d["dy"], wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32,
+                                             evaluation=True)
+    G.assert_close(G.host(dz), dz_r, dt, "dz")
+    G.assert_close(G.host(dg), dg_r, dt, "dgamma")
+    G.assert_close(G.host(dbt), db_r, dt, "dbeta")
+
+
 # ------------------------------------------------------------------ full-size workloads
 _CACHE = {}
 
