@@ -69,11 +69,12 @@ __device__ __forceinline__ void merge_rows(float* red, int rpi, int width, int r
 
 // Per-slab sums of two quantities per channel over a slab of rows, merged across the
 // workgroup's row groups in a fixed order and written to part[c][q][slab] (q = 0, 1).
-// Each lane streams UNROLL 16-byte vectors per iteration.
+// Each lane streams UNROLL 16-byte vectors per iteration.  An accumulator with kOut
+// also produces one output element per input element (written to `out`, same layout).
 template <typename T, int VEC, class Acc>
 __device__ __forceinline__ void slab_partials(const T* __restrict__ a, const T* __restrict__ b, int64_t M, int C,
                                               int tpr, int rpi, int64_t rows_per_block, Acc accf,
-                                              float* __restrict__ part, float* red) {
+                                              float* __restrict__ part, float* red, T* out = nullptr) {
     constexpr int UNROLL = 4;
     const int t = threadIdx.x, cv = t % tpr, r = t / tpr;
     const int c0 = (blockIdx.y * tpr + cv) * VEC;
@@ -94,13 +95,27 @@ __device__ __forceinline__ void slab_partials(const T* __restrict__ a, const T* 
                 if (b) Vec<T, VEC>::load(b + (m + u * rpi) * C + c0, vb[u]);
             }
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) accf.add(va[u], vb[u], s1, s2);
+            for (int u = 0; u < UNROLL; ++u) {
+                if constexpr (Acc::kOut) {
+                    float o[VEC];
+                    accf.add_out(va[u], vb[u], s1, s2, o);
+                    Vec<T, VEC>::store(out + (m + u * rpi) * C + c0, o);
+                } else {
+                    accf.add(va[u], vb[u], s1, s2);
+                }
+            }
         }
         for (; m < m1; m += rpi) {
             float va[VEC], vb[VEC];
             Vec<T, VEC>::load(a + m * C + c0, va);
             if (b) Vec<T, VEC>::load(b + m * C + c0, vb);
-            accf.add(va, vb, s1, s2);
+            if constexpr (Acc::kOut) {
+                float o[VEC];
+                accf.add_out(va, vb, s1, s2, o);
+                Vec<T, VEC>::store(out + m * C + c0, o);
+            } else {
+                accf.add(va, vb, s1, s2);
+            }
         }
     }
     const int width = tpr * VEC * 2, slot = cv * VEC * 2;
@@ -122,6 +137,7 @@ __device__ __forceinline__ void slab_partials(const T* __restrict__ a, const T* 
 // Shifted sums for the statistics: shift_c = z[0][c] keeps E[(z-s)^2] - E[z-s]^2 free of
 // cancellation when |mean| >> std.
 template <typename T, int VEC> struct StatsAcc {
+    static constexpr bool kOut = false;
     const T* z;
     float sh[VEC];
     __device__ __forceinline__ void init(int c0) { Vec<T, VEC>::load(z + c0, sh); }
@@ -137,6 +153,7 @@ template <typename T, int VEC> struct StatsAcc {
 
 // Sums of dno and dno*zhat for the batch-norm backward.
 template <typename T, int VEC, int ACT> struct BwdAcc {
+    static constexpr bool kOut = false;
     const float *gamma, *beta, *mean, *inv_std;
     float g[VEC], bt[VEC], mu[VEC], is[VEC];
     __device__ __forceinline__ void init(int c0) {
@@ -153,6 +170,32 @@ template <typename T, int VEC, int ACT> struct BwdAcc {
             const float dno = act_slope<ACT>(a) * gv[j];
             s1[j] += dno;
             s2[j] = __builtin_fmaf(dno, zh, s2[j]);
+        }
+    }
+};
+
+// Evaluation mode: the same sums, and dz = dno * gamma * inv_std in the same pass (the
+// statistics are constants, so dz needs no reduction).
+template <typename T, int VEC, int ACT> struct EvalBwdAcc {
+    static constexpr bool kOut = true;
+    const float *gamma, *beta, *mean, *inv_std;
+    float g[VEC], bt[VEC], mu[VEC], is[VEC];
+    __device__ __forceinline__ void init(int c0) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j]; mu[j] = mean[c0 + j]; is[j] = inv_std[c0 + j];
+        }
+    }
+    __device__ __forceinline__ void add_out(const float* zv, const float* gv, float* s1, float* s2,
+                                            float* o) const {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            float zh;
+            const float a = bn_affine(zv[j], mu[j], is[j], g[j], bt[j], &zh);
+            const float dno = act_slope<ACT>(a) * gv[j];
+            s1[j] += dno;
+            s2[j] = __builtin_fmaf(dno, zh, s2[j]);
+            o[j] = dno * (g[j] * is[j]);
         }
     }
 };
@@ -242,6 +285,21 @@ __global__ __launch_bounds__(kThreads) void bn_bwd_partials(const T* __restrict_
     extern __shared__ float red[];
     BwdAcc<T, VEC, ACT> acc{gamma, beta, mean, inv_std, {}, {}, {}, {}};
     slab_partials<T, VEC>(z, dy, M, C, tpr, rpi, rows_per_block, acc, part, red);
+}
+
+// Evaluation-mode batch-norm backward, first launch: dz and the slab partials of
+// A = sum dno and B = sum dno*zhat in one pass over z and dy.
+template <typename T, int VEC, int ACT>
+__global__ __launch_bounds__(kThreads) void bn_bwd_eval(const T* __restrict__ z, const T* dy, T* dz, int64_t M, int C,
+                                                        int tpr, int rpi, int64_t rows_per_block,
+                                                        const float* __restrict__ gamma,
+                                                        const float* __restrict__ beta,
+                                                        const float* __restrict__ mean,
+                                                        const float* __restrict__ inv_std,
+                                                        float* __restrict__ part) {
+    extern __shared__ float red[];
+    EvalBwdAcc<T, VEC, ACT> acc{gamma, beta, mean, inv_std, {}, {}, {}, {}};
+    slab_partials<T, VEC>(z, dy, M, C, tpr, rpi, rows_per_block, acc, part, red, dz);
 }
 
 // Second launch: dgamma (+)= B, dbeta (+)= A and the coefficients of
@@ -479,6 +537,17 @@ hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_
     float* coef = (float*)((char*)ws + partial_bytes(p, C));
     dim3 grid(p.blocks, p.chunks), block(kThreads);
     size_t lds = (size_t)p.rpi * p.tpr * p.vec * 2 * sizeof(float);
+    if (evaluation) {  // one pass for dz and the partials, then dgamma / dbeta
+        CONVMI_VEC_SWITCH(dt, p.vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (bn_bwd_eval<T, VEC, A><<<grid, block, lds, s>>>(
+                                                                          (const T*)z, (const T*)dy, (T*)dz, M, C,
+                                                                          p.tpr, p.rpi, p.rows_per_block, gamma, beta,
+                                                                          mean, inv_std, part))));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        bn_bwd_finalize<<<merge_grid(C), block, 0, s>>>(part, p.blocks, C, M, gamma, inv_std, dgamma, dbeta,
+                                                        accumulate, 1, coef);
+        return hipGetLastError();
+    }
     CONVMI_VEC_SWITCH(dt, p.vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (bn_bwd_partials<T, VEC, A><<<grid, block, lds, s>>>(
                                                                       (const T*)z, (const T*)dy, M, C, p.tpr, p.rpi,
                                                                       p.rows_per_block, gamma, beta, mean, inv_std,
