@@ -203,7 +203,17 @@ CONVMI_API convmi_status conv2d_forward(const convmi_desc* desc, const void* x, 
     hipStream_t s = (hipStream_t)stream;
     const int act = desc->activation;
     hipError_t e;
-    // Without batch norm the activation is fused into the convolution's epilogue.
+    // Without batch norm the activation is fused into the convolution's epilogue; so is
+    // evaluation-mode batch norm on the input-tile-reuse path (its statistics are known
+    // before the convolution runs).
+    if (bn && desc->mode == CONVMI_MODE_EVAL && halo_fwd_supported(desc->dtype, d)) {
+        e = launch_bn_eval_stats(running_mean, running_var, d.OC, desc->eps, save_mean, save_inv_std, s);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: batch-norm statistics launch");
+        const float* bn_eval[4] = {save_mean, save_inv_std, gamma, beta};
+        e = launch_halo_fwd(desc->dtype, x, w, bias, z, y, d, act, workspace, s, bn_eval);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: convolution launch");
+        return CONVMI_OK;
+    }
     void* conv_y = bn ? nullptr : y;
     if (igemm_fwd_supported(desc->dtype, d))
         e = launch_igemm_fwd(desc->dtype, x, w, bias, z, conv_y, d, act, workspace, s);

@@ -85,8 +85,11 @@ bool halo_fwd_supported(int dt, const ConvDims& d);
 bool halo_dx_supported(int dt, const ConvDims& d);
 size_t halo_fwd_ws_bytes(int dt, const ConvDims& d);
 size_t halo_dx_ws_bytes(int dt, const ConvDims& d);
+// bn_eval: null, or {mean, inv_std, gamma, beta} of evaluation-mode batch norm, applied
+// before the activation in the epilogue (y = act(gamma*(z - mean)*inv_std + beta)).
 hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
-                           const ConvDims& d, int act, void* ws, hipStream_t s);
+                           const ConvDims& d, int act, void* ws, hipStream_t s,
+                           const float* const* bn_eval = nullptr);
 hipError_t launch_halo_dx(int dt, const void* dz, const void* w, void* dx, const ConvDims& d, void* ws,
                           hipStream_t s);
 

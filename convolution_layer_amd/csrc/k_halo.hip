@@ -98,14 +98,17 @@ template <> __device__ __forceinline__ void put16<bf16>(bf16* p, const float* v)
 }
 
 // z = stored(acc + bias), y = act(z).  `raw` holds 16 bytes of stored z of one pixel.
+// `prep` loads a thread's per-column parameters once (none here).
 struct HFwdOut {
     void* z;            // nullable
     void* y;            // nullable
     const float* bias;  // nullable
     int OC;
+    struct Cache {};
     __device__ __forceinline__ float colbias(int col) const { return (bias && col < OC) ? bias[col] : 0.0f; }
+    __device__ __forceinline__ Cache prep(int, int) const { return Cache{}; }
     template <typename T, int ACT>
-    __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv) const {
+    __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv, const Cache&) const {
         constexpr int VEC = 16 / (int)sizeof(T);
         T v[VEC];
         __builtin_memcpy(v, &raw, 16);
@@ -127,12 +130,64 @@ struct HFwdOut {
     }
 };
 
+// Evaluation-mode batch norm in the epilogue (its statistics are known before the
+// convolution): z = stored(acc + bias), y = act(gamma*(z - mean)*inv_std + beta), with
+// the same fp32 operation order as the separate normalise/activate pass.
+struct HFwdBnOut {
+    void* z;            // nullable
+    void* y;
+    const float* bias;  // nullable
+    int OC;
+    const float *mean, *inv_std, *gamma, *beta;
+    struct Cache {
+        float m[8], i[8], g[8], b[8];
+    };
+    __device__ __forceinline__ float colbias(int col) const { return (bias && col < OC) ? bias[col] : 0.0f; }
+    __device__ __forceinline__ Cache prep(int col, int nv) const {
+        Cache c;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cc = col + (j < nv ? j : 0);
+            c.m[j] = mean[cc];
+            c.i[j] = inv_std[cc];
+            c.g[j] = gamma[cc];
+            c.b[j] = beta[cc];
+        }
+        return c;
+    }
+    template <int ACT> __device__ __forceinline__ float yval(float zv, const Cache& c, int j) const {
+        float zh;
+        return act_fwd<ACT>(bn_affine(zv, c.m[j], c.i[j], c.g[j], c.b[j], &zh));
+    }
+    template <typename T, int ACT>
+    __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv, const Cache& c) const {
+        constexpr int VEC = 16 / (int)sizeof(T);
+        T v[VEC];
+        __builtin_memcpy(v, &raw, 16);
+        const int64_t off = pix * OC + col;
+        if (nv == VEC && OC % VEC == 0) {
+            if (z) *(uint4*)((T*)z + off) = raw;
+            float yr[VEC];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) yr[j] = yval<ACT>(to_f32(v[j]), c, j);
+            put16<T>((T*)y + off, yr);
+        } else {
+            for (int j = 0; j < nv; ++j) {
+                if (z) ((T*)z)[off + j] = v[j];
+                ((T*)y)[off + j] = from_f32<T>(yval<ACT>(to_f32(v[j]), c, j));
+            }
+        }
+    }
+};
+
 struct HDxOut {
     void* dx;
     int IC;
+    struct Cache {};
     __device__ __forceinline__ float colbias(int) const { return 0.0f; }
+    __device__ __forceinline__ Cache prep(int, int) const { return Cache{}; }
     template <typename T, int ACT>
-    __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv) const {
+    __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv, const Cache&) const {
         constexpr int VEC = 16 / (int)sizeof(T);
         const int64_t off = pix * IC + col;
         if (nv == VEC && IC % VEC == 0) {
@@ -373,13 +428,14 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     if (col >= g.Nn) return;
     const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
     const int RQ = g.R * g.Q;
+    const typename Out::Cache cache = out.prep(col, nv);
     for (int m = t / OVR; m < RQ; m += NTH / OVR) {
         const int rr = fdiv(m, g.fQ);
         const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
         if (oh >= g.Hout || ow >= g.Wout) continue;
         const int64_t pix = ((int64_t)n * g.Hout + oh) * g.Wout + ow;
         const uint4 raw = *(const uint4*)(Cs + m * LDC + cv * VEC);
-        out.template put<T, ACT>(pix, col, raw, nv);
+        out.template put<T, ACT>(pix, col, raw, nv, cache);
     }
 }
 
@@ -556,13 +612,14 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     if (col >= g.Nn) return;
     const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
     const int RQ = g.R * g.Q;
+    const typename Out::Cache cache = out.prep(col, nv);
     for (int m = t / OVR; m < RQ; m += NTH / OVR) {
         const int rr = fdiv(m, g.fQ);
         const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
         if (oh >= g.Hout || ow >= g.Wout) continue;
         const int64_t pix = ((int64_t)n * g.Hout + oh) * g.Wout + ow;
         const uint4 raw = *(const uint4*)(Cs + m * LDC + cv * VEC);
-        out.template put<bf16, ACT>(pix, col, raw, nv);
+        out.template put<bf16, ACT>(pix, col, raw, nv, cache);
     }
 }
 
@@ -814,18 +871,27 @@ size_t halo_dx_ws_bytes(int dt, const ConvDims& d) {
 }
 
 hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
-                           const ConvDims& d, int act, void* ws, hipStream_t s) {
+                           const ConvDims& d, int act, void* ws, hipStream_t s, const float* const* bn_eval) {
     const Sides sd = fwd_sides(d);
     HaloPlan p;
     if (d.sh != 1 || d.sw != 1 || !pick_halo(dt, d, sd, &p)) return hipErrorInvalidValue;
     const HaloGeom g = make_geom(d, sd, p, dt, true);
     const HFwdOut o{z, y, bias, d.OC};
+    const HFwdBnOut ob{z, y, bias, d.OC, bn_eval ? bn_eval[0] : nullptr, bn_eval ? bn_eval[1] : nullptr,
+                       bn_eval ? bn_eval[2] : nullptr, bn_eval ? bn_eval[3] : nullptr};
+    if (bn_eval && (!y || !bn_eval[0] || !bn_eval[1] || !bn_eval[2] || !bn_eval[3])) return hipErrorInvalidValue;
     if (dt == DT_BF16) {
         const hipError_t e = launch_frag_weights((const bf16*)w, (uint4*)ws, d, sd, p, true, s);
         if (e != hipSuccess) return e;
+        if (bn_eval)
+            CONVMI_ACT_SWITCH(act, A_, return (dispatch_bf16<A_, HFwdBnOut>((const bf16*)x, g, (const uint4*)ws, ob,
+                                                                            p, d.N, s)));
         CONVMI_ACT_SWITCH(act, A_, return (dispatch_bf16<A_, HFwdOut>((const bf16*)x, g, (const uint4*)ws, o, p,
                                                                       d.N, s)));
     } else {
+        if (bn_eval)
+            CONVMI_ACT_SWITCH(act, A_, return (dispatch_f32<A_, HFwdBnOut>((const float*)x, g, (const float*)w, ob,
+                                                                           p, d.N, s)));
         CONVMI_ACT_SWITCH(act, A_, return (dispatch_f32<A_, HFwdOut>((const float*)x, g, (const float*)w, o, p,
                                                                      d.N, s)));
     }
