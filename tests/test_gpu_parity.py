@@ -207,8 +207,8 @@ def test_medium_batchnorm_evaluation(case):
 
 
 def test_full_batchnorm_evaluation_c3():
-    """c3 at full size in evaluation mode (running statistics drawn per channel): y and
-    the backward dz, dgamma, dbeta against the oracle on the same z."""
+    """c3 at full size in evaluation mode (running statistics drawn per channel): z, y
+    and the backward dz, dgamma, dbeta against the oracle."""
     wl = WL.WORKLOADS["c3"]
     s, dt = wl.shape, wl.dtype
     d = _inputs("c3")
@@ -218,14 +218,17 @@ def test_full_batchnorm_evaluation_c3():
     desc = G.shape_desc(s, dt, wl.act, WL.NORM_BATCH, wl.momentum, wl.eps, evaluation=True)
     out = G.run_forward(desc, dt, G.dev(d["x"], dt), G.dev(d["w"], dt), G.dev(d["b"]), G.dev(d["gamma"]),
                         G.dev(d["beta"]), G.dev(rm0), G.dev(rv0))
-    zg = G.host(out["z"])  # the oracle takes the library's stored z (identical inputs)
+    z_r = O.conv2d_forward(d["x"], d["w"], d["b"], (s.sh, s.sw), (s.ph, s.pw))
+    G.assert_close(G.host(out["z"]), z_r, dt, "z")
+    zs = WL.round_to(dt, z_r)
     mean_r, inv_r = O.bn_eval_stats(rm0, rv0, wl.eps)
     m32, i32 = WL.round_to(WL.F32, mean_r), WL.round_to(WL.F32, inv_r)
-    y_r = O.apply_activation(zg, wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32)
+    y_r = O.apply_activation(zs, wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32)
     G.assert_close(G.host(out["y"]), y_r, dt, "y")
-    dz, dg, dbt = G.run_act_bwd(desc, dt, out["z"], G.dev(d["dy"], dt), G.dev(d["gamma"]), G.dev(d["beta"]),
+    # backward on the oracle's z (rounded to the storage type), not the library's
+    dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(zs, dt), G.dev(d["dy"], dt), G.dev(d["gamma"]), G.dev(d["beta"]),
                                 G.dev(m32), G.dev(i32))
-    dz_r, dg_r, db_r = O.activation_backward(zg, d["dy"], wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32,
+    dz_r, dg_r, db_r = O.activation_backward(zs, d["dy"], wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32,
                                              evaluation=True)
     G.assert_close(G.host(dz), dz_r, dt, "dz")
     G.assert_close(G.host(dg), dg_r, dt, "dgamma")
@@ -366,6 +369,51 @@ def test_full_backward_weight(name):
         dw_r, db_r = O.conv2d_backward_weight(d["x"], dz, s.w_shape, st, pd)
         G.assert_close(G.host(dw), dw_r, dt, f"{name} dw")
         G.assert_close(G.host(db), db_r, dt, f"{name} db")
+
+
+def test_rl_stack_chained():
+    """The RL-encoder stack end to end on the first 8 images: the forward chain feeds
+    each layer the previous layer's output, and the backward chain feeds each layer's
+    activation backward the next layer's dX, from the top gradient dY of c2c down to dX
+    of c2a, with dW and db of every layer.  Library chain and oracle chain run
+    independently from the same seeded inputs.  Precondition (oracle values only): no
+    pre-activation lies within 1e-6 of max|z| of zero, so fp32 rounding cannot flip a
+    ReLU mask between the two chains."""
+    N0 = 8
+    names = list(WL.RL_STACK)
+    ds = {nm: _inputs(nm) for nm in names}
+    x_r = ds[names[0]]["x"][:N0]
+    x_g = G.dev(x_r, WL.F32)
+    layers = []
+    for nm in names:
+        wl = WL.WORKLOADS[nm]
+        s, d = wl.shape.with_batch(N0), ds[nm]
+        st, pd = (s.sh, s.sw), (s.ph, s.pw)
+        desc = G.shape_desc(s, WL.F32, wl.act)
+        w_g, b_g = G.dev(d["w"], WL.F32), G.dev(d.get("b"))
+        out = G.run_forward(desc, WL.F32, x_g, w_g, b_g)
+        z_r = O.conv2d_forward(x_r, d["w"], d.get("b"), st, pd)
+        assert np.abs(z_r).min() >= 1e-6 * np.abs(z_r).max(), f"{nm}: a pre-activation sits at the ReLU kink"
+        y_r = WL.round_to(WL.F32, O.apply_activation(z_r, wl.act))
+        G.assert_close(G.host(out["z"]), z_r, WL.F32, f"chain {nm} z")
+        G.assert_close(G.host(out["y"]), y_r, WL.F32, f"chain {nm} y")
+        layers.append((nm, wl, s, desc, x_g, x_r, w_g, d["w"], out["z"], WL.round_to(WL.F32, z_r)))
+        x_g, x_r = out["y"], y_r
+    g_r = ds[names[-1]]["dy"][:N0]
+    g_g = G.dev(g_r, WL.F32)
+    for nm, wl, s, desc, xl_g, xl_r, w_g, w_r, z_g, z_r in reversed(layers):
+        st, pd = (s.sh, s.sw), (s.ph, s.pw)
+        dz_g, _, _ = G.run_act_bwd(desc, WL.F32, z_g, g_g)
+        dz_r, _, _ = O.activation_backward(z_r, g_r, wl.act)
+        G.assert_close(G.host(dz_g), dz_r, WL.F32, f"chain {nm} dz")
+        dw_g, db_g = G.run_backward_weight(desc, xl_g, dz_g)
+        dw_r, db_r = O.conv2d_backward_weight(xl_r, dz_r, s.w_shape, st, pd)
+        G.assert_close(G.host(dw_g), dw_r, WL.F32, f"chain {nm} dw")
+        G.assert_close(G.host(db_g), db_r, WL.F32, f"chain {nm} db")
+        dx_g = G.run_backward_data(desc, WL.F32, dz_g, w_g)
+        dx_r = O.conv2d_backward_data(dz_r, w_r, s.x_shape, st, pd)
+        G.assert_close(G.host(dx_g), dx_r, WL.F32, f"chain {nm} dx")
+        g_g, g_r = dx_g, WL.round_to(WL.F32, dx_r)
 
 
 def test_full_bn_stats_c3():
