@@ -140,6 +140,35 @@ def timed_steps(layer, steps, warmup, only=None):
     return total, ms
 
 
+def graph_steps(layer, steps, warmup):
+    """Seconds for `steps` training steps launched as one captured HIP graph of the step's
+    calls (the same kernels in the same order; the graph removes the host's per-launch
+    gaps between them).  The replayed step must reproduce the eager step bit for bit."""
+    import torch
+    calls = [f for _, f in layer.calls()]
+    for _ in range(warmup):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    eager = (layer.dx.clone(), layer.dw.clone(), layer.y.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in calls:
+            f()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(eager[0], layer.dx) and torch.equal(eager[1], layer.dw) and torch.equal(eager[2], layer.y)):
+        raise RuntimeError("graph replay of the training step differs from the eager step")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    del g
+    return total
+
+
 def time_call(f, reps):
     import torch
     f()
@@ -442,14 +471,15 @@ def main():
     log(f"bench: workload {wl.name} ({wl.note}); building inputs")
     layer = Layer(wl)
     log("bench: timing steps")
-    total, ms = timed_steps(layer, args.steps, args.warmup, args.only)
-    step_ms = total / args.steps * 1e3
-    flops = 3 * s.flops()
-    value = flops / (total / args.steps) / 1e12
-    log(f"bench: step {step_ms:.3f} ms; per call ms {ms}")
+    eager_total, ms = timed_steps(layer, args.steps, args.warmup, args.only)
     if args.only:
         print(json.dumps({"only": args.only, "ms": ms}), flush=True)
         return
+    total = graph_steps(layer, args.steps, args.warmup)
+    step_ms = total / args.steps * 1e3
+    flops = 3 * s.flops()
+    value = flops / (total / args.steps) / 1e12
+    log(f"bench: step {step_ms:.3f} ms (graph), {eager_total / args.steps * 1e3:.3f} ms (eager); per call ms {ms}")
 
     # dominant call: the convolution call with the longest mean duration
     conv_calls = {k: v for k, v in ms.items() if k in CONV_CALLS}
@@ -507,6 +537,8 @@ def main():
             "config": {"workload": f"{wl.name}: {wl.note}", "N": s.N, "H": s.H, "W": s.W, "IC": s.IC,
                        "OC": s.OC, "kernel": f"{s.KH}x{s.KW}", "stride": s.sh, "pad": s.ph,
                        "step": "forward + activation_backward + backward_data + backward_weight",
+                       "launch": "the step's calls captured once in a HIP graph and replayed",
+                       "eager_ms_per_step": round(eager_total / args.steps * 1e3, 4),
                        "flops_per_step": flops},
             "mfma_peak_frac": round(value / peak, 4),
             "roofline": roofline, "bn_stats": bn, "cpu_baseline": cpu}
