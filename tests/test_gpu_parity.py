@@ -416,6 +416,57 @@ def test_rl_stack_chained():
         g_g, g_r = dx_g, WL.round_to(WL.F32, dx_r)
 
 
+def _window(t, n, r, c, R, Q, ph, pw):
+    """Host fp64 copy of rows r-ph .. r-ph+R-1, columns c-pw .. c-pw+Q-1 of image n of a
+    device NHWC tensor, zero outside the image (the convolution's padding)."""
+    N_, H_, W_, C_ = t.shape
+    out = np.zeros((1, R, Q, C_))
+    r0, c0 = r - ph, c - pw
+    rs, re = max(r0, 0), min(r0 + R, H_)
+    cs, ce = max(c0, 0), min(c0 + Q, W_)
+    if rs < re and cs < ce:
+        out[0, rs - r0:re - r0, cs - c0:ce - c0] = t[n, rs:re, cs:ce].float().cpu().numpy()
+    return out
+
+
+def test_largest_tensors():
+    """Tensors past 2**31 elements (4.4 GB each in bf16): forward, activation backward
+    and dX on the GPU, checked at sampled outputs (every corner of every axis included,
+    so the highest offsets are hit) against the oracle on host windows of the same
+    seeded inputs, which are drawn on the GPU (they are too large to draw on the host)."""
+    shape = WL.ConvShape(65, 512, 512, 128, 128, 3, 3, 1, 1, 1, 1)
+    dt, act = WL.BF16, WL.ACT_TANH
+    assert shape.N * shape.H * shape.W * shape.IC > 2 ** 31
+    x = WL.device_normal(shape.x_shape, dt, 71)
+    w = WL.device_normal(shape.w_shape, dt, 72, (2.0 / shape.Kdim) ** 0.5)
+    b = WL.device_normal((shape.OC,), WL.F32, 73, 0.1)
+    desc = G.shape_desc(shape, dt, act)
+    w_h, b_h = G.host(w), G.host(b)
+    idx = G.sample_indices(shape.y_shape, 192, 74)
+    out = G.run_forward(desc, dt, x, w, b)
+    z_g, y_g = out["z"], out["y"]
+    z_r = np.array([O.conv2d_forward_at(_window(x, n, oh, ow, 3, 3, 1, 1), w_h, b_h, [(0, 1, 1, oc)], (1, 1),
+                                        (1, 1))[0] for n, oh, ow, oc in idx])
+    ti = tuple(torch.as_tensor(idx.T))
+    G.assert_close(z_g[ti].float().cpu().numpy(), z_r, dt, "z (sampled)")
+    y_r = O.apply_activation(WL.round_to(dt, z_r).reshape(-1, 1), act).reshape(-1)
+    G.assert_close(y_g[ti].float().cpu().numpy(), y_r, dt, "y (sampled)")
+    del out, z_g, y_g
+    # activation backward and dX on generated z and dz (not on the library's outputs)
+    z = WL.device_normal(shape.y_shape, dt, 75, 1.5)
+    dy = WL.device_normal(shape.y_shape, dt, 76)
+    dz, _, _ = G.run_act_bwd(desc, dt, z, dy)
+    dz_r, _, _ = O.activation_backward(z[ti].double().cpu().numpy(), dy[ti].double().cpu().numpy(), act)
+    G.assert_close(dz[ti].float().cpu().numpy(), dz_r, dt, "dz (sampled)")
+    del z, dy
+    dx = G.run_backward_data(desc, dt, dz, w)
+    xi = G.sample_indices(shape.x_shape, 192, 77)
+    # dx(n, ih, iw, :) needs dz at rows ih - 1 .. ih + 1 (stride 1, pad 1, 3x3): a 3x3 window
+    dx_r = np.array([O.conv2d_backward_data_at(_window(dz, n, ih, iw, 3, 3, 1, 1), w_h, (1, 3, 3, shape.IC),
+                                               [(0, 1, 1, ic)], (1, 1), (1, 1))[0] for n, ih, iw, ic in xi])
+    G.assert_close(dx[tuple(torch.as_tensor(xi.T))].float().cpu().numpy(), dx_r, dt, "dx (sampled)")
+
+
 def test_full_bn_stats_c3():
     """bn_stats_training alone on a synthetic pre-activation of the c3 shape."""
     wl = WL.WORKLOADS["c3"]

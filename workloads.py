@@ -230,3 +230,14 @@ def random_tensor(shape, dtype: str, seed: int, dist=("normal", 0.0, 1.0)) -> np
     """Generic seeded tensor for shape sweeps in the tests."""
     rng = np.random.default_rng(seed)
     return round_to(dtype, _draw(rng, dist, shape))
+
+
+def device_normal(shape, dtype: str, seed: int, std: float = 1.0):
+    """Seeded N(0, std) tensor drawn directly on the GPU (torch's CUDA Philox generator),
+    rounded to the data dtype: for shapes too large to draw on the host.  Tests hand the
+    oracle host copies of small windows of it."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std
+    return t.to(torch.bfloat16 if dtype == BF16 else torch.float32)
