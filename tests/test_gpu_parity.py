@@ -430,8 +430,8 @@ def _window(t, n, r, c, R, Q, ph, pw):
 
 
 def test_largest_tensors():
-    """Tensors past 2**31 elements (4.4 GB each in bf16): forward, activation backward
-    and dX on the GPU, checked at sampled outputs (every corner of every axis included,
+    """Tensors past 2**31 elements (4.4 GB each in bf16): forward, activation backward,
+    dX and dW on the GPU, checked at sampled outputs (every corner of every axis included,
     so the highest offsets are hit) against the oracle on host windows of the same
     seeded inputs, which are drawn on the GPU (they are too large to draw on the host)."""
     shape = WL.ConvShape(65, 512, 512, 128, 128, 3, 3, 1, 1, 1, 1)
@@ -465,6 +465,20 @@ def test_largest_tensors():
     dx_r = np.array([O.conv2d_backward_data_at(_window(dz, n, ih, iw, 3, 3, 1, 1), w_h, (1, 3, 3, shape.IC),
                                                [(0, 1, 1, ic)], (1, 1), (1, 1))[0] for n, ih, iw, ic in xi])
     G.assert_close(dx[tuple(torch.as_tensor(xi.T))].float().cpu().numpy(), dx_r, dt, "dx (sampled)")
+    del dx
+    # dW and db: one weight sums over all N*OH*OW = 17M output pixels; the oracle gets the
+    # single input channel and output channel the weight connects (a 1-channel problem)
+    dw, db = G.run_backward_weight(desc, x, dz)
+    wi = np.array([(0, 0, 0, 0), (127, 2, 2, 127), (5, 0, 2, 64), (77, 1, 1, 3), (127, 2, 0, 0), (0, 1, 2, 127)])
+    dw_r, db_r = [], []
+    for oc, kh, kw, ic in wi:
+        xc = x[..., ic:ic + 1].double().cpu().numpy()
+        dzc = dz[..., oc:oc + 1].double().cpu().numpy()
+        dw_r.append(O.conv2d_backward_weight_at(xc, dzc, (1, 3, 3, 1), [(0, kh, kw, 0)], (1, 1), (1, 1))[0])
+        db_r.append(O.bias_grad(dzc)[0])
+        del xc, dzc
+    G.assert_close(dw[tuple(torch.as_tensor(wi.T))].cpu().numpy(), np.array(dw_r), dt, "dw (sampled)")
+    G.assert_close(db[torch.as_tensor(wi[:, 0])].cpu().numpy(), np.array(db_r), dt, "db (sampled)")
 
 
 def test_full_bn_stats_c3():
