@@ -84,6 +84,7 @@ struct HaloGeom {
     int Kb;                // weight row length KH*KW*Cin
     int sign;              // +1 forward (tap at (kh, kw)), -1 input gradient (flipped)
     int hb;                // halo buffers (1 or 2)
+    int par_off;           // LDS byte offset of the per-column epilogue parameters
     int64_t img_stride;    // Hin*Win*Cin
     FastDiv fQ, fHQ, fTR, fTC;
 };
@@ -97,16 +98,28 @@ template <> __device__ __forceinline__ void put16<bf16>(bf16* p, const float* v)
                             pack_bf16x2(v[6], v[7]));
 }
 
+// Per-column epilogue parameters (bias, batch-norm statistics) are copied into LDS when a
+// workgroup starts, kPar arrays of BN floats (0 past the last column), so the epilogue
+// reads them at LDS latency instead of waiting on global loads after the main loop.
+// `colbias` takes a column of the tile; `prep` loads a thread's parameters for its 8
+// columns once.
+__device__ __forceinline__ void load_cols(float* dst, const float* src, int n0, int bn, int n, int t, int nth) {
+    for (int c = t; c < bn; c += nth) dst[c] = (src && n0 + c < n) ? src[n0 + c] : 0.0f;
+}
+
 // z = stored(acc + bias), y = act(z).  `raw` holds 16 bytes of stored z of one pixel.
-// `prep` loads a thread's per-column parameters once (none here).
 struct HFwdOut {
     void* z;            // nullable
     void* y;            // nullable
     const float* bias;  // nullable
     int OC;
+    static constexpr int kPar = 1;
     struct Cache {};
-    __device__ __forceinline__ float colbias(int col) const { return (bias && col < OC) ? bias[col] : 0.0f; }
-    __device__ __forceinline__ Cache prep(int, int) const { return Cache{}; }
+    __device__ __forceinline__ void load_par(float* par, int n0, int bn, int t, int nth) const {
+        load_cols(par, bias, n0, bn, OC, t, nth);
+    }
+    __device__ __forceinline__ float colbias(const float* par, int cl) const { return par[cl]; }
+    __device__ __forceinline__ Cache prep(const float*, int, int, int) const { return Cache{}; }
     template <typename T, int ACT>
     __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv, const Cache&) const {
         constexpr int VEC = 16 / (int)sizeof(T);
@@ -139,19 +152,28 @@ struct HFwdBnOut {
     const float* bias;  // nullable
     int OC;
     const float *mean, *inv_std, *gamma, *beta;
+    static constexpr int kPar = 5;  // bias, mean, inv_std, gamma, beta
     struct Cache {
         float m[8], i[8], g[8], b[8];
     };
-    __device__ __forceinline__ float colbias(int col) const { return (bias && col < OC) ? bias[col] : 0.0f; }
-    __device__ __forceinline__ Cache prep(int col, int nv) const {
+    __device__ __forceinline__ void load_par(float* par, int n0, int bn, int t, int nth) const {
+        load_cols(par, bias, n0, bn, OC, t, nth);
+        load_cols(par + bn, mean, n0, bn, OC, t, nth);
+        load_cols(par + 2 * bn, inv_std, n0, bn, OC, t, nth);
+        load_cols(par + 3 * bn, gamma, n0, bn, OC, t, nth);
+        load_cols(par + 4 * bn, beta, n0, bn, OC, t, nth);
+    }
+    __device__ __forceinline__ float colbias(const float* par, int cl) const { return par[cl]; }
+    // columns cl .. cl + nv - 1 lie inside the tile; the unused entries repeat column cl
+    __device__ __forceinline__ Cache prep(const float* par, int bn, int cl, int nv) const {
         Cache c;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int cc = col + (j < nv ? j : 0);
-            c.m[j] = mean[cc];
-            c.i[j] = inv_std[cc];
-            c.g[j] = gamma[cc];
-            c.b[j] = beta[cc];
+            const int cc = cl + (j < nv ? j : 0);
+            c.m[j] = par[bn + cc];
+            c.i[j] = par[2 * bn + cc];
+            c.g[j] = par[3 * bn + cc];
+            c.b[j] = par[4 * bn + cc];
         }
         return c;
     }
@@ -183,9 +205,11 @@ struct HFwdBnOut {
 struct HDxOut {
     void* dx;
     int IC;
+    static constexpr int kPar = 0;
     struct Cache {};
-    __device__ __forceinline__ float colbias(int) const { return 0.0f; }
-    __device__ __forceinline__ Cache prep(int, int) const { return Cache{}; }
+    __device__ __forceinline__ void load_par(float*, int, int, int, int) const {}
+    __device__ __forceinline__ float colbias(const float*, int) const { return 0.0f; }
+    __device__ __forceinline__ Cache prep(const float*, int, int, int) const { return Cache{}; }
     template <typename T, int ACT>
     __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv, const Cache&) const {
         constexpr int VEC = 16 / (int)sizeof(T);
@@ -238,6 +262,8 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
     const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
     const T* Aimg = A + (int64_t)n * g.img_stride;
+    float* par = (float*)(smem + g.par_off);
+    out.load_par(par, n0, BN, t, NTH);  // read after the prologue barrier
     const int nsteps = g.nchunks * g.KH * g.KW;
 
     // Copy group grp covers 8 LDS rows (halo positions or weight rows) 8*grp .. 8*grp+7;
@@ -414,7 +440,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int cl = wn * TN * MF + j * MF + lr;
-        const float bj = out.colbias(n0 + cl);
+        const float bj = out.colbias(par, cl);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -428,7 +454,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     if (col >= g.Nn) return;
     const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
     const int RQ = g.R * g.Q;
-    const typename Out::Cache cache = out.prep(col, nv);
+    const typename Out::Cache cache = out.prep(par, BN, cv * VEC, nv);
     for (int m = t / OVR; m < RQ; m += NTH / OVR) {
         const int rr = fdiv(m, g.fQ);
         const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
@@ -476,6 +502,8 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
     const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
     const bf16* Aimg = A + (int64_t)n * g.img_stride;
+    float* par = (float*)(smem + g.par_off);
+    out.load_par(par, n0, BN, t, NTH);  // read after the prologue barrier
     const int taps = g.KH * g.KW;
     const int nsteps = g.nchunks * taps;
 
@@ -536,7 +564,10 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 
     auto step = [&](int st, const uint4 (&cur)[TN][KST], uint4 (&nxt)[TN][KST]) {
         const int c = st / taps, tap = st - c * taps;
-        if (st + 1 < nsteps) load_b(st + 1, nxt);
+        // Always issued (the last step reloads its own fragments): a load on only some
+        // paths makes the compiler wait for it at the merge as if it were on every path,
+        // which would stall each step on the next step's fragments.
+        load_b(st + 1 < nsteps ? st + 1 : st, nxt);
         const int kh = tap / g.KW, kw = tap - kh * g.KW;
         const int toff = g.sign > 0 ? kh * g.HQ + kw : (g.KH - 1 - kh) * g.HQ + (g.KW - 1 - kw);
         const unsigned char* Hs = smem + (two ? (c & 1) : 0) * halo_bytes;
@@ -595,7 +626,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
             const int cl = wn * TN * MF + j * MF + MM::row(lg, 4 * g4);  // 4 consecutive channels
             float bj[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bj[q] = out.colbias(n0 + cl + q);
+            for (int q = 0; q < 4; ++q) bj[q] = out.colbias(par, cl + q);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int m = wm * TM * MF + i * MF + lr;
@@ -612,7 +643,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     if (col >= g.Nn) return;
     const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
     const int RQ = g.R * g.Q;
-    const typename Out::Cache cache = out.prep(col, nv);
+    const typename Out::Cache cache = out.prep(par, BN, cv * VEC, nv);
     for (int m = t / OVR; m < RQ; m += NTH / OVR) {
         const int rr = fdiv(m, g.fQ);
         const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
@@ -671,15 +702,21 @@ int halo_groups(int R, int Q, int KH, int KW) { return ((R + KH - 1) * (Q + KW -
 
 // bf16 tiles keep only the halo in LDS (weights go to registers); fp32 tiles also hold a
 // two-slot weight ring.  The epilogue reuses the same bytes.
-int plan_lds(int bm, int bn, int hb, int gh, int esize) {
+// Bytes before the per-column parameters: the halo (and weight) ring, reused by the epilogue.
+int plan_main(int bm, int bn, int hb, int gh, int esize) {
     const int ring = hb * gh * 1024 + (esize == 2 ? 0 : 2 * bn * 128);
     const int epi = bm * (bn + 16 / esize) * esize;
-    return ring > epi ? ring : epi;
+    return (int)align_up((size_t)(ring > epi ? ring : epi), 16);
 }
 
 struct Sides {
     int Hout, Wout, Cin, Nn;
+    int par;  // per-column epilogue parameter arrays (forward: bias and four batch-norm ones)
 };
+
+int plan_lds(int bm, int bn, int hb, int gh, int esize, const Sides& sd) {
+    return plan_main(bm, bn, hb, gh, esize) + sd.par * bn * 4;
+}
 
 // Estimated time of a tile layout: rounds of workgroups times the slower of the bytes a
 // CU loads (16-byte loads of whole cache lines run at about 34-60 B/clk per CU) and its
@@ -723,7 +760,7 @@ bool pick_halo(int dt, const ConvDims& d, const Sides& sd, HaloPlan* best) {
             if (R * Q * 4 < bm * 3) continue;
             const int gh = halo_groups(R, Q, d.KH, d.KW);
             for (int hb = 1; hb <= (chunks > 1 ? 2 : 1); ++hb) {
-                const int lds = plan_lds(bm, bn, hb, gh, es);
+                const int lds = plan_lds(bm, bn, hb, gh, es, sd);
                 if (lds > kLdsMax) continue;
                 const int occ = lds <= kLdsMax / 2 ? 2 : 1;
                 const double cost = plan_cost(dt, d, sd, bm, bn, hb, R, Q, occ);
@@ -762,6 +799,7 @@ HaloGeom make_geom(const ConvDims& d, const Sides& sd, const HaloPlan& p, int dt
     g.Kb = d.KH * d.KW * sd.Cin;
     g.sign = fwd ? 1 : -1;
     g.hb = p.hb;
+    g.par_off = plan_main(p.bm, p.bn, p.hb, g.GH, (int)dtype_size(dt));
     g.img_stride = (int64_t)g.Hin * g.Win * g.Cin;
     g.fQ = make_fastdiv(p.Q);
     g.fHQ = make_fastdiv(g.HQ);
@@ -826,8 +864,8 @@ hipError_t dispatch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, cons
     return hipErrorInvalidValue;
 }
 
-Sides fwd_sides(const ConvDims& d) { return Sides{d.OH, d.OW, d.IC, d.OC}; }
-Sides dx_sides(const ConvDims& d) { return Sides{d.H, d.W, d.OC, d.IC}; }
+Sides fwd_sides(const ConvDims& d) { return Sides{d.OH, d.OW, d.IC, d.OC, HFwdBnOut::kPar}; }
+Sides dx_sides(const ConvDims& d) { return Sides{d.H, d.W, d.OC, d.IC, HDxOut::kPar}; }
 
 // Fragment-ordered weights: 32-row groups covering every column tile, KH*KW*Cin k each.
 size_t frag_bytes(const ConvDims& d, const Sides& sd, const HaloPlan& p) {
