@@ -545,9 +545,10 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
 struct Dw3Geom {
     int N, H, W, IC, OC, KH, KW, OH, OW, ph, pw;
     int SEG, RS, nseg;  // stage: RS segments of SEG positions of output rows
+    int SEGp;           // LDS row of the second segment's first dz row (SEG rounded up to 4)
     int SPp;            // positions per stage, padded to a multiple of 16
     int XW, XR;         // input positions per segment (SEG + KW - 1), input rows per stage
-    int XWp;            // LDS row of the second segment's first input row (SEG + a multiple of 4)
+    int XWp;            // LDS row of the second segment's first input row (SEGp + a multiple of 4)
     int G;              // segments in all (N*OH*nseg)
     int nst;            // stages in all (ceil(G / RS))
     int spb;            // stages per slab
@@ -588,71 +589,74 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
     // every kernel row's workgroup sums every KH-th dz row of a stage for the bias gradient
     const bool do_db = want_db && ict_i == 0;
 
-    // Copy instructions of a stage: NA for dz (4 rows of 256 bytes each), then NB for the
-    // input rows; this wave issues instructions wid, wid + NW, ...  Lane l copies 16-byte
-    // chunk l%16 of row 4j + l/16; the swizzle of that row depends on l/16 only.
+    // Copy instructions of a stage: NA for dz (4 LDS rows of 256 bytes each), then NB for
+    // the input rows; this wave issues instructions wid, wid + NW, ...  Lane l copies
+    // 16-byte chunk l%16 of row 4j + l/16; the swizzle of that row depends on l/16 only.
+    // Segment r of a stage (RS <= 2 of them) holds its dz rows at LDS rows r*SEGp + q and
+    // its input row at LDS rows r*XWp + c (c = input column + pw - w0); a copy never spans
+    // two segments.  Each segment's dz rows and its input row are raw buffers sized to
+    // the valid data, so dz rows past the segment's length, input columns left or right
+    // of the image (offsets below the start wrap to huge values) and input rows above or
+    // below it (an empty buffer) all read as zeros.
     const int NA = g.SPp / 4, NB = g.XR / 4;
     const int rsub = lane >> 4;
     const int choff = ((lane & 15) ^ sw3(rsub)) * 16;  // source byte offset of the chunk
+    const uint32_t lane_dz = rsub * (g.OC * 2) + choff, lane_x = rsub * (g.IC * 2) + choff;
     const int nmine = (NA + NB - wid + NW - 1) / NW;    // instructions of this wave per stage
-    // Segment data of the stage being copied: uniform per workgroup.
+    // Buffers of the stage being copied (uniform per workgroup); fields are separate
+    // scalars, selected by value, so nothing is indexed at run time.
     struct Segs {
-        const char* dzb[2];  // first dz pixel of segment r (+ oc0), bytes
-        const char* xb[2];   // input row of segment r at iw = 0 (+ ic0), bytes; null if outside
-        int len[2];          // valid positions of segment r (0 if none)
-        int w0[2];
+        dma_rsrc dz0, dz1, x0, x1;
+        int xo0, xo1;  // byte offset of the segment's LDS input row 0 from its buffer: (w0 - pw)*IC*2
         uint32_t slot;
+    };
+    auto one_seg = [&](int gr, dma_rsrc& dzr, dma_rsrc& xr, int& xo) {
+        const bf16* dzb = dz;
+        const bf16* xb = x;
+        uint32_t dz_bytes = 0, x_bytes = 0;
+        xo = 0;
+        if (gr < g.G) {
+            const int f = fdiv(gr, g.fnseg);
+            const int sgi = gr - f * g.nseg;
+            const int n = fdiv(f, g.fOH), oh = f - n * g.OH;
+            const int w0 = sgi * g.SEG;
+            const int len = min(g.SEG, g.OW - w0);
+            dzb = dz + ((int64_t)f * g.OW + w0) * g.OC + oc0;
+            dz_bytes = (uint32_t)(len * g.OC * 2 - oc0 * 2);
+            const int ih = oh + kh - g.ph;
+            if ((unsigned)ih < (unsigned)g.H) {
+                xb = x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0;
+                x_bytes = (uint32_t)(g.W * g.IC * 2 - ic0 * 2);
+            }
+            xo = (w0 - g.pw) * g.IC * 2;
+        }
+        dzr = make_rsrc(dzb, dz_bytes);
+        xr = make_rsrc(xb, x_bytes);
     };
     auto segs_of = [&](int st) {
         Segs sg;
-        const int sidx = s_begin + st;
+        const int gr = (s_begin + st) * g.RS;
         sg.slot = smem_base + (uint32_t)((st & 1) * stage_bytes);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int gr = sidx * g.RS + r;
-            sg.len[r] = 0;
-            sg.w0[r] = 0;
-            sg.dzb[r] = (const char*)dz;
-            sg.xb[r] = nullptr;
-            if (r < g.RS && gr < g.G) {
-                const int f = fdiv(gr, g.fnseg);
-                const int sgi = gr - f * g.nseg;
-                const int n = fdiv(f, g.fOH), oh = f - n * g.OH;
-                sg.w0[r] = sgi * g.SEG;
-                sg.len[r] = min(g.SEG, g.OW - sg.w0[r]);
-                sg.dzb[r] = (const char*)(dz + ((int64_t)f * g.OW + sg.w0[r]) * g.OC + oc0);
-                const int ih = oh + kh - g.ph;
-                if ((unsigned)ih < (unsigned)g.H)
-                    sg.xb[r] = (const char*)(x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0);
-            }
-        }
+        one_seg(gr, sg.dz0, sg.x0, sg.xo0);
+        one_seg(g.RS == 2 ? gr + 1 : g.G, sg.dz1, sg.x1, sg.xo1);
         return sg;
     };
     // issue this wave's copy instructions i0 .. i1-1 of a stage
     auto issue = [&](const Segs& sg, int i0, int i1) {
         for (int i = i0; i < i1; ++i) {
             const int j = wid + NW * i;
-            const void* src = &kZero16;
-            uint32_t dst;
             if (j < NA) {
-                const int p = 4 * j + rsub;
-                const bool r = p >= g.SEG;
-                const int q = r ? p - g.SEG : p;
-                if (q < (r ? sg.len[1] : sg.len[0]))
-                    src = (r ? sg.dzb[1] : sg.dzb[0]) + q * (g.OC * 2) + choff;
-                dst = sg.slot + j * 1024;
+                const bool r = 4 * j >= g.SEGp;
+                const int row = 4 * j - (r ? g.SEGp : 0);
+                dma16_buf(lane_dz + (uint32_t)(row * (g.OC * 2)), r ? sg.dz1 : sg.dz0,
+                          __builtin_amdgcn_readfirstlane(sg.slot + j * 1024));
             } else {
                 const int jb = j - NA;
-                const int xr = 4 * jb + rsub;
-                const bool r = xr >= g.XWp;
-                const int qq = r ? xr - g.XWp : xr;
-                const char* xb = r ? sg.xb[1] : sg.xb[0];
-                const int iw = (r ? sg.w0[1] : sg.w0[0]) + qq - g.pw;
-                if (xb != nullptr && qq < g.XW && (r ? sg.len[1] : sg.len[0]) > 0 && (unsigned)iw < (unsigned)g.W)
-                    src = xb + iw * (g.IC * 2) + choff;
-                dst = sg.slot + g.SPp * 256 + jb * 1024;
+                const bool r = 4 * jb >= g.XWp;
+                const int row = 4 * jb - (r ? g.XWp : 0);
+                dma16_buf(lane_x + (uint32_t)(row * (g.IC * 2) + (r ? sg.xo1 : sg.xo0)), r ? sg.x1 : sg.x0,
+                          __builtin_amdgcn_readfirstlane(sg.slot + g.SPp * 256 + jb * 1024));
             }
-            dma16(src, __builtin_amdgcn_readfirstlane(dst));
         }
     };
 
@@ -690,7 +694,7 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
             b_off[j][half] = lds_off(prow[half] + (col >> 7), col & 127);
         }
     }
-    const int seg_shift = (g.XWp - g.SEG) * 256;
+    const int seg_shift = (g.XWp - g.SEGp) * 256;
     auto read_frags = [&](const unsigned char* As, const unsigned char* Xs, int kk, dw_short8 (&af)[TM],
                           dw_short8 (&bf)[TN]) {
         const unsigned char* Ak = As + kk * 256;
@@ -701,8 +705,8 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
             const dw_short4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Ak + a_off[i][1]));
             af[i] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        const int sh0 = kk + prow[0] >= g.SEG ? seg_shift : 0;
-        const int sh1 = kk + prow[1] >= g.SEG ? seg_shift : 0;
+        const int sh0 = kk + prow[0] >= g.SEGp ? seg_shift : 0;
+        const int sh1 = kk + prow[1] >= g.SEGp ? seg_shift : 0;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const dw_short4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Xk + b_off[j][0] + sh0));
@@ -963,11 +967,12 @@ Dw3Geom plan3(const ConvDims& d) {
         g.nseg = (int)ceil_div(d.OW, 128);
         g.SEG = (int)ceil_div(d.OW, g.nseg);
     }
-    g.SPp = (int)ceil_div(g.RS * g.SEG, 16) * 16;
+    g.SEGp = (int)ceil_div(g.SEG, 4) * 4;
+    g.SPp = (int)ceil_div(g.RS == 2 ? g.SEGp + g.SEG : g.SEG, 16) * 16;
     g.XW = g.SEG + d.KW - 1;
-    g.XWp = g.SEG + (int)ceil_div(d.KW - 1, 4) * 4;  // same swizzle phase as the first segment
+    g.XWp = g.SEGp + (int)ceil_div(d.KW - 1, 4) * 4;  // same swizzle phase as the first segment
     const int need_rows = g.RS == 2 ? g.XWp + g.XW : g.XW;
-    const int read_rows = g.SPp + (g.XWp - g.SEG) + d.KW - 1;  // padded positions included
+    const int read_rows = g.SPp + (g.XWp - g.SEGp) + d.KW - 1;  // padded positions included
     g.XR = (int)ceil_div(need_rows > read_rows ? need_rows : read_rows, 4) * 4;
     g.G = d.N * d.OH * g.nseg;
     g.nst = (int)ceil_div(g.G, g.RS);

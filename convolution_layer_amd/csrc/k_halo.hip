@@ -98,14 +98,34 @@ template <> __device__ __forceinline__ void put16<bf16>(bf16* p, const float* v)
                             pack_bf16x2(v[6], v[7]));
 }
 
-// Per-column epilogue parameters (bias, batch-norm statistics) are copied into LDS when a
-// workgroup starts, kPar arrays of BN floats (0 past the last column), so the epilogue
-// reads them at LDS latency instead of waiting on global loads after the main loop.
-// `colbias` takes a column of the tile; `prep` loads a thread's parameters for its 8
-// columns once.
-__device__ __forceinline__ void load_cols(float* dst, const float* src, int n0, int bn, int n, int t, int nth) {
-    for (int c = t; c < bn; c += nth) dst[c] = (src && n0 + c < n) ? src[n0 + c] : 0.0f;
-}
+// Per-column epilogue parameters (bias, batch-norm statistics) go to LDS, kPar arrays of
+// BN floats (0 past the last column): a workgroup loads them into registers while its
+// first halo is in flight and writes them to LDS after the prologue barrier, so the
+// epilogue reads them at LDS latency instead of waiting on global loads after the main
+// loop.  `par_src(k)` is parameter array k (nullable); `colbias` takes a column of the
+// tile; `prep` loads a thread's parameters for its 8 columns once.
+template <class Out, int BN, int NTH> struct ParStage {
+    static constexpr int N = Out::kPar * BN;
+    static constexpr int R = N > 0 ? (N + NTH - 1) / NTH : 1;  // registers per thread
+    float v[R];
+    __device__ __forceinline__ void load(const Out& out, int n0, int t) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int idx = t + k * NTH;
+            v[k] = 0.0f;
+            if (idx < N) {
+                const int kind = idx / BN, c = idx - kind * BN;
+                const float* src = out.par_src(kind);
+                if (src && n0 + c < out.ncols()) v[k] = src[n0 + c];
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float* par, int t) const {
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (t + k * NTH < N) par[t + k * NTH] = v[k];
+    }
+};
 
 // z = stored(acc + bias), y = act(z).  `raw` holds 16 bytes of stored z of one pixel.
 struct HFwdOut {
@@ -115,9 +135,8 @@ struct HFwdOut {
     int OC;
     static constexpr int kPar = 1;
     struct Cache {};
-    __device__ __forceinline__ void load_par(float* par, int n0, int bn, int t, int nth) const {
-        load_cols(par, bias, n0, bn, OC, t, nth);
-    }
+    __device__ __forceinline__ int ncols() const { return OC; }
+    __device__ __forceinline__ const float* par_src(int) const { return bias; }
     __device__ __forceinline__ float colbias(const float* par, int cl) const { return par[cl]; }
     __device__ __forceinline__ Cache prep(const float*, int, int, int) const { return Cache{}; }
     template <typename T, int ACT>
@@ -156,12 +175,9 @@ struct HFwdBnOut {
     struct Cache {
         float m[8], i[8], g[8], b[8];
     };
-    __device__ __forceinline__ void load_par(float* par, int n0, int bn, int t, int nth) const {
-        load_cols(par, bias, n0, bn, OC, t, nth);
-        load_cols(par + bn, mean, n0, bn, OC, t, nth);
-        load_cols(par + 2 * bn, inv_std, n0, bn, OC, t, nth);
-        load_cols(par + 3 * bn, gamma, n0, bn, OC, t, nth);
-        load_cols(par + 4 * bn, beta, n0, bn, OC, t, nth);
+    __device__ __forceinline__ int ncols() const { return OC; }
+    __device__ __forceinline__ const float* par_src(int k) const {
+        return k == 0 ? bias : k == 1 ? mean : k == 2 ? inv_std : k == 3 ? gamma : beta;
     }
     __device__ __forceinline__ float colbias(const float* par, int cl) const { return par[cl]; }
     // columns cl .. cl + nv - 1 lie inside the tile; the unused entries repeat column cl
@@ -207,7 +223,8 @@ struct HDxOut {
     int IC;
     static constexpr int kPar = 0;
     struct Cache {};
-    __device__ __forceinline__ void load_par(float*, int, int, int, int) const {}
+    __device__ __forceinline__ int ncols() const { return IC; }
+    __device__ __forceinline__ const float* par_src(int) const { return nullptr; }
     __device__ __forceinline__ float colbias(const float*, int) const { return 0.0f; }
     __device__ __forceinline__ Cache prep(const float*, int, int, int) const { return Cache{}; }
     template <typename T, int ACT>
@@ -262,8 +279,8 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
     const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
     const T* Aimg = A + (int64_t)n * g.img_stride;
-    float* par = (float*)(smem + g.par_off);
-    out.load_par(par, n0, BN, t, NTH);  // read after the prologue barrier
+    ParStage<Out, BN, NTH> pst;  // stored to LDS after the main loop
+    pst.load(out, n0, t);
     const int nsteps = g.nchunks * g.KH * g.KW;
 
     // Copy group grp covers 8 LDS rows (halo positions or weight rows) 8*grp .. 8*grp+7;
@@ -432,6 +449,8 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
         kh = kh2;
         kw = kw2;
     }
+    float* par = (float*)(smem + g.par_off);
+    pst.store(par, t);
     __syncthreads();
 
     // epilogue: stored values -> LDS (rows of BN + 16 bytes) -> 16-byte vectors
@@ -502,8 +521,8 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
     const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
     const bf16* Aimg = A + (int64_t)n * g.img_stride;
-    float* par = (float*)(smem + g.par_off);
-    out.load_par(par, n0, BN, t, NTH);  // read after the prologue barrier
+    ParStage<Out, BN, NTH> pst;  // stored to LDS after the main loop
+    pst.load(out, n0, t);
     const int taps = g.KH * g.KW;
     const int nsteps = g.nchunks * taps;
 
@@ -559,6 +578,13 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     uint4 bA[TN][KST], bB[TN][KST];
     issue_halo(0, 0, JH);
     load_b(0, bA);
+    // The first fragments are waited for here, while the halo copies are in flight;
+    // otherwise the compiler sinks their loads below the barrier and the first step
+    // waits for them on its own.
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk) asm volatile("" ::"v"(bA[j][kk].x));
     wait_dma(0);
     __syncthreads();
 
@@ -612,6 +638,8 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
         step(st, bA, bB);
         if (st + 1 < nsteps) step(st + 1, bB, bA);
     }
+    float* par = (float*)(smem + g.par_off);
+    pst.store(par, t);
     __syncthreads();
 
     // epilogue: stored values -> LDS (rows of BN + 16 bytes) -> 16-byte vectors.  The

@@ -25,6 +25,29 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
 }
 
+// The same copy through a raw buffer resource: lane i copies the 16 bytes at byte offset
+// voff of the buffer.  A 16-byte piece whose offset lies at or past the buffer's size
+// (including "negative" offsets, which wrap to huge unsigned values) is written as zeros,
+// so a buffer per tensor segment turns every padding and ragged-edge test into the
+// hardware's range check.
+typedef int dma_rsrc __attribute__((ext_vector_type(4)));
+
+// Raw buffer of `bytes` bytes at `base` (both wave-uniform; stride 0, no swizzle).
+__device__ __forceinline__ dma_rsrc make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    dma_rsrc r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    r.w = __builtin_amdgcn_readfirstlane(0x00020000);
+    return r;
+}
+
+__device__ __forceinline__ void dma16_buf(uint32_t voff, dma_rsrc rsrc, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // Wait until at most n of this wave's copies are outstanding (n wave-uniform; values
 // above 31 wait for 31, which is only more conservative).
 __device__ __forceinline__ void wait_dma(int n) {
