@@ -108,9 +108,22 @@ convmi_status check_ws(void* ws, size_t have, size_t want, const char* op) {
 
 int64_t rows_of(const ConvDims& d) { return (int64_t)d.N * d.OH * d.OW; }
 
+// Per-tile batch-norm statistics of the fused training forward, after its weight copy.
+size_t stats_offset(const convmi_desc* desc, const ConvDims& d) { return halo_fwd_ws_bytes(desc->dtype, d); }
+size_t stats_bytes(const convmi_desc* desc, const ConvDims& d) {
+    return align_up((size_t)halo_fwd_stat_tiles(desc->dtype, d) * 4 * d.OC * sizeof(float), 256);
+}
+
 size_t ws_forward(const convmi_desc* desc, const ConvDims& d) {
     size_t a = igemm_fwd_supported(desc->dtype, d) ? igemm_fwd_ws_bytes(desc->dtype, d) : 0;
-    size_t b = desc->normalization == CONVMI_NORM_BATCH ? bn_stats_ws_bytes(rows_of(d), d.OC, desc->dtype) : 0;
+    size_t b = 0;
+    if (desc->normalization == CONVMI_NORM_BATCH) {
+        b = bn_stats_ws_bytes(rows_of(d), d.OC, desc->dtype);
+        if (halo_fwd_supported(desc->dtype, d)) {
+            const size_t c = stats_offset(desc, d) + stats_bytes(desc, d);
+            if (c > b) b = c;
+        }
+    }
     return a > b ? a : b;
 }
 size_t ws_backward_data(const convmi_desc* desc, const ConvDims& d) {
@@ -212,6 +225,19 @@ CONVMI_API convmi_status conv2d_forward(const convmi_desc* desc, const void* x, 
         const float* bn_eval[4] = {save_mean, save_inv_std, gamma, beta};
         e = launch_halo_fwd(desc->dtype, x, w, bias, z, y, d, act, workspace, s, bn_eval);
         if (e != hipSuccess) return hip_fail(e, "conv2d_forward: convolution launch");
+        return CONVMI_OK;
+    }
+    // Training-mode batch norm on the input-tile-reuse path: the convolution's epilogue
+    // also reduces per-tile statistics of the stored z, so z is not read again for them.
+    if (bn && desc->mode == CONVMI_MODE_TRAIN && halo_fwd_supported(desc->dtype, d)) {
+        float* part = (float*)((char*)workspace + stats_offset(desc, d));
+        e = launch_halo_fwd(desc->dtype, x, w, bias, z, nullptr, d, act, workspace, s, nullptr, part);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: convolution launch");
+        e = launch_bn_tiles_finalize(part, halo_fwd_stat_tiles(desc->dtype, d), (int)d.OC, rows_of(d),
+                                     desc->momentum, desc->eps, save_mean, save_inv_std, running_mean, running_var, s);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: batch-norm statistics launch");
+        e = launch_apply_act(desc->dtype, z, y, rows_of(d), d.OC, act, 1, gamma, beta, save_mean, save_inv_std, s);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: normalise/activate launch");
         return CONVMI_OK;
     }
     void* conv_y = bn ? nullptr : y;

@@ -87,9 +87,16 @@ size_t halo_fwd_ws_bytes(int dt, const ConvDims& d);
 size_t halo_dx_ws_bytes(int dt, const ConvDims& d);
 // bn_eval: null, or {mean, inv_std, gamma, beta} of evaluation-mode batch norm, applied
 // before the activation in the epilogue (y = act(gamma*(z - mean)*inv_std + beta)).
+// stats_part: null, or room for 4 * C * halo_fwd_stat_tiles floats of per-tile training
+// batch-norm statistics of z; then only z is written (y and act are ignored) and
+// launch_bn_tiles_finalize turns the statistics into the batch mean and inverse std.
 hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
                            const ConvDims& d, int act, void* ws, hipStream_t s,
-                           const float* const* bn_eval = nullptr);
+                           const float* const* bn_eval = nullptr, float* stats_part = nullptr);
+int halo_fwd_stat_tiles(int dt, const ConvDims& d);  // spatial tiles of the forward (0: path not taken)
+// part[(c*4 + q)*ntiles + tile], q = S1, S2, shift, count (see the forward epilogue).
+hipError_t launch_bn_tiles_finalize(const float* part, int ntiles, int C, int64_t M, float momentum, float eps,
+                                    float* mean, float* inv_std, float* run_mean, float* run_var, hipStream_t s);
 hipError_t launch_halo_dx(int dt, const void* dz, const void* w, void* dx, const ConvDims& d, void* ws,
                           hipStream_t s);
 

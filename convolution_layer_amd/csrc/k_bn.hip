@@ -273,6 +273,56 @@ __global__ __launch_bounds__(kThreads) void bn_stats_finalize(const float* __res
     });
 }
 
+// Statistics from per-tile partials of the convolution epilogue: tile t of channel c
+// holds S1 = sum (z - s), S2 = sum (z - s)^2, its shift s and pixel count n at
+// part[(c*4 + q)*ntiles + t].  One workgroup per channel; in fp64 and in a fixed order
+// (thread j takes tiles j, j + kThreads, ..., then a tree over the threads):
+// mean = sum (n*s + S1) / M, then var = sum [S2 - S1^2/n + n*(s + S1/n - mean)^2] / M
+// (the tile's squared deviations about its own mean plus its mean's offset), so no
+// term cancels.  Running statistics as in bn_stats_finalize.
+__global__ __launch_bounds__(kThreads) void bn_tiles_finalize(const float* __restrict__ part, int ntiles, int64_t M,
+                                                              float momentum, float eps, float* __restrict__ mean,
+                                                              float* __restrict__ inv_std,
+                                                              float* __restrict__ run_mean,
+                                                              float* __restrict__ run_var) {
+    __shared__ double dred[kThreads];
+    const int c = blockIdx.x, t = threadIdx.x;
+    const float* S1 = part + (int64_t)c * 4 * ntiles;
+    const float* S2 = S1 + ntiles;
+    const float* SH = S2 + ntiles;
+    const float* CN = SH + ntiles;
+    auto tree = [&](double v) {  // fixed-order sum over the workgroup; every thread gets it
+        dred[t] = v;
+        __syncthreads();
+        for (int h = kThreads / 2; h > 0; h >>= 1) {
+            if (t < h) dred[t] += dred[t + h];
+            __syncthreads();
+        }
+        const double r = dred[0];
+        __syncthreads();
+        return r;
+    };
+    double a = 0.0;
+    for (int j = t; j < ntiles; j += kThreads) a += (double)CN[j] * (double)SH[j] + (double)S1[j];
+    const double mu = tree(a) / (double)M;
+    double b = 0.0;
+    for (int j = t; j < ntiles; j += kThreads) {
+        const double n = (double)CN[j], s1 = (double)S1[j];
+        const double dm = (double)SH[j] + s1 / n - mu;
+        b += ((double)S2[j] - s1 * s1 / n) + n * dm * dm;
+    }
+    double var = tree(b) / (double)M;
+    if (var < 0.0) var = 0.0;
+    if (t == 0) {
+        mean[c] = (float)mu;
+        inv_std[c] = (float)(1.0 / sqrt(var + (double)eps));
+        if (run_mean) {
+            run_mean[c] = (float)((1.0 - (double)momentum) * (double)run_mean[c] + (double)momentum * mu);
+            run_var[c] = (float)((1.0 - (double)momentum) * (double)run_var[c] + (double)momentum * var);
+        }
+    }
+}
+
 // Batch-norm backward, first launch: slab partials of A = sum dno and B = sum dno*zhat.
 template <typename T, int VEC, int ACT>
 __global__ __launch_bounds__(kThreads) void bn_bwd_partials(const T* __restrict__ z, const T* __restrict__ dy,
@@ -520,6 +570,12 @@ hipError_t launch_act_bwd(int dt, const void* z, const void* dy, void* dz, int64
     dim3 grid(elementwise_grid(nvec)), block(kThreads);
     CONVMI_VEC_SWITCH(dt, vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (act_bwd<T, VEC, A><<<grid, block, 0, s>>>(
                                                                    (const T*)z, (const T*)dy, (T*)dz, nvec))));
+    return hipGetLastError();
+}
+
+hipError_t launch_bn_tiles_finalize(const float* part, int ntiles, int C, int64_t M, float momentum, float eps,
+                                    float* mean, float* inv_std, float* run_mean, float* run_var, hipStream_t s) {
+    bn_tiles_finalize<<<C, kThreads, 0, s>>>(part, ntiles, M, momentum, eps, mean, inv_std, run_mean, run_var);
     return hipGetLastError();
 }
 

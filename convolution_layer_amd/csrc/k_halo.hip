@@ -134,6 +134,7 @@ struct HFwdOut {
     const float* bias;  // nullable
     int OC;
     static constexpr int kPar = 1;
+    static constexpr bool kStats = false;
     struct Cache {};
     __device__ __forceinline__ int ncols() const { return OC; }
     __device__ __forceinline__ const float* par_src(int) const { return bias; }
@@ -172,6 +173,7 @@ struct HFwdBnOut {
     int OC;
     const float *mean, *inv_std, *gamma, *beta;
     static constexpr int kPar = 5;  // bias, mean, inv_std, gamma, beta
+    static constexpr bool kStats = false;
     struct Cache {
         float m[8], i[8], g[8], b[8];
     };
@@ -218,10 +220,44 @@ struct HFwdBnOut {
     }
 };
 
+// Training-mode batch norm: z = stored(acc + bias) only (the normalisation needs the
+// batch statistics, so y comes from a later pass), plus per-tile statistics of the
+// stored z for each column: with shift s = the tile's first pixel, S1 = sum (z - s),
+// S2 = sum (z - s)^2 and the pixel count, at part[((c * 4 + q) * ntiles) + tile] for
+// q = S1, S2, s, count.  The shift keeps S2 free of cancellation when |mean| >> std;
+// bn_tiles_finalize merges the tiles in a fixed order.
+struct HFwdStatsOut {
+    void* z;
+    const float* bias;  // nullable
+    int OC;
+    float* part;
+    int ntiles;  // spatial tiles (images x tile rows x tile columns)
+    static constexpr int kPar = 1;
+    static constexpr bool kStats = true;
+    struct Cache {};
+    __device__ __forceinline__ int ncols() const { return OC; }
+    __device__ __forceinline__ const float* par_src(int) const { return bias; }
+    __device__ __forceinline__ float colbias(const float* par, int cl) const { return par[cl]; }
+    __device__ __forceinline__ Cache prep(const float*, int, int, int) const { return Cache{}; }
+    template <typename T, int ACT>
+    __device__ __forceinline__ void put(int64_t pix, int col, const uint4& raw, int nv, const Cache&) const {
+        constexpr int VEC = 16 / (int)sizeof(T);
+        const int64_t off = pix * OC + col;
+        if (nv == VEC && OC % VEC == 0) {
+            *(uint4*)((T*)z + off) = raw;
+        } else {
+            T v[VEC];
+            __builtin_memcpy(v, &raw, 16);
+            for (int j = 0; j < nv; ++j) ((T*)z)[off + j] = v[j];
+        }
+    }
+};
+
 struct HDxOut {
     void* dx;
     int IC;
     static constexpr int kPar = 0;
+    static constexpr bool kStats = false;
     struct Cache {};
     __device__ __forceinline__ int ncols() const { return IC; }
     __device__ __forceinline__ const float* par_src(int) const { return nullptr; }
@@ -242,6 +278,88 @@ struct HDxOut {
 };
 
 constexpr int kThreadsH = 256;  // four waves, WM x WN
+
+// Second half of the epilogue: the tile's stored values sit in LDS (Cs, rows of LDC
+// elements, pixel m = rr*Q + qq of the tile at row m); thread t writes columns
+// (t % OVR)*VEC .. +VEC of rows t/OVR, t/OVR + NTH/OVR, ...  With Out::kStats it also
+// reduces the per-tile column statistics (every thread of the workgroup reaches the
+// barriers below, active or not).
+template <typename T, int ACT, int BM, int BN, int NTH, class Out>
+__device__ __forceinline__ void epilogue_store(const T* Cs, const Out& out, const float* par, const HaloGeom& g,
+                                               int n, int r0, int c0, int n0, int sp) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    constexpr int LDC = BN + VEC;
+    constexpr int OVR = BN / VEC;
+    constexpr int RG = NTH / OVR;  // row groups
+    static_assert(NTH % OVR == 0, "each thread keeps one column range");
+    static_assert((2 * RG * BN + BN + RG) * 4 <= BM * LDC * (int)sizeof(T), "statistics fit the staging area");
+    const int t = threadIdx.x;
+    const int cv = t % OVR, col = n0 + cv * VEC;
+    const bool active = col < g.Nn;
+    if (!Out::kStats && !active) return;
+    const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
+    const int RQ = g.R * g.Q;
+    const typename Out::Cache cache = out.prep(par, BN, cv * VEC, nv);
+    float s1[VEC], s2[VEC], sh[VEC];
+    int cnt = 0;
+    if constexpr (Out::kStats) {
+        // pixel 0 of the tile (its first row and column) always lies inside the image
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            sh[j] = to_f32(Cs[cv * VEC + j]);
+            s1[j] = s2[j] = 0.0f;
+        }
+    }
+    if (active) {
+        for (int m = t / OVR; m < RQ; m += RG) {
+            const int rr = fdiv(m, g.fQ);
+            const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
+            if (oh >= g.Hout || ow >= g.Wout) continue;
+            const int64_t pix = ((int64_t)n * g.Hout + oh) * g.Wout + ow;
+            const uint4 raw = *(const uint4*)(Cs + m * LDC + cv * VEC);
+            out.template put<T, ACT>(pix, col, raw, nv, cache);
+            if constexpr (Out::kStats) {
+                T v[VEC];
+                __builtin_memcpy(v, &raw, 16);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const float d = to_f32(v[j]) - sh[j];
+                    s1[j] += d;
+                    s2[j] = __builtin_fmaf(d, d, s2[j]);
+                }
+                ++cnt;
+            }
+        }
+    }
+    if constexpr (Out::kStats) {
+        // fixed-order merge of the RG row groups per column (the staged tile is no longer read)
+        __syncthreads();
+        float* red = (float*)(void*)Cs;  // [2][RG][BN] sums, [BN] shifts, [RG] counts
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            red[(t / OVR) * BN + cv * VEC + j] = s1[j];
+            red[(RG + t / OVR) * BN + cv * VEC + j] = s2[j];
+        }
+        if (t < OVR)
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) red[2 * RG * BN + cv * VEC + j] = sh[j];
+        if (cv == 0) red[2 * RG * BN + BN + t / OVR] = (float)cnt;
+        __syncthreads();
+        if (t < BN && n0 + t < g.Nn) {
+            float a = 0.0f, b = 0.0f, c = 0.0f;
+            for (int k = 0; k < RG; ++k) {
+                a += red[k * BN + t];
+                b += red[(RG + k) * BN + t];
+                c += red[2 * RG * BN + BN + k];
+            }
+            float* p = out.part + (int64_t)(n0 + t) * 4 * out.ntiles + sp;
+            p[0] = a;
+            p[out.ntiles] = b;
+            p[2 * (int64_t)out.ntiles] = red[2 * RG * BN + t];
+            p[3 * (int64_t)out.ntiles] = c;
+        }
+    }
+}
 
 // Two workgroups per CU must fit the register file: at most 256 registers per lane.
 template <typename T, int MF, int BM, int BN, int WM, int WN, int ACT, class Out>
@@ -467,21 +585,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
                 Cs[(wm * TM * MF + i * MF + MM::row(lg, e)) * LDC + cl] = from_f32<T>(acc[i][j][e] + bj);
     }
     __syncthreads();
-    constexpr int OVR = BN / VEC;
-    static_assert(NTH % OVR == 0, "each thread keeps one column range");
-    const int cv = t % OVR, col = n0 + cv * VEC;
-    if (col >= g.Nn) return;
-    const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
-    const int RQ = g.R * g.Q;
-    const typename Out::Cache cache = out.prep(par, BN, cv * VEC, nv);
-    for (int m = t / OVR; m < RQ; m += NTH / OVR) {
-        const int rr = fdiv(m, g.fQ);
-        const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
-        if (oh >= g.Hout || ow >= g.Wout) continue;
-        const int64_t pix = ((int64_t)n * g.Hout + oh) * g.Wout + ow;
-        const uint4 raw = *(const uint4*)(Cs + m * LDC + cv * VEC);
-        out.template put<T, ACT>(pix, col, raw, nv, cache);
-    }
+    epilogue_store<T, ACT, BM, BN, NTH>(Cs, out, par, g, n, r0, c0, n0, sp);
 }
 
 // bf16 variant without a per-step barrier.  The weights are first laid out in MFMA
@@ -665,21 +769,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
         }
     }
     __syncthreads();
-    constexpr int OVR = BN / VEC;
-    static_assert(NTH % OVR == 0, "each thread keeps one column range");
-    const int cv = t % OVR, col = n0 + cv * VEC;
-    if (col >= g.Nn) return;
-    const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
-    const int RQ = g.R * g.Q;
-    const typename Out::Cache cache = out.prep(par, BN, cv * VEC, nv);
-    for (int m = t / OVR; m < RQ; m += NTH / OVR) {
-        const int rr = fdiv(m, g.fQ);
-        const int oh = r0 + rr, ow = c0 + (m - rr * g.Q);
-        if (oh >= g.Hout || ow >= g.Wout) continue;
-        const int64_t pix = ((int64_t)n * g.Hout + oh) * g.Wout + ow;
-        const uint4 raw = *(const uint4*)(Cs + m * LDC + cv * VEC);
-        out.template put<bf16, ACT>(pix, col, raw, nv, cache);
-    }
+    epilogue_store<bf16, ACT, BM, BN, NTH>(Cs, out, par, g, n, r0, c0, n0, sp);
 }
 
 // Weights in B-fragment order for halo_rb_kernel.  Output 16-byte unit
@@ -936,12 +1026,31 @@ size_t halo_dx_ws_bytes(int dt, const ConvDims& d) {
     return frag_bytes(d, dx_sides(d), p);
 }
 
+int halo_fwd_stat_tiles(int dt, const ConvDims& d) {
+    const Sides sd = fwd_sides(d);
+    HaloPlan p;
+    if (d.sh != 1 || d.sw != 1 || !pick_halo(dt, d, sd, &p)) return 0;
+    return (int)(d.N * ceil_div(sd.Hout, p.R) * ceil_div(sd.Wout, p.Q));
+}
+
 hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
-                           const ConvDims& d, int act, void* ws, hipStream_t s, const float* const* bn_eval) {
+                           const ConvDims& d, int act, void* ws, hipStream_t s, const float* const* bn_eval,
+                           float* stats_part) {
     const Sides sd = fwd_sides(d);
     HaloPlan p;
     if (d.sh != 1 || d.sw != 1 || !pick_halo(dt, d, sd, &p)) return hipErrorInvalidValue;
     const HaloGeom g = make_geom(d, sd, p, dt, true);
+    if (stats_part) {
+        if (bn_eval || !z) return hipErrorInvalidValue;
+        const int ntiles = d.N * g.tiles_r * g.tiles_c;
+        const HFwdStatsOut os{z, bias, d.OC, stats_part, ntiles};
+        if (dt == DT_BF16) {
+            const hipError_t e = launch_frag_weights((const bf16*)w, (uint4*)ws, d, sd, p, true, s);
+            if (e != hipSuccess) return e;
+            return dispatch_bf16<ACT_IDENTITY, HFwdStatsOut>((const bf16*)x, g, (const uint4*)ws, os, p, d.N, s);
+        }
+        return dispatch_f32<ACT_IDENTITY, HFwdStatsOut>((const float*)x, g, (const float*)w, os, p, d.N, s);
+    }
     const HFwdOut o{z, y, bias, d.OC};
     const HFwdBnOut ob{z, y, bias, d.OC, bn_eval ? bn_eval[0] : nullptr, bn_eval ? bn_eval[1] : nullptr,
                        bn_eval ? bn_eval[2] : nullptr, bn_eval ? bn_eval[3] : nullptr};

@@ -130,6 +130,12 @@ BN_MEDIUM = [
     ((2, 12, 12, 32, 40, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH),
     ((2, 7, 9, 5, 6, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_IDENTITY),
     ((1, 33, 35, 8, 300, 1, 1, 1, 1, 0, 0), WL.F32, WL.ACT_RELU),
+    # input-tile-reuse path (statistics reduced per tile in the convolution epilogue):
+    # ragged tiles, fewer channels than a column tile, several column tiles, bf16 layouts
+    ((2, 21, 19, 64, 40, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_SIGMOID),
+    ((2, 20, 20, 64, 130, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_IDENTITY),
+    ((2, 15, 17, 64, 72, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH),
+    ((3, 30, 9, 128, 64, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
 ]
 
 
@@ -493,6 +499,23 @@ def test_full_bn_stats_c3():
     G.assert_bn_stats(G.host(sm), G.host(si), mean_r, var_r, inv_r, wl.eps, "c3 stats")
     G.assert_close(G.host(rm_d), rm_r, WL.F32, "running_mean")
     G.assert_close(G.host(rv_d), rv_r, WL.F32, "running_var")
+
+
+def test_forward_batchnorm_large_offset():
+    """Training forward with batch norm whose channels sit far from zero (|mean| ~ 1000
+    std): the statistics reduced in the convolution epilogue must keep the variance."""
+    shape = WL.ConvShape(4, 16, 16, 64, 64, 3, 3, 1, 1, 1, 1)
+    x = WL.random_tensor(shape.x_shape, WL.F32, 62, ("normal", 0.0, 1.0))
+    w = WL.random_tensor(shape.w_shape, WL.F32, 63, ("normal", 0.0, (1.0 / shape.Kdim) ** 0.5))
+    b = WL.round_to(WL.F32, 1000.0 + np.arange(shape.OC))
+    gamma, beta = np.ones(shape.OC, np.float32), np.zeros(shape.OC, np.float32)
+    desc = G.shape_desc(shape, WL.F32, WL.ACT_IDENTITY, WL.NORM_BATCH, 0.1, 1e-5)
+    out = G.run_forward(desc, WL.F32, G.dev(x), G.dev(w), G.dev(b), G.dev(gamma), G.dev(beta))
+    zs = WL.round_to(WL.F32, O.conv2d_forward(x, w, b, (1, 1), (1, 1)))
+    G.assert_close(G.host(out["z"]), zs, WL.F32, "z")
+    mean_r, var_r, inv_r, *_ = O.bn_stats(zs, 0.1, 1e-5)
+    assert np.all(np.abs(mean_r) > 500 * np.sqrt(var_r))
+    G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, 1e-5, "offset fwd")
 
 
 def test_bn_stats_large_offset():
