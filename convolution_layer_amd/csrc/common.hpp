@@ -60,7 +60,8 @@ template <typename T> __device__ __forceinline__ float round_trip(float v) { ret
 // the hardware exponential and reciprocal (v_exp_f32, v_rcp_f32) keep it to a handful of
 // instructions.  Absolute error stays near fp32 rounding of values of order 1.
 __device__ __forceinline__ float fast_tanh(float a) {
-    const float e = __expf(-2.0f * __builtin_fabsf(a));
+    // exp(-2|a|) = 2^(|a| * -2 log2 e): one multiply (with the |.| source modifier) and v_exp_f32
+    const float e = __builtin_amdgcn_exp2f(__builtin_fabsf(a) * -2.8853900817779268f);
     const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
     return __builtin_copysignf(t, a);
 }
