@@ -534,21 +534,23 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
 
 // ------------------------------------------------------------------ stride-1 bf16 kernel
 // For stride 1 the KW taps of one kernel row read the same input row shifted by one
-// position each.  A workgroup owns a whole kernel row kh: 128 output channels x (KW taps
-// x 128 input channels).  It streams stages of RS output-row segments of SEG positions:
-// the dz rows (positions x 128 oc) and, once, the input rows they touch (SEG + KW - 1
-// positions x 128 ic); tap kw reads the input tile at a row offset of kw.  That loads
-// about a third of the bytes per FLOP of the per-tap gather above.  Operands are read
-// with transposing LDS reads into 32x32x16 MFMA fragments (lane l: column l%32,
-// positions 8*(l/32) .. +7 of the k-step).  One workgroup of eight waves per CU (the
-// stage ring is ~115 KB); each wave holds 2 x KW accumulator fragments.
+// position each.  A workgroup owns a whole kernel row kh: CH output channels x (KW taps
+// x CH input channels), CH = 128 or 64.  It streams stages of RS output-row segments of
+// SEG positions: the dz rows (positions x CH oc) and, once, the input rows they touch
+// (SEG + KW - 1 positions x CH ic); tap kw reads the input tile at a row offset of kw.
+// That loads about a third of the bytes per FLOP of the per-tap gather above.  Operands
+// are read with transposing LDS reads into 32x32x16 MFMA fragments (lane l: column l%32,
+// positions 8*(l/32) .. +7 of the k-step).  Each wave holds 2 x KW accumulator fragments
+// (64 oc x KW*32 columns).  CH = 128: eight waves (2 x 4), one workgroup per CU (the
+// stage ring is ~115 KB).  CH = 64 (64-channel layers): two waves (1 x 2) per workgroup
+// and shorter stages, four workgroups per CU.
 struct Dw3Geom {
     int N, H, W, IC, OC, KH, KW, OH, OW, ph, pw;
     int SEG, RS, nseg;  // stage: RS segments of SEG positions of output rows
-    int SEGp;           // LDS row of the second segment's first dz row (SEG rounded up to 4)
+    int SEGp;           // LDS row of the second segment's first dz row (SEG rounded up to a copy's rows)
     int SPp;            // positions per stage, padded to a multiple of 16
     int XW, XR;         // input positions per segment (SEG + KW - 1), input rows per stage
-    int XWp;            // LDS row of the second segment's first input row (SEGp + a multiple of 4)
+    int XWp;            // LDS row of the second segment's first input row (SEGp + a multiple of a copy's rows)
     int G;              // segments in all (N*OH*nseg)
     int nst;            // stages in all (ceil(G / RS))
     int spb;            // stages per slab
@@ -557,24 +559,35 @@ struct Dw3Geom {
     FastDiv fnseg, fOH;
 };
 
-// 16-byte chunk swizzle of a 256-byte LDS row: 4 consecutive rows read at the same
-// 32-byte column piece by one transposing read land in 4 different quarters of the banks.
-__device__ __forceinline__ int sw3(int row) { return (row & 3) << 2; }
+// 16-byte chunk swizzle of an LDS row: 4 consecutive rows read at the same 32-byte column
+// piece by one transposing read land in 4 different 32-byte slots of the 256 bytes the
+// banks span.  256-byte rows: chunk ^ 4*(row%4); 128-byte rows (two rows per bank span):
+// chunk ^ 2*((row/2)%2).
+template <int CH> __device__ __forceinline__ int sw3(int row) {
+    return CH == 128 ? (row & 3) << 2 : ((row >> 1) & 1) << 1;
+}
 
-constexpr int kDw3Threads = 512;  // eight waves: two per SIMD, so one wave's address work overlaps the other's MFMAs
+// Threads per workgroup: eight waves for 128-channel tiles (two per SIMD, so one wave's
+// address work overlaps the other's MFMAs); two waves for 64-channel tiles, four
+// workgroups per CU.
+template <int CH> constexpr int dw3_threads() { return CH == 128 ? 512 : 128; }
 
 // NK: k-steps per stage when known at compile time (0: read from the geometry); with a
 // fixed count every LDS offset of a k-step is an immediate.
-template <int KW_, int NK>
-__global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw3_kernel(
+template <int CH, int KW_, int NK>
+__global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw3_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ dz, Dw3Geom g, float* __restrict__ part,
     float* __restrict__ part_db, int want_db) {
-    constexpr int NW = kDw3Threads / 64;
-    constexpr int TM = 2, TN = KW_;  // wave tile 64 oc x KW*32 columns (waves 2 x 4)
+    constexpr int NT = dw3_threads<CH>(), NW = NT / 64;
+    constexpr int ROWB = CH * 2;         // LDS row bytes (one position)
+    constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+    constexpr int RPI = 1024 / ROWB;     // rows per 1-KB copy instruction
+    constexpr int WN = CH == 128 ? 4 : 2;  // waves: (CH/64) x WN
+    constexpr int TM = 2, TN = KW_;        // wave tile 64 oc x KW*32 columns
     extern __shared__ __align__(1024) unsigned char smem[];
     const int t = threadIdx.x, lane = t & 63;
     const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int stage_bytes = (g.SPp + g.XR) * 256;
+    const int stage_bytes = (g.SPp + g.XR) * ROWB;
     const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     // (slab, tile); the tiles of one slab share its dz rows and stay on one XCD
@@ -582,25 +595,25 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
     const int slab = lin / g.tiles, tile = lin - slab * g.tiles;
     const int oct_i = tile % g.oct, r1 = tile / g.oct;
     const int ict_i = r1 % g.ict, kh = r1 / g.ict;
-    const int oc0 = oct_i * 128, ic0 = ict_i * 128;
+    const int oc0 = oct_i * CH, ic0 = ict_i * CH;
     const int s_begin = slab * g.spb;
     const int s_end = min(g.nst, s_begin + g.spb);
     const int KT = s_end - s_begin;
     // every kernel row's workgroup sums every KH-th dz row of a stage for the bias gradient
     const bool do_db = want_db && ict_i == 0;
 
-    // Copy instructions of a stage: NA for dz (4 LDS rows of 256 bytes each), then NB for
-    // the input rows; this wave issues instructions wid, wid + NW, ...  Lane l copies
-    // 16-byte chunk l%16 of row 4j + l/16; the swizzle of that row depends on l/16 only.
+    // Copy instructions of a stage: NA for dz (RPI LDS rows each), then NB for the input
+    // rows; this wave issues instructions wid, wid + NW, ...  Lane l copies 16-byte chunk
+    // l%CPR of row RPI*j + l/CPR; the swizzle of that row depends on l/CPR only.
     // Segment r of a stage (RS <= 2 of them) holds its dz rows at LDS rows r*SEGp + q and
     // its input row at LDS rows r*XWp + c (c = input column + pw - w0); a copy never spans
     // two segments.  Each segment's dz rows and its input row are raw buffers sized to
     // the valid data, so dz rows past the segment's length, input columns left or right
     // of the image (offsets below the start wrap to huge values) and input rows above or
     // below it (an empty buffer) all read as zeros.
-    const int NA = g.SPp / 4, NB = g.XR / 4;
-    const int rsub = lane >> 4;
-    const int choff = ((lane & 15) ^ sw3(rsub)) * 16;  // source byte offset of the chunk
+    const int NA = g.SPp / RPI, NB = g.XR / RPI;
+    const int rsub = lane / CPR;
+    const int choff = ((lane % CPR) ^ sw3<CH>(rsub)) * 16;  // source byte offset of the chunk
     const uint32_t lane_dz = rsub * (g.OC * 2) + choff, lane_x = rsub * (g.IC * 2) + choff;
     const int nmine = (NA + NB - wid + NW - 1) / NW;    // instructions of this wave per stage
     // Buffers of the stage being copied (uniform per workgroup); fields are separate
@@ -646,21 +659,21 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
         for (int i = i0; i < i1; ++i) {
             const int j = wid + NW * i;
             if (j < NA) {
-                const bool r = 4 * j >= g.SEGp;
-                const int row = 4 * j - (r ? g.SEGp : 0);
+                const bool r = RPI * j >= g.SEGp;
+                const int row = RPI * j - (r ? g.SEGp : 0);
                 dma16_buf(lane_dz + (uint32_t)(row * (g.OC * 2)), r ? sg.dz1 : sg.dz0,
                           __builtin_amdgcn_readfirstlane(sg.slot + j * 1024));
             } else {
                 const int jb = j - NA;
-                const bool r = 4 * jb >= g.XWp;
-                const int row = 4 * jb - (r ? g.XWp : 0);
+                const bool r = RPI * jb >= g.XWp;
+                const int row = RPI * jb - (r ? g.XWp : 0);
                 dma16_buf(lane_x + (uint32_t)(row * (g.IC * 2) + (r ? sg.xo1 : sg.xo0)), r ? sg.x1 : sg.x0,
-                          __builtin_amdgcn_readfirstlane(sg.slot + g.SPp * 256 + jb * 1024));
+                          __builtin_amdgcn_readfirstlane(sg.slot + g.SPp * ROWB + jb * 1024));
             }
         }
     };
 
-    const int wm = wid >> 2, wn = wid & 3;
+    const int wm = wid / WN, wn = wid % WN;
     floatx16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -672,14 +685,14 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
     // Transposing fragment read: lane l gets column c + l%32 at positions
     // kk + 8*(l/32) .. +7; in each 16-lane group lane i addresses position +i/4 of a
     // half and the 8-byte piece 4*(i%4) of the group's 16 columns.  Input rows of tap kw
-    // sit kw rows further; the second segment's rows start XWp - SEG rows later, a
+    // sit kw rows further; the second segment's rows start XWp - SEGp rows later, a
     // multiple of 4, so the swizzle is unchanged.  k-steps start at multiples of 16, so
-    // every offset is a per-lane constant plus kk*256 (plus the second-segment shift).
+    // every offset is a per-lane constant plus kk*ROWB (plus the second-segment shift).
     typedef short dw_short8 __attribute__((ext_vector_type(8)));
     const int l16 = lane & 15, hi = (lane >> 4) & 1, kb8 = 8 * (lane >> 5);
     auto lds_off = [&](int row, int c) {
         const int cb = 2 * (c + 16 * hi + 4 * (l16 & 3));
-        return row * 256 + ((((cb >> 4) ^ sw3(row)) << 4) | (cb & 15));
+        return row * ROWB + ((((cb >> 4) ^ sw3<CH>(row)) << 4) | (cb & 15));
     };
     int a_off[TM][2], b_off[TN][2];
     int prow[2];
@@ -690,15 +703,15 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
         for (int i = 0; i < TM; ++i) a_off[i][half] = lds_off(prow[half], wm * 64 + i * 32);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = wn * KW_ * 32 + j * 32;  // tap col/128, input channel col%128
-            b_off[j][half] = lds_off(prow[half] + (col >> 7), col & 127);
+            const int col = wn * KW_ * 32 + j * 32;  // tap col/CH, input channel col%CH
+            b_off[j][half] = lds_off(prow[half] + col / CH, col % CH);
         }
     }
-    const int seg_shift = (g.XWp - g.SEGp) * 256;
+    const int seg_shift = (g.XWp - g.SEGp) * ROWB;
     auto read_frags = [&](const unsigned char* As, const unsigned char* Xs, int kk, dw_short8 (&af)[TM],
                           dw_short8 (&bf)[TN]) {
-        const unsigned char* Ak = As + kk * 256;
-        const unsigned char* Xk = Xs + kk * 256;
+        const unsigned char* Ak = As + kk * ROWB;
+        const unsigned char* Xk = Xs + kk * ROWB;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const dw_short4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(Ak + a_off[i][0]));
@@ -724,15 +737,15 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
                                                                     0, 0, 0);
     };
 
-    // Column sums of dz for the bias gradient: thread t owns chunk t%16 (8 channels) of
-    // rows kh + KH*(t/16), kh + KH*(t/16 + 32), ...
-    constexpr int RG = kDw3Threads / 16;  // row groups
+    // Column sums of dz for the bias gradient: thread t owns chunk t%CPR (8 channels) of
+    // rows kh + KH*(t/CPR), kh + KH*(t/CPR + RG), ...
+    constexpr int RG = NT / CPR;  // row groups
     float dbs[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) dbs[j] = 0.0f;
     auto db_sum = [&](const unsigned char* As) {
-        for (int row = kh + g.KH * (t >> 4); row < g.SPp; row += RG * g.KH) {
-            const uint4 v = *(const uint4*)(As + row * 256 + (((t & 15) ^ sw3(row)) << 4));
+        for (int row = kh + g.KH * (t / CPR); row < g.SPp; row += RG * g.KH) {
+            const uint4 v = *(const uint4*)(As + row * ROWB + (((t % CPR) ^ sw3<CH>(row)) << 4));
             const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -754,7 +767,7 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
         const bool next = k + 1 < KT;
         const Segs sg = segs_of(next ? k + 1 : k);
         const unsigned char* As = smem + (k & 1) * stage_bytes;
-        const unsigned char* Xs = As + g.SPp * 256;
+        const unsigned char* Xs = As + g.SPp * ROWB;
         if (do_db) db_sum(As);
         dw_short8 fa[2][TM], fb[2][TN];
         read_frags(As, Xs, 0, fa[0], fb[0]);
@@ -789,7 +802,7 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int col = wn * KW_ * 32 + j * 32;
-            const int k = (kh * g.KW + (col >> 7)) * g.IC + ic0 + (col & 127) + (lane & 31);
+            const int k = (kh * g.KW + col / CH) * g.IC + ic0 + col % CH + (lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int oc = oc0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
@@ -798,13 +811,13 @@ __global__ __launch_bounds__(kDw3Threads) __attribute__((amdgpu_waves_per_eu(2, 
         }
     if (do_db) {  // uniform per workgroup
         __syncthreads();
-        float* red = (float*)smem;  // [RG][128]; the ring is no longer needed
+        float* red = (float*)smem;  // [RG][CH]; the ring is no longer needed
 #pragma unroll
-        for (int j = 0; j < 8; ++j) red[(t >> 4) * 128 + (t & 15) * 8 + j] = dbs[j];
+        for (int j = 0; j < 8; ++j) red[(t / CPR) * CH + (t % CPR) * 8 + j] = dbs[j];
         __syncthreads();
-        if (t < 128) {
+        if (t < CH) {
             float s_ = 0.0f;
-            for (int q = 0; q < RG; ++q) s_ += red[q * 128 + t];
+            for (int q = 0; q < RG; ++q) s_ += red[q * CH + t];
             part_db[((int64_t)slab * g.KH + kh) * g.OC + oc0 + t] = s_;
         }
     }
@@ -946,40 +959,48 @@ hipError_t launch_cfg(const T* x, const T* dz, const DwGeom& g, const Plan& p, f
     return hipGetLastError();
 }
 
-// Stride-1 bf16 layers with 128-channel multiples and kernels at most 3 wide.
-bool dw3_ok(int dt, const ConvDims& d) {
-    return dt == DT_BF16 && d.sh == 1 && d.sw == 1 && d.OC % 128 == 0 && d.IC % 128 == 0 && d.KW >= 1 &&
-           d.KW <= 3;
+// Channel width of the stride-1 bf16 kernel for this layer: 128 when both channel counts
+// are multiples of 128, else 64 when both are multiples of 64; 0: not taken (kernels at
+// most 3 wide).
+int dw3_ch(int dt, const ConvDims& d) {
+    if (dt != DT_BF16 || d.sh != 1 || d.sw != 1 || d.KW < 1 || d.KW > 3) return 0;
+    if (d.OC % 128 == 0 && d.IC % 128 == 0) return 128;
+    if (d.OC % 64 == 0 && d.IC % 64 == 0) return 64;
+    return 0;
 }
+bool dw3_ok(int dt, const ConvDims& d) { return dw3_ch(dt, d) != 0; }
 
-// Stage geometry: two whole output rows when they fit in 128 positions, else one row
-// split into equal segments of at most 128.  About one workgroup per CU.
-Dw3Geom plan3(const ConvDims& d) {
+// Stage geometry.  128 channels: two whole output rows when they fit in 128 positions,
+// else one row split into equal segments of at most 128; about one workgroup per CU.
+// 64 channels: two segments of at most 32 positions (or two whole rows of at most 32);
+// about four workgroups per CU.  Segment starts are aligned to a copy's rows.
+Dw3Geom plan3(const ConvDims& d, int ch) {
     Dw3Geom g;
     g.N = d.N; g.H = d.H; g.W = d.W; g.IC = d.IC; g.OC = d.OC; g.KH = d.KH; g.KW = d.KW;
     g.OH = d.OH; g.OW = d.OW; g.ph = d.ph; g.pw = d.pw;
-    if (2 * d.OW <= 128) {
+    const int seg_max = ch == 128 ? 128 : 32, rpi = 1024 / (2 * ch);
+    if (2 * d.OW <= (ch == 128 ? 128 : 64)) {
         g.RS = 2;
         g.nseg = 1;
         g.SEG = d.OW;
     } else {
-        g.RS = 1;
-        g.nseg = (int)ceil_div(d.OW, 128);
+        g.RS = ch == 128 ? 1 : 2;
+        g.nseg = (int)ceil_div(d.OW, seg_max);
         g.SEG = (int)ceil_div(d.OW, g.nseg);
     }
-    g.SEGp = (int)ceil_div(g.SEG, 4) * 4;
+    g.SEGp = (int)ceil_div(g.SEG, rpi) * rpi;
     g.SPp = (int)ceil_div(g.RS == 2 ? g.SEGp + g.SEG : g.SEG, 16) * 16;
     g.XW = g.SEG + d.KW - 1;
-    g.XWp = g.SEGp + (int)ceil_div(d.KW - 1, 4) * 4;  // same swizzle phase as the first segment
+    g.XWp = g.SEGp + (int)ceil_div(d.KW - 1, rpi) * rpi;  // same swizzle phase as the first segment
     const int need_rows = g.RS == 2 ? g.XWp + g.XW : g.XW;
     const int read_rows = g.SPp + (g.XWp - g.SEGp) + d.KW - 1;  // padded positions included
-    g.XR = (int)ceil_div(need_rows > read_rows ? need_rows : read_rows, 4) * 4;
+    g.XR = (int)ceil_div(need_rows > read_rows ? need_rows : read_rows, rpi) * rpi;
     g.G = d.N * d.OH * g.nseg;
     g.nst = (int)ceil_div(g.G, g.RS);
-    g.ict = d.IC / 128;
-    g.oct = d.OC / 128;
+    g.ict = d.IC / ch;
+    g.oct = d.OC / ch;
     g.tiles = d.KH * g.ict * g.oct;
-    int S = 256 / g.tiles;
+    int S = (ch == 128 ? 256 : 1024) / g.tiles;
     if (S < 1) S = 1;
     if (S > g.nst) S = g.nst;
     g.spb = (int)ceil_div(g.nst, S);
@@ -990,12 +1011,12 @@ Dw3Geom plan3(const ConvDims& d) {
     return g;
 }
 
-size_t dw3_lds(const Dw3Geom& g) { return (size_t)2 * (g.SPp + g.XR) * 256; }
+size_t dw3_lds(const Dw3Geom& g, int ch) { return (size_t)2 * (g.SPp + g.XR) * 2 * ch; }
 
-template <int KW_, int NK>
+template <int CH, int KW_, int NK>
 hipError_t launch_dw3_kw(const bf16* x, const bf16* dz, const Dw3Geom& g, float* part, float* part_db, int want_db,
                          hipStream_t s) {
-    auto kern = dw3_kernel<KW_, NK>;
+    auto kern = dw3_kernel<CH, KW_, NK>;
     static bool raised = false;  // the dynamic LDS limit is raised once per instantiation
     if (!raised) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1003,8 +1024,8 @@ hipError_t launch_dw3_kw(const bf16* x, const bf16* dz, const Dw3Geom& g, float*
         if (e != hipSuccess) return e;
         raised = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(g.S * g.tiles)), dim3(kDw3Threads), dw3_lds(g), s, x, dz, g, part,
-                       part_db, want_db);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(g.S * g.tiles)), dim3(dw3_threads<CH>()), dw3_lds(g, CH), s, x, dz, g,
+                       part, part_db, want_db);
     return hipGetLastError();
 }
 
@@ -1017,7 +1038,7 @@ bool igemm_dw_supported(int dt, const ConvDims& d) {
 
 size_t igemm_dw_ws_bytes(int dt, const ConvDims& d) {
     const bool s1 = dw3_ok(dt, d);
-    const int S = s1 ? plan3(d).S : plan(dt, d).S;
+    const int S = s1 ? plan3(d, dw3_ch(dt, d)).S : plan(dt, d).S;
     const int Sdb = s1 ? S * d.KH : S;  // bias partials: one per slab (and kernel row)
     const size_t Kdim = (size_t)d.KH * d.KW * d.IC;
     return align_up((size_t)S * d.OC * Kdim * 4, 256) + align_up((size_t)Sdb * d.OC * 4, 256);
@@ -1026,18 +1047,26 @@ size_t igemm_dw_ws_bytes(int dt, const ConvDims& d) {
 hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, float* db, int accumulate,
                            const ConvDims& d, void* ws, hipStream_t s) {
     if (dw3_ok(dt, d)) {
-        const Dw3Geom g = plan3(d);
+        const int ch = dw3_ch(dt, d);
+        const Dw3Geom g = plan3(d, ch);
         float* part = (float*)ws;
         float* part_db = (float*)((char*)ws + align_up((size_t)g.S * d.OC * g.Kdim * 4, 256));
         const int want_db = db != nullptr;
         const bf16 *xb = (const bf16*)x, *zb = (const bf16*)dz;
         hipError_t e = hipErrorInvalidValue;
         const int nk = g.SPp / 16;
-        if (d.KW == 3 && nk == 7) e = launch_dw3_kw<3, 7>(xb, zb, g, part, part_db, want_db, s);
-        else if (d.KW == 3 && nk == 8) e = launch_dw3_kw<3, 8>(xb, zb, g, part, part_db, want_db, s);
-        else if (d.KW == 3) e = launch_dw3_kw<3, 0>(xb, zb, g, part, part_db, want_db, s);
-        else if (d.KW == 2) e = launch_dw3_kw<2, 0>(xb, zb, g, part, part_db, want_db, s);
-        else e = launch_dw3_kw<1, 0>(xb, zb, g, part, part_db, want_db, s);
+        if (ch == 128) {
+            if (d.KW == 3 && nk == 7) e = launch_dw3_kw<128, 3, 7>(xb, zb, g, part, part_db, want_db, s);
+            else if (d.KW == 3 && nk == 8) e = launch_dw3_kw<128, 3, 8>(xb, zb, g, part, part_db, want_db, s);
+            else if (d.KW == 3) e = launch_dw3_kw<128, 3, 0>(xb, zb, g, part, part_db, want_db, s);
+            else if (d.KW == 2) e = launch_dw3_kw<128, 2, 0>(xb, zb, g, part, part_db, want_db, s);
+            else e = launch_dw3_kw<128, 1, 0>(xb, zb, g, part, part_db, want_db, s);
+        } else {
+            if (d.KW == 3 && nk == 4) e = launch_dw3_kw<64, 3, 4>(xb, zb, g, part, part_db, want_db, s);
+            else if (d.KW == 3) e = launch_dw3_kw<64, 3, 0>(xb, zb, g, part, part_db, want_db, s);
+            else if (d.KW == 2) e = launch_dw3_kw<64, 2, 0>(xb, zb, g, part, part_db, want_db, s);
+            else e = launch_dw3_kw<64, 1, 0>(xb, zb, g, part, part_db, want_db, s);
+        }
         if (e != hipSuccess) return e;
         const int64_t count = (int64_t)d.OC * g.Kdim;
         dw_reduce4<<<reduce_grid(count, d.OC, db != nullptr), NT, 0, s>>>(part, part_db, dw, db, count, d.OC, g.S,

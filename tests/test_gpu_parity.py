@@ -66,6 +66,13 @@ MEDIUM = [
     ((2, 11, 33, 128, 128, 1, 2, 1, 1, 0, 0), WL.BF16, WL.ACT_SIGMOID),
     ((1, 6, 50, 128, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),      # 7 k-steps, padded
     ((1, 4, 60, 128, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_IDENTITY),  # 8 k-steps, padded
+    # the same kernel with 64-channel tiles: segmented rows, whole-row stages, two channel
+    # tiles on either side, 1-3 taps wide, asymmetric padding
+    ((2, 9, 70, 64, 64, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+    ((1, 6, 20, 64, 64, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+    ((1, 5, 300, 64, 128, 2, 3, 1, 1, 0, 1), WL.BF16, WL.ACT_IDENTITY),
+    ((3, 7, 40, 128, 64, 3, 1, 1, 1, 1, 0), WL.BF16, WL.ACT_TANH),
+    ((2, 11, 33, 64, 64, 1, 2, 1, 1, 0, 0), WL.BF16, WL.ACT_SIGMOID),
 ]
 
 
