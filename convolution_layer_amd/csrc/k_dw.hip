@@ -559,13 +559,101 @@ struct Dw3Geom {
     FastDiv fnseg, fOH;
 };
 
-// 16-byte chunk swizzle of an LDS row: 4 consecutive rows read at the same 32-byte column
-// piece by one transposing read land in 4 different 32-byte slots of the 256 bytes the
-// banks span.  256-byte rows: chunk ^ 4*(row%4); 128-byte rows (two rows per bank span):
-// chunk ^ 2*((row/2)%2).
-template <int CH> __device__ __forceinline__ int sw3(int row) {
-    return CH == 128 ? (row & 3) << 2 : ((row >> 1) & 1) << 1;
+// 16-byte chunk swizzle of an LDS row of ROWB bytes: 4 consecutive rows read at the same
+// 32-byte column piece (bf16 transposing reads) or 64-byte piece (fp32 reads) land in
+// different slots of the 256 bytes the banks span.  256-byte rows: chunk ^ 4*(row%4);
+// 128-byte rows (two rows per bank span): chunk ^ 2*((row/2)%2).
+template <int ROWB> __device__ __forceinline__ int sw3(int row) {
+    return ROWB == 256 ? (row & 3) << 2 : ((row >> 1) & 1) << 1;
 }
+
+// Stage copies of the stride-1 weight-gradient kernels, for tiles of CH channels of T
+// (LDS rows of ROWB = CH*sizeof(T) bytes, RPI rows per 1-KB copy) and NT threads.
+// Copy instructions of a stage: NA for dz (RPI LDS rows each), then NB for the input
+// rows; wave w issues instructions w, w + NW, ...  Lane l copies 16-byte chunk l%CPR of
+// row RPI*j + l/CPR; the swizzle of that row depends on l/CPR only.  Segment r of a
+// stage (RS <= 2 of them) holds its dz rows at LDS rows r*SEGp + q and its input row at
+// LDS rows r*XWp + c (c = input column + pw - w0); a copy never spans two segments.
+// Each segment's dz rows and its input row are raw buffers sized to the valid data, so
+// dz rows past the segment's length, input columns left or right of the image (offsets
+// below the start wrap to huge values) and input rows above or below it (an empty
+// buffer) all read as zeros.
+template <typename T, int CH, int NT> struct Dw3Copies {
+    static constexpr int ES = (int)sizeof(T), ROWB = CH * ES, CPR = ROWB / 16, RPI = 1024 / ROWB, NW = NT / 64;
+    // Buffers of the stage being copied (uniform per workgroup); fields are separate
+    // scalars, selected by value, so nothing is indexed at run time.
+    struct Segs {
+        dma_rsrc dz0, dz1, x0, x1;
+        int xo0, xo1;  // byte offset of the segment's LDS input row 0 from its buffer: (w0 - pw)*IC*ES
+        uint32_t slot;
+    };
+    const T* x;
+    const T* dz;
+    int kh, oc0, ic0, s_begin, wid, NA, NB, nmine, stage_bytes;
+    uint32_t lane_dz, lane_x, smem_base;
+
+    __device__ __forceinline__ Dw3Copies(const Dw3Geom& g, const T* x_, const T* dz_, int kh_, int oc0_, int ic0_,
+                                         int s_begin_, int wid_, int lane, uint32_t smem_base_)
+        : x(x_), dz(dz_), kh(kh_), oc0(oc0_), ic0(ic0_), s_begin(s_begin_), wid(wid_), smem_base(smem_base_) {
+        NA = g.SPp / RPI;
+        NB = g.XR / RPI;
+        nmine = (NA + NB - wid + NW - 1) / NW;  // instructions of this wave per stage
+        stage_bytes = (g.SPp + g.XR) * ROWB;
+        const int rsub = lane / CPR;
+        const int choff = ((lane % CPR) ^ sw3<ROWB>(rsub)) * 16;  // source byte offset of the chunk
+        lane_dz = rsub * (g.OC * ES) + choff;
+        lane_x = rsub * (g.IC * ES) + choff;
+    }
+    __device__ __forceinline__ void one_seg(const Dw3Geom& g, int gr, dma_rsrc& dzr, dma_rsrc& xr, int& xo) const {
+        const T* dzb = dz;
+        const T* xb = x;
+        uint32_t dz_bytes = 0, x_bytes = 0;
+        xo = 0;
+        if (gr < g.G) {
+            const int f = fdiv(gr, g.fnseg);
+            const int sgi = gr - f * g.nseg;
+            const int n = fdiv(f, g.fOH), oh = f - n * g.OH;
+            const int w0 = sgi * g.SEG;
+            const int len = min(g.SEG, g.OW - w0);
+            dzb = dz + ((int64_t)f * g.OW + w0) * g.OC + oc0;
+            dz_bytes = (uint32_t)((len * g.OC - oc0) * ES);
+            const int ih = oh + kh - g.ph;
+            if ((unsigned)ih < (unsigned)g.H) {
+                xb = x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0;
+                x_bytes = (uint32_t)((g.W * g.IC - ic0) * ES);
+            }
+            xo = (w0 - g.pw) * g.IC * ES;
+        }
+        dzr = make_rsrc(dzb, dz_bytes);
+        xr = make_rsrc(xb, x_bytes);
+    }
+    __device__ __forceinline__ Segs segs_of(const Dw3Geom& g, int st) const {
+        Segs sg;
+        const int gr = (s_begin + st) * g.RS;
+        sg.slot = smem_base + (uint32_t)((st & 1) * stage_bytes);
+        one_seg(g, gr, sg.dz0, sg.x0, sg.xo0);
+        one_seg(g, g.RS == 2 ? gr + 1 : g.G, sg.dz1, sg.x1, sg.xo1);
+        return sg;
+    }
+    // this wave's copy instructions i0 .. i1-1 of a stage
+    __device__ __forceinline__ void issue(const Dw3Geom& g, const Segs& sg, int i0, int i1) const {
+        for (int i = i0; i < i1; ++i) {
+            const int j = wid + NW * i;
+            if (j < NA) {
+                const bool r = RPI * j >= g.SEGp;
+                const int row = RPI * j - (r ? g.SEGp : 0);
+                dma16_buf(lane_dz + (uint32_t)(row * (g.OC * ES)), r ? sg.dz1 : sg.dz0,
+                          __builtin_amdgcn_readfirstlane(sg.slot + j * 1024));
+            } else {
+                const int jb = j - NA;
+                const bool r = RPI * jb >= g.XWp;
+                const int row = RPI * jb - (r ? g.XWp : 0);
+                dma16_buf(lane_x + (uint32_t)(row * (g.IC * ES) + (r ? sg.xo1 : sg.xo0)), r ? sg.x1 : sg.x0,
+                          __builtin_amdgcn_readfirstlane(sg.slot + g.SPp * ROWB + jb * 1024));
+            }
+        }
+    }
+};
 
 // Threads per workgroup: eight waves for 128-channel tiles (two per SIMD, so one wave's
 // address work overlaps the other's MFMAs); two waves for 64-channel tiles, four
@@ -578,10 +666,9 @@ template <int CH, int KW_, int NK>
 __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw3_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ dz, Dw3Geom g, float* __restrict__ part,
     float* __restrict__ part_db, int want_db) {
-    constexpr int NT = dw3_threads<CH>(), NW = NT / 64;
+    constexpr int NT = dw3_threads<CH>();
     constexpr int ROWB = CH * 2;         // LDS row bytes (one position)
     constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
-    constexpr int RPI = 1024 / ROWB;     // rows per 1-KB copy instruction
     constexpr int WN = CH == 128 ? 4 : 2;  // waves: (CH/64) x WN
     constexpr int TM = 2, TN = KW_;        // wave tile 64 oc x KW*32 columns
     extern __shared__ __align__(1024) unsigned char smem[];
@@ -602,76 +689,11 @@ __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_
     // every kernel row's workgroup sums every KH-th dz row of a stage for the bias gradient
     const bool do_db = want_db && ict_i == 0;
 
-    // Copy instructions of a stage: NA for dz (RPI LDS rows each), then NB for the input
-    // rows; this wave issues instructions wid, wid + NW, ...  Lane l copies 16-byte chunk
-    // l%CPR of row RPI*j + l/CPR; the swizzle of that row depends on l/CPR only.
-    // Segment r of a stage (RS <= 2 of them) holds its dz rows at LDS rows r*SEGp + q and
-    // its input row at LDS rows r*XWp + c (c = input column + pw - w0); a copy never spans
-    // two segments.  Each segment's dz rows and its input row are raw buffers sized to
-    // the valid data, so dz rows past the segment's length, input columns left or right
-    // of the image (offsets below the start wrap to huge values) and input rows above or
-    // below it (an empty buffer) all read as zeros.
-    const int NA = g.SPp / RPI, NB = g.XR / RPI;
-    const int rsub = lane / CPR;
-    const int choff = ((lane % CPR) ^ sw3<CH>(rsub)) * 16;  // source byte offset of the chunk
-    const uint32_t lane_dz = rsub * (g.OC * 2) + choff, lane_x = rsub * (g.IC * 2) + choff;
-    const int nmine = (NA + NB - wid + NW - 1) / NW;    // instructions of this wave per stage
-    // Buffers of the stage being copied (uniform per workgroup); fields are separate
-    // scalars, selected by value, so nothing is indexed at run time.
-    struct Segs {
-        dma_rsrc dz0, dz1, x0, x1;
-        int xo0, xo1;  // byte offset of the segment's LDS input row 0 from its buffer: (w0 - pw)*IC*2
-        uint32_t slot;
-    };
-    auto one_seg = [&](int gr, dma_rsrc& dzr, dma_rsrc& xr, int& xo) {
-        const bf16* dzb = dz;
-        const bf16* xb = x;
-        uint32_t dz_bytes = 0, x_bytes = 0;
-        xo = 0;
-        if (gr < g.G) {
-            const int f = fdiv(gr, g.fnseg);
-            const int sgi = gr - f * g.nseg;
-            const int n = fdiv(f, g.fOH), oh = f - n * g.OH;
-            const int w0 = sgi * g.SEG;
-            const int len = min(g.SEG, g.OW - w0);
-            dzb = dz + ((int64_t)f * g.OW + w0) * g.OC + oc0;
-            dz_bytes = (uint32_t)(len * g.OC * 2 - oc0 * 2);
-            const int ih = oh + kh - g.ph;
-            if ((unsigned)ih < (unsigned)g.H) {
-                xb = x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0;
-                x_bytes = (uint32_t)(g.W * g.IC * 2 - ic0 * 2);
-            }
-            xo = (w0 - g.pw) * g.IC * 2;
-        }
-        dzr = make_rsrc(dzb, dz_bytes);
-        xr = make_rsrc(xb, x_bytes);
-    };
-    auto segs_of = [&](int st) {
-        Segs sg;
-        const int gr = (s_begin + st) * g.RS;
-        sg.slot = smem_base + (uint32_t)((st & 1) * stage_bytes);
-        one_seg(gr, sg.dz0, sg.x0, sg.xo0);
-        one_seg(g.RS == 2 ? gr + 1 : g.G, sg.dz1, sg.x1, sg.xo1);
-        return sg;
-    };
-    // issue this wave's copy instructions i0 .. i1-1 of a stage
-    auto issue = [&](const Segs& sg, int i0, int i1) {
-        for (int i = i0; i < i1; ++i) {
-            const int j = wid + NW * i;
-            if (j < NA) {
-                const bool r = RPI * j >= g.SEGp;
-                const int row = RPI * j - (r ? g.SEGp : 0);
-                dma16_buf(lane_dz + (uint32_t)(row * (g.OC * 2)), r ? sg.dz1 : sg.dz0,
-                          __builtin_amdgcn_readfirstlane(sg.slot + j * 1024));
-            } else {
-                const int jb = j - NA;
-                const bool r = RPI * jb >= g.XWp;
-                const int row = RPI * jb - (r ? g.XWp : 0);
-                dma16_buf(lane_x + (uint32_t)(row * (g.IC * 2) + (r ? sg.xo1 : sg.xo0)), r ? sg.x1 : sg.x0,
-                          __builtin_amdgcn_readfirstlane(sg.slot + g.SPp * ROWB + jb * 1024));
-            }
-        }
-    };
+    const Dw3Copies<bf16, CH, NT> cp(g, x, dz, kh, oc0, ic0, s_begin, wid, lane, smem_base);
+    const int nmine = cp.nmine;
+    using Segs = typename Dw3Copies<bf16, CH, NT>::Segs;
+    auto segs_of = [&](int st) { return cp.segs_of(g, st); };
+    auto issue = [&](const Segs& sg, int i0, int i1) { cp.issue(g, sg, i0, i1); };
 
     const int wm = wid / WN, wn = wid % WN;
     floatx16 acc[TM][TN];
@@ -692,7 +714,7 @@ __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_
     const int l16 = lane & 15, hi = (lane >> 4) & 1, kb8 = 8 * (lane >> 5);
     auto lds_off = [&](int row, int c) {
         const int cb = 2 * (c + 16 * hi + 4 * (l16 & 3));
-        return row * ROWB + ((((cb >> 4) ^ sw3<CH>(row)) << 4) | (cb & 15));
+        return row * ROWB + ((((cb >> 4) ^ sw3<ROWB>(row)) << 4) | (cb & 15));
     };
     int a_off[TM][2], b_off[TN][2];
     int prow[2];
@@ -745,7 +767,7 @@ __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_
     for (int j = 0; j < 8; ++j) dbs[j] = 0.0f;
     auto db_sum = [&](const unsigned char* As) {
         for (int row = kh + g.KH * (t / CPR); row < g.SPp; row += RG * g.KH) {
-            const uint4 v = *(const uint4*)(As + row * ROWB + (((t % CPR) ^ sw3<CH>(row)) << 4));
+            const uint4 v = *(const uint4*)(As + row * ROWB + (((t % CPR) ^ sw3<ROWB>(row)) << 4));
             const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -814,6 +836,158 @@ __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_
         float* red = (float*)smem;  // [RG][CH]; the ring is no longer needed
 #pragma unroll
         for (int j = 0; j < 8; ++j) red[(t / CPR) * CH + (t % CPR) * 8 + j] = dbs[j];
+        __syncthreads();
+        if (t < CH) {
+            float s_ = 0.0f;
+            for (int q = 0; q < RG; ++q) s_ += red[q * CH + t];
+            part_db[((int64_t)slab * g.KH + kh) * g.OC + oc0 + t] = s_;
+        }
+    }
+}
+
+// fp32 variant of the stride-1 weight-gradient kernel: 64-channel tiles (256-byte LDS
+// rows, the same stage copies), four waves of 64 oc x KW*16 columns, two workgroups per
+// CU.  v_mfma_f32_16x16x4_f32 takes 4 positions per k-step with one fp32 value of each
+// operand per lane (A: channel l%16 at position l/16; B likewise), so the operands are
+// read from the natural position-major tiles with plain 4-byte LDS reads; the row
+// swizzle keeps the four positions a read touches in different banks.
+template <int KW_, int NK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw3f_kernel(
+    const float* __restrict__ x, const float* __restrict__ dz, Dw3Geom g, float* __restrict__ part,
+    float* __restrict__ part_db, int want_db) {
+    constexpr int CH = 64, NT = 256, ROWB = 256, CPR = 16;
+    constexpr int TM = 4, TN = KW_;  // wave tile 64 oc x KW*16 columns (waves 1 x 4)
+    extern __shared__ __align__(1024) unsigned char smem[];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int stage_bytes = (g.SPp + g.XR) * ROWB;
+    const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+    const int lin = xcd_tile(blockIdx.x, gridDim.x);
+    const int slab = lin / g.tiles, tile = lin - slab * g.tiles;
+    const int oct_i = tile % g.oct, r1 = tile / g.oct;
+    const int ict_i = r1 % g.ict, kh = r1 / g.ict;
+    const int oc0 = oct_i * CH, ic0 = ict_i * CH;
+    const int s_begin = slab * g.spb;
+    const int s_end = min(g.nst, s_begin + g.spb);
+    const int KT = s_end - s_begin;
+    const bool do_db = want_db && ict_i == 0;
+
+    const Dw3Copies<float, CH, NT> cp(g, x, dz, kh, oc0, ic0, s_begin, wid, lane, smem_base);
+    const int nmine = cp.nmine;
+
+    floatx4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Lane l reads position kq = l/16 of the k-step and channel c16 = l%16 of its fragment.
+    // k-steps start at multiples of 4 positions, so a read's row is kk + kq (+ the tap)
+    // and its swizzle depends on kq (+ the tap) only: offsets are per-lane constants plus
+    // kk*ROWB (plus the second-segment shift, a multiple of 4 rows, uniform per k-step
+    // since segments start at multiples of 4).
+    const int kq = lane >> 4, c16 = lane & 15;
+    auto lds_off = [&](int row, int c) {  // byte offset of channel c in LDS row `row`
+        return row * ROWB + ((((c >> 2) ^ sw3<ROWB>(row)) << 4) | ((c & 3) << 2));
+    };
+    int a_off[TM], b_off[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a_off[i] = lds_off(kq, i * 16 + c16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int col = wid * KW_ * 16 + j * 16;  // tap col/64, input channel col%64
+        b_off[j] = lds_off(kq + col / CH, col % CH + c16);
+    }
+    const int seg_shift = (g.XWp - g.SEGp) * ROWB;
+    auto read_frags = [&](const unsigned char* As, const unsigned char* Xs, int kk, float (&af)[TM],
+                          float (&bf)[TN]) {
+        const unsigned char* Ak = As + kk * ROWB;
+        const unsigned char* Xk = Xs + kk * ROWB + (kk >= g.SEGp ? seg_shift : 0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = *(const float*)(Ak + a_off[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[j] = *(const float*)(Xk + b_off[j]);
+    };
+    auto mfmas = [&](const float (&af)[TM], const float (&bf)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+
+    // Column sums of dz for the bias gradient: thread t owns chunk t%CPR (4 channels) of
+    // rows kh + KH*(t/CPR), kh + KH*(t/CPR + RG), ...
+    constexpr int RG = NT / CPR;
+    float dbs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto db_sum = [&](const unsigned char* As) {
+        for (int row = kh + g.KH * (t / CPR); row < g.SPp; row += RG * g.KH) {
+            const float4 v = *(const float4*)(As + row * ROWB + (((t % CPR) ^ sw3<ROWB>(row)) << 4));
+            dbs[0] += v.x;
+            dbs[1] += v.y;
+            dbs[2] += v.z;
+            dbs[3] += v.w;
+        }
+    };
+
+    // Stage k: the copies of stage k + 1 go out in slices over the first k-steps of stage
+    // k; the reads of k-step kk + 4 are issued before the MFMAs of kk.
+    const int nk = NK > 0 ? NK : g.SPp / 4;
+    const int spread = nk > 4 ? 4 : nk;
+    if (KT > 0) cp.issue(g, cp.segs_of(g, 0), 0, nmine);
+    for (int k = 0; k < KT; ++k) {
+        wait_dma(0);
+        __syncthreads();
+        const bool next = k + 1 < KT;
+        const typename Dw3Copies<float, CH, NT>::Segs sg = cp.segs_of(g, next ? k + 1 : k);
+        const unsigned char* As = smem + (k & 1) * stage_bytes;
+        const unsigned char* Xs = As + g.SPp * ROWB;
+        if (do_db) db_sum(As);
+        float fa[2][TM], fb[2][TN];
+        read_frags(As, Xs, 0, fa[0], fb[0]);
+        if constexpr (NK > 0) {
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                if (kk + 1 < NK) read_frags(As, Xs, (kk + 1) * 4, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                mfmas(fa[kk & 1], fb[kk & 1]);
+                if (next && kk < spread) cp.issue(g, sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+            }
+        } else {
+            int kk = 0;
+            for (; kk + 1 < nk; kk += 2) {
+                read_frags(As, Xs, (kk + 1) * 4, fa[1], fb[1]);
+                mfmas(fa[0], fb[0]);
+                if (next && kk < spread) cp.issue(g, sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+                if (kk + 2 < nk) read_frags(As, Xs, (kk + 2) * 4, fa[0], fb[0]);
+                mfmas(fa[1], fb[1]);
+                if (next && kk + 1 < spread) cp.issue(g, sg, (kk + 1) * nmine / spread, (kk + 2) * nmine / spread);
+            }
+            if (kk < nk) {
+                mfmas(fa[0], fb[0]);
+                if (next && kk < spread) cp.issue(g, sg, kk * nmine / spread, nmine);
+            }
+        }
+    }
+
+    // partial tile: row (oc) 4*(lane/16) + e of fragment i, column lane%16 of fragment j
+    float* dst = part + (int64_t)slab * g.OC * g.Kdim;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = wid * KW_ * 16 + j * 16;
+            const int k = (kh * g.KW + col / CH) * g.IC + ic0 + col % CH + c16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int oc = oc0 + i * 16 + 4 * kq + e;
+                dst[(int64_t)oc * g.Kdim + k] = acc[i][j][e];
+            }
+        }
+    if (do_db) {  // uniform per workgroup
+        __syncthreads();
+        float* red = (float*)smem;  // [RG][CH]; the ring is no longer needed
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[(t / CPR) * CH + (t % CPR) * 4 + j] = dbs[j];
         __syncthreads();
         if (t < CH) {
             float s_ = 0.0f;
@@ -969,22 +1143,29 @@ int dw3_ch(int dt, const ConvDims& d) {
     return 0;
 }
 bool dw3_ok(int dt, const ConvDims& d) { return dw3_ch(dt, d) != 0; }
+// fp32 stride-1 layers with 64-channel multiples and kernels at most 3 wide.
+bool dw3f_ok(int dt, const ConvDims& d) {
+    return dt == DT_F32 && d.sh == 1 && d.sw == 1 && d.KW >= 1 && d.KW <= 3 && d.OC % 64 == 0 && d.IC % 64 == 0;
+}
 
-// Stage geometry.  128 channels: two whole output rows when they fit in 128 positions,
-// else one row split into equal segments of at most 128; about one workgroup per CU.
-// 64 channels: two segments of at most 32 positions (or two whole rows of at most 32);
-// about four workgroups per CU.  Segment starts are aligned to a copy's rows.
-Dw3Geom plan3(const ConvDims& d, int ch) {
+// Stage geometry.  bf16, 128 channels: two whole output rows when they fit in 128
+// positions, else one row split into equal segments of at most 128; about one workgroup
+// per CU.  bf16, 64 channels: two segments of at most 32 positions (or two whole rows of
+// at most 32); about four workgroups per CU.  fp32 (64 channels, 256-byte rows): two
+// whole rows when they fit in 64 positions, else one segment of at most 64; about two
+// workgroups per CU.  Segment starts are aligned to a copy's rows.
+Dw3Geom plan3(const ConvDims& d, int ch, int es = 2) {
     Dw3Geom g;
     g.N = d.N; g.H = d.H; g.W = d.W; g.IC = d.IC; g.OC = d.OC; g.KH = d.KH; g.KW = d.KW;
     g.OH = d.OH; g.OW = d.OW; g.ph = d.ph; g.pw = d.pw;
-    const int seg_max = ch == 128 ? 128 : 32, rpi = 1024 / (2 * ch);
-    if (2 * d.OW <= (ch == 128 ? 128 : 64)) {
+    const bool f32 = es == 4;
+    const int seg_max = f32 ? 64 : (ch == 128 ? 128 : 32), rpi = 1024 / (es * ch);
+    if (2 * d.OW <= (f32 ? 64 : (ch == 128 ? 128 : 64))) {
         g.RS = 2;
         g.nseg = 1;
         g.SEG = d.OW;
     } else {
-        g.RS = ch == 128 ? 1 : 2;
+        g.RS = (ch == 128 || f32) ? 1 : 2;
         g.nseg = (int)ceil_div(d.OW, seg_max);
         g.SEG = (int)ceil_div(d.OW, g.nseg);
     }
@@ -1000,7 +1181,7 @@ Dw3Geom plan3(const ConvDims& d, int ch) {
     g.ict = d.IC / ch;
     g.oct = d.OC / ch;
     g.tiles = d.KH * g.ict * g.oct;
-    int S = (ch == 128 ? 256 : 1024) / g.tiles;
+    int S = (f32 ? 512 : (ch == 128 ? 256 : 1024)) / g.tiles;
     if (S < 1) S = 1;
     if (S > g.nst) S = g.nst;
     g.spb = (int)ceil_div(g.nst, S);
@@ -1011,7 +1192,7 @@ Dw3Geom plan3(const ConvDims& d, int ch) {
     return g;
 }
 
-size_t dw3_lds(const Dw3Geom& g, int ch) { return (size_t)2 * (g.SPp + g.XR) * 2 * ch; }
+size_t dw3_lds(const Dw3Geom& g, int ch, int es = 2) { return (size_t)2 * (g.SPp + g.XR) * es * ch; }
 
 template <int CH, int KW_, int NK>
 hipError_t launch_dw3_kw(const bf16* x, const bf16* dz, const Dw3Geom& g, float* part, float* part_db, int want_db,
@@ -1029,6 +1210,22 @@ hipError_t launch_dw3_kw(const bf16* x, const bf16* dz, const Dw3Geom& g, float*
     return hipGetLastError();
 }
 
+template <int KW_, int NK>
+hipError_t launch_dw3f_kw(const float* x, const float* dz, const Dw3Geom& g, float* part, float* part_db,
+                          int want_db, hipStream_t s) {
+    auto kern = dw3f_kernel<KW_, NK>;
+    static bool raised = false;  // the dynamic LDS limit is raised once per instantiation
+    if (!raised) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 160 * 1024);
+        if (e != hipSuccess) return e;
+        raised = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(g.S * g.tiles)), dim3(256), dw3_lds(g, 64, 4), s, x, dz, g, part,
+                       part_db, want_db);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool igemm_dw_supported(int dt, const ConvDims& d) {
@@ -1037,8 +1234,8 @@ bool igemm_dw_supported(int dt, const ConvDims& d) {
 }
 
 size_t igemm_dw_ws_bytes(int dt, const ConvDims& d) {
-    const bool s1 = dw3_ok(dt, d);
-    const int S = s1 ? plan3(d, dw3_ch(dt, d)).S : plan(dt, d).S;
+    const bool s1 = dw3_ok(dt, d) || dw3f_ok(dt, d);
+    const int S = dw3_ok(dt, d) ? plan3(d, dw3_ch(dt, d)).S : dw3f_ok(dt, d) ? plan3(d, 64, 4).S : plan(dt, d).S;
     const int Sdb = s1 ? S * d.KH : S;  // bias partials: one per slab (and kernel row)
     const size_t Kdim = (size_t)d.KH * d.KW * d.IC;
     return align_up((size_t)S * d.OC * Kdim * 4, 256) + align_up((size_t)Sdb * d.OC * 4, 256);
@@ -1046,6 +1243,23 @@ size_t igemm_dw_ws_bytes(int dt, const ConvDims& d) {
 
 hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, float* db, int accumulate,
                            const ConvDims& d, void* ws, hipStream_t s) {
+    if (dw3f_ok(dt, d)) {
+        const Dw3Geom g = plan3(d, 64, 4);
+        float* part = (float*)ws;
+        float* part_db = (float*)((char*)ws + align_up((size_t)g.S * d.OC * g.Kdim * 4, 256));
+        const int want_db = db != nullptr;
+        const float *xf = (const float*)x, *zf = (const float*)dz;
+        hipError_t e;
+        if (d.KW == 3 && g.SPp == 64) e = launch_dw3f_kw<3, 16>(xf, zf, g, part, part_db, want_db, s);
+        else if (d.KW == 3) e = launch_dw3f_kw<3, 0>(xf, zf, g, part, part_db, want_db, s);
+        else if (d.KW == 2) e = launch_dw3f_kw<2, 0>(xf, zf, g, part, part_db, want_db, s);
+        else e = launch_dw3f_kw<1, 0>(xf, zf, g, part, part_db, want_db, s);
+        if (e != hipSuccess) return e;
+        const int64_t count = (int64_t)d.OC * g.Kdim;
+        dw_reduce4<<<reduce_grid(count, d.OC, db != nullptr), NT, 0, s>>>(part, part_db, dw, db, count, d.OC, g.S,
+                                                                          g.S * g.KH, accumulate);
+        return hipGetLastError();
+    }
     if (dw3_ok(dt, d)) {
         const int ch = dw3_ch(dt, d);
         const Dw3Geom g = plan3(d, ch);
