@@ -1143,9 +1143,12 @@ int dw3_ch(int dt, const ConvDims& d) {
     return 0;
 }
 bool dw3_ok(int dt, const ConvDims& d) { return dw3_ch(dt, d) != 0; }
-// fp32 stride-1 layers with 64-channel multiples and kernels at most 3 wide.
+// fp32 stride-1 layers with 64-channel multiples and kernels at most 3 wide, on output
+// rows of at least 16 positions (shorter rows leave most of a 16-position stage padding;
+// the per-tap kernel is faster there: c2c's 7-wide rows).
 bool dw3f_ok(int dt, const ConvDims& d) {
-    return dt == DT_F32 && d.sh == 1 && d.sw == 1 && d.KW >= 1 && d.KW <= 3 && d.OC % 64 == 0 && d.IC % 64 == 0;
+    return dt == DT_F32 && d.sh == 1 && d.sw == 1 && d.KW >= 1 && d.KW <= 3 && d.OC % 64 == 0 && d.IC % 64 == 0 &&
+           d.OW >= 16;
 }
 
 // Stage geometry.  bf16, 128 channels: two whole output rows when they fit in 128

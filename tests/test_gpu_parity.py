@@ -77,7 +77,7 @@ MEDIUM = [
     # stages, two channel tiles on either side, 1-3 taps wide
     ((2, 10, 80, 64, 64, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_RELU),
     ((3, 12, 20, 64, 128, 2, 3, 1, 1, 0, 1), WL.F32, WL.ACT_TANH),
-    ((2, 7, 9, 128, 64, 3, 1, 1, 1, 1, 0), WL.F32, WL.ACT_IDENTITY),
+    ((2, 7, 20, 128, 64, 3, 1, 1, 1, 1, 0), WL.F32, WL.ACT_IDENTITY),
     ((2, 6, 30, 64, 64, 1, 2, 1, 1, 0, 0), WL.F32, WL.ACT_SIGMOID),
 ]
 
