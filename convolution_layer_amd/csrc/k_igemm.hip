@@ -536,6 +536,10 @@ template <typename T, int SIGN, int ACT, class Out>
 hipError_t launch2_any(const T* A, const GatherGeom& g, const T* B, int Nn, int Kb, const Out& out,
                        hipStream_t s) {
     const int bn = pick_bn(Nn);
+    // fp32 grids of fewer 112-row tiles than CUs (small images, few channels): 32-row
+    // tiles spread the work over every CU (measured 33 -> 22 us on 256 x 7x7x64 outputs).
+    if (sizeof(T) == 4 && bn == 64 && ceil_div(g.M, 112) * ceil_div(Nn, 64) < 256)
+        return launch2_cfg<T, 32, 64, 2, 2, SIGN, ACT, Out>(A, g, B, Nn, Kb, out, s);
     if (bn == 128) {
         const double c128 = tile_cost(g.M, Nn, 128, 128, lds2(128, 128), 1.0);
         const double c112 = tile_cost(g.M, Nn, 112, 128, lds2(112, 128), 0.97);
