@@ -570,7 +570,7 @@ template <int ROWB> __device__ __forceinline__ int sw3(int row) {
 // Stage copies of the stride-1 weight-gradient kernels, for tiles of CH channels of T
 // (LDS rows of ROWB = CH*sizeof(T) bytes, RPI rows per 1-KB copy) and NT threads.
 // Copy instructions of a stage: NA for dz (RPI LDS rows each), then NB for the input
-// rows; wave w issues instructions w, w + NW, ...  Lane l copies 16-byte chunk l%CPR of
+// rows; each wave issues a contiguous block of them.  Lane l copies 16-byte chunk l%CPR of
 // row RPI*j + l/CPR; the swizzle of that row depends on l/CPR only.  Segment r of a
 // stage (RS <= 2 of them) holds its dz rows at LDS rows r*SEGp + q and its input row at
 // LDS rows r*XWp + c (c = input column + pw - w0); a copy never spans two segments.
@@ -589,40 +589,62 @@ template <typename T, int CH, int NT> struct Dw3Copies {
     };
     const T* x;
     const T* dz;
-    int kh, oc0, ic0, s_begin, wid, NA, NB, nmine, stage_bytes;
+    // A stage's copies c = 0 .. NA+NB-1 land at LDS byte c*1024 of its slot and form four
+    // streams: dz rows of segment 0 [0, A0), of segment 1 [A0, NA), input rows of segment
+    // 0 [NA, NA+B0), of segment 1 [NA+B0, NA+NB).  Wave w issues the contiguous block
+    // [c_lo, c_lo + nmine), so it touches one or two streams and picks each stream's
+    // buffer once per stage, not once per copy.
+    int kh, oc0, ic0, s_begin, NA, NB, A0, B0, c_lo, nmine, stage_bytes;
+    bool use_dz0, use_dz1, use_x0, use_x1;
     uint32_t lane_dz, lane_x, smem_base;
 
     __device__ __forceinline__ Dw3Copies(const Dw3Geom& g, const T* x_, const T* dz_, int kh_, int oc0_, int ic0_,
-                                         int s_begin_, int wid_, int lane, uint32_t smem_base_)
-        : x(x_), dz(dz_), kh(kh_), oc0(oc0_), ic0(ic0_), s_begin(s_begin_), wid(wid_), smem_base(smem_base_) {
+                                         int s_begin_, int wid, int lane, uint32_t smem_base_)
+        : x(x_), dz(dz_), kh(kh_), oc0(oc0_), ic0(ic0_), s_begin(s_begin_), smem_base(smem_base_) {
         NA = g.SPp / RPI;
         NB = g.XR / RPI;
-        nmine = (NA + NB - wid + NW - 1) / NW;  // instructions of this wave per stage
+        A0 = g.SEGp / RPI;  // SEGp and XWp are multiples of RPI, SEGp <= SPp, XWp <= XR
+        B0 = g.XWp / RPI;
+        const int total = NA + NB, per = (total + NW - 1) / NW;
+        c_lo = wid * per;
+        const int c_hi = min(total, c_lo + per);
+        nmine = c_hi > c_lo ? c_hi - c_lo : 0;
+        auto touches = [&](int lo, int hi) { return max(c_lo, lo) < min(c_hi, hi); };
+        use_dz0 = touches(0, A0);
+        use_dz1 = touches(A0, NA);
+        use_x0 = touches(NA, NA + B0);
+        use_x1 = touches(NA + B0, total);
         stage_bytes = (g.SPp + g.XR) * ROWB;
         const int rsub = lane / CPR;
         const int choff = ((lane % CPR) ^ sw3<ROWB>(rsub)) * 16;  // source byte offset of the chunk
         lane_dz = rsub * (g.OC * ES) + choff;
         lane_x = rsub * (g.IC * ES) + choff;
     }
-    __device__ __forceinline__ void one_seg(const Dw3Geom& g, int gr, dma_rsrc& dzr, dma_rsrc& xr, int& xo) const {
+    // Buffers of segment gr (none past the last segment: every copy reads zeros).
+    __device__ __forceinline__ void one_seg(const Dw3Geom& g, int gr, bool want_dz, bool want_x, dma_rsrc& dzr,
+                                            dma_rsrc& xr, int& xo) const {
         const T* dzb = dz;
         const T* xb = x;
         uint32_t dz_bytes = 0, x_bytes = 0;
         xo = 0;
-        if (gr < g.G) {
+        if (gr < g.G && (want_dz || want_x)) {
             const int f = fdiv(gr, g.fnseg);
             const int sgi = gr - f * g.nseg;
-            const int n = fdiv(f, g.fOH), oh = f - n * g.OH;
             const int w0 = sgi * g.SEG;
-            const int len = min(g.SEG, g.OW - w0);
-            dzb = dz + ((int64_t)f * g.OW + w0) * g.OC + oc0;
-            dz_bytes = (uint32_t)((len * g.OC - oc0) * ES);
-            const int ih = oh + kh - g.ph;
-            if ((unsigned)ih < (unsigned)g.H) {
-                xb = x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0;
-                x_bytes = (uint32_t)((g.W * g.IC - ic0) * ES);
+            if (want_dz) {
+                const int len = min(g.SEG, g.OW - w0);
+                dzb = dz + ((int64_t)f * g.OW + w0) * g.OC + oc0;
+                dz_bytes = (uint32_t)((len * g.OC - oc0) * ES);
             }
-            xo = (w0 - g.pw) * g.IC * ES;
+            if (want_x) {
+                const int n = fdiv(f, g.fOH), oh = f - n * g.OH;
+                const int ih = oh + kh - g.ph;
+                if ((unsigned)ih < (unsigned)g.H) {
+                    xb = x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0;
+                    x_bytes = (uint32_t)((g.W * g.IC - ic0) * ES);
+                }
+                xo = (w0 - g.pw) * g.IC * ES;
+            }
         }
         dzr = make_rsrc(dzb, dz_bytes);
         xr = make_rsrc(xb, x_bytes);
@@ -631,27 +653,28 @@ template <typename T, int CH, int NT> struct Dw3Copies {
         Segs sg;
         const int gr = (s_begin + st) * g.RS;
         sg.slot = smem_base + (uint32_t)((st & 1) * stage_bytes);
-        one_seg(g, gr, sg.dz0, sg.x0, sg.xo0);
-        one_seg(g, g.RS == 2 ? gr + 1 : g.G, sg.dz1, sg.x1, sg.xo1);
+        one_seg(g, gr, use_dz0, use_x0, sg.dz0, sg.x0, sg.xo0);
+        one_seg(g, g.RS == 2 ? gr + 1 : g.G, use_dz1, use_x1, sg.dz1, sg.x1, sg.xo1);
         return sg;
+    }
+    // Copies [a, b) that fall in the stream [lo, hi): row RPI*(c - lo) of the stream's
+    // buffer, `stride` bytes per row, shifted by xo.
+    __device__ __forceinline__ void stream(dma_rsrc rs, int a, int b, int lo, int hi, uint32_t lane, int stride,
+                                           int xo, uint32_t slot) const {
+        const int c0 = max(a, lo), c1 = min(b, hi);
+        uint32_t voff = lane + (uint32_t)(RPI * (c0 - lo) * stride + xo);
+        for (int c = c0; c < c1; ++c) {
+            dma16_buf(voff, rs, __builtin_amdgcn_readfirstlane(slot + (uint32_t)c * 1024u));
+            voff += (uint32_t)(RPI * stride);
+        }
     }
     // this wave's copy instructions i0 .. i1-1 of a stage
     __device__ __forceinline__ void issue(const Dw3Geom& g, const Segs& sg, int i0, int i1) const {
-        for (int i = i0; i < i1; ++i) {
-            const int j = wid + NW * i;
-            if (j < NA) {
-                const bool r = RPI * j >= g.SEGp;
-                const int row = RPI * j - (r ? g.SEGp : 0);
-                dma16_buf(lane_dz + (uint32_t)(row * (g.OC * ES)), r ? sg.dz1 : sg.dz0,
-                          __builtin_amdgcn_readfirstlane(sg.slot + j * 1024));
-            } else {
-                const int jb = j - NA;
-                const bool r = RPI * jb >= g.XWp;
-                const int row = RPI * jb - (r ? g.XWp : 0);
-                dma16_buf(lane_x + (uint32_t)(row * (g.IC * ES) + (r ? sg.xo1 : sg.xo0)), r ? sg.x1 : sg.x0,
-                          __builtin_amdgcn_readfirstlane(sg.slot + g.SPp * ROWB + jb * 1024));
-            }
-        }
+        const int a = c_lo + i0, b = c_lo + i1;
+        if (use_dz0) stream(sg.dz0, a, b, 0, A0, lane_dz, g.OC * ES, 0, sg.slot);
+        if (use_dz1) stream(sg.dz1, a, b, A0, NA, lane_dz, g.OC * ES, 0, sg.slot);
+        if (use_x0) stream(sg.x0, a, b, NA, NA + B0, lane_x, g.IC * ES, sg.xo0, sg.slot);
+        if (use_x1) stream(sg.x1, a, b, NA + B0, NA + NB, lane_x, g.IC * ES, sg.xo1, sg.slot);
     }
 };
 
