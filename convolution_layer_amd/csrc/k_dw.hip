@@ -570,7 +570,7 @@ template <int ROWB> __device__ __forceinline__ int sw3(int row) {
 // Stage copies of the stride-1 weight-gradient kernels, for tiles of CH channels of T
 // (LDS rows of ROWB = CH*sizeof(T) bytes, RPI rows per 1-KB copy) and NT threads.
 // Copy instructions of a stage: NA for dz (RPI LDS rows each), then NB for the input
-// rows; each wave issues a contiguous block of them.  Lane l copies 16-byte chunk l%CPR of
+// rows, split into per-segment streams (below).  Lane l copies 16-byte chunk l%CPR of
 // row RPI*j + l/CPR; the swizzle of that row depends on l/CPR only.  Segment r of a
 // stage (RS <= 2 of them) holds its dz rows at LDS rows r*SEGp + q and its input row at
 // LDS rows r*XWp + c (c = input column + pw - w0); a copy never spans two segments.
@@ -580,101 +580,102 @@ template <int ROWB> __device__ __forceinline__ int sw3(int row) {
 // buffer) all read as zeros.
 template <typename T, int CH, int NT> struct Dw3Copies {
     static constexpr int ES = (int)sizeof(T), ROWB = CH * ES, CPR = ROWB / 16, RPI = 1024 / ROWB, NW = NT / 64;
-    // Buffers of the stage being copied (uniform per workgroup); fields are separate
-    // scalars, selected by value, so nothing is indexed at run time.
+    // A stage's copies c = 0 .. NA+NB-1 land at LDS byte c*1024 of its slot and form four
+    // streams: k = 0 the dz rows of segment 0 ([0, A0)), 1 those of segment 1 ([A0, NA)),
+    // 2 the input row of segment 0 ([NA, NA+B0)), 3 that of segment 1 ([NA+B0, NA+NB)).
+    // With four or more waves, wave w copies part w/4 of stream w%4; with two, wave w
+    // copies streams w and w+2 (both of segment w).  Either way a wave needs the geometry
+    // of one segment and one or two buffer descriptors per stage, which keeps the scalar
+    // work and registers of the copies small next to the MFMA loop.
+    static_assert(NW == 2 || NW % 4 == 0, "two waves or a multiple of four");
+    static constexpr int SPW = NW >= 4 ? 1 : 2;  // streams per wave
     struct Segs {
-        dma_rsrc dz0, dz1, x0, x1;
-        int xo0, xo1;  // byte offset of the segment's LDS input row 0 from its buffer: (w0 - pw)*IC*ES
+        dma_rsrc rs[SPW];
+        int xo;  // byte offset of the segment's LDS input row 0 from its buffer: (w0 - pw)*IC*ES
         uint32_t slot;
     };
     const T* x;
     const T* dz;
-    // A stage's copies c = 0 .. NA+NB-1 land at LDS byte c*1024 of its slot and form four
-    // streams: dz rows of segment 0 [0, A0), of segment 1 [A0, NA), input rows of segment
-    // 0 [NA, NA+B0), of segment 1 [NA+B0, NA+NB).  Wave w issues the contiguous block
-    // [c_lo, c_lo + nmine), so it touches one or two streams and picks each stream's
-    // buffer once per stage, not once per copy.
-    int kh, oc0, ic0, s_begin, NA, NB, A0, B0, c_lo, nmine, stage_bytes;
-    bool use_dz0, use_dz1, use_x0, use_x1;
-    uint32_t lane_dz, lane_x, smem_base;
+    int kh, oc0, ic0, s_begin, seg, nmine, stage_bytes;
+    int kind[SPW], c_lo[SPW], c_hi[SPW], row_lo[SPW];  // stream, copy range, row of its first copy
+    uint32_t lane_off[SPW];                             // per-lane source offset of the stream's row 0
+    int stride[SPW];                                    // source bytes per row
 
     __device__ __forceinline__ Dw3Copies(const Dw3Geom& g, const T* x_, const T* dz_, int kh_, int oc0_, int ic0_,
-                                         int s_begin_, int wid, int lane, uint32_t smem_base_)
-        : x(x_), dz(dz_), kh(kh_), oc0(oc0_), ic0(ic0_), s_begin(s_begin_), smem_base(smem_base_) {
-        NA = g.SPp / RPI;
-        NB = g.XR / RPI;
-        A0 = g.SEGp / RPI;  // SEGp and XWp are multiples of RPI, SEGp <= SPp, XWp <= XR
-        B0 = g.XWp / RPI;
-        const int total = NA + NB, per = (total + NW - 1) / NW;
-        c_lo = wid * per;
-        const int c_hi = min(total, c_lo + per);
-        nmine = c_hi > c_lo ? c_hi - c_lo : 0;
-        auto touches = [&](int lo, int hi) { return max(c_lo, lo) < min(c_hi, hi); };
-        use_dz0 = touches(0, A0);
-        use_dz1 = touches(A0, NA);
-        use_x0 = touches(NA, NA + B0);
-        use_x1 = touches(NA + B0, total);
-        stage_bytes = (g.SPp + g.XR) * ROWB;
+                                         int s_begin_, int wid, int lane, uint32_t smem_base)
+        : x(x_), dz(dz_), kh(kh_), oc0(oc0_), ic0(ic0_), s_begin(s_begin_) {
+        const int NA = g.SPp / RPI, NB = g.XR / RPI;
+        const int A0 = g.SEGp / RPI, B0 = g.XWp / RPI;  // SEGp <= SPp, XWp <= XR, multiples of RPI
+        const int lo[4] = {0, A0, NA, NA + B0}, hi[4] = {A0, NA, NA + B0, NA + NB};
         const int rsub = lane / CPR;
         const int choff = ((lane % CPR) ^ sw3<ROWB>(rsub)) * 16;  // source byte offset of the chunk
-        lane_dz = rsub * (g.OC * ES) + choff;
-        lane_x = rsub * (g.IC * ES) + choff;
+        stage_bytes = (g.SPp + g.XR) * ROWB;
+        nmine = 0;
+        seg = NW >= 4 ? (wid & 1) : wid;
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) {
+            const int k = NW >= 4 ? (wid & 3) : wid + 2 * q;
+            const int parts = NW >= 4 ? NW / 4 : 1, part = NW >= 4 ? wid / 4 : 0;
+            const int per = (hi[k] - lo[k] + parts - 1) / parts;
+            kind[q] = k;
+            c_lo[q] = min(hi[k], lo[k] + part * per);
+            c_hi[q] = min(hi[k], c_lo[q] + per);
+            row_lo[q] = RPI * (c_lo[q] - lo[k]);
+            const bool is_x = k >= 2;
+            stride[q] = (is_x ? g.IC : g.OC) * ES;
+            lane_off[q] = (uint32_t)(rsub * stride[q] + choff);
+            nmine += c_hi[q] - c_lo[q];
+        }
+        smem_base_ = smem_base;
     }
-    // Buffers of segment gr (none past the last segment: every copy reads zeros).
-    __device__ __forceinline__ void one_seg(const Dw3Geom& g, int gr, bool want_dz, bool want_x, dma_rsrc& dzr,
-                                            dma_rsrc& xr, int& xo) const {
-        const T* dzb = dz;
-        const T* xb = x;
-        uint32_t dz_bytes = 0, x_bytes = 0;
-        xo = 0;
-        if (gr < g.G && (want_dz || want_x)) {
-            const int f = fdiv(gr, g.fnseg);
-            const int sgi = gr - f * g.nseg;
-            const int w0 = sgi * g.SEG;
-            if (want_dz) {
+    uint32_t smem_base_;
+    __device__ __forceinline__ Segs segs_of(const Dw3Geom& g, int st) const {
+        Segs sg;
+        sg.slot = smem_base_ + (uint32_t)((st & 1) * stage_bytes);
+        sg.xo = 0;
+        // this wave's segment of the stage; none (every copy reads zeros) past the last one
+        const int gr = seg == 0 || g.RS == 2 ? (s_begin + st) * g.RS + seg : g.G;
+        int f = 0, w0 = 0;
+        const bool valid = gr < g.G;
+        if (valid) {
+            f = fdiv(gr, g.fnseg);
+            w0 = (gr - f * g.nseg) * g.SEG;
+        }
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) {
+            const T* b = kind[q] >= 2 ? x : dz;
+            uint32_t bytes = 0;
+            if (valid && kind[q] < 2) {
                 const int len = min(g.SEG, g.OW - w0);
-                dzb = dz + ((int64_t)f * g.OW + w0) * g.OC + oc0;
-                dz_bytes = (uint32_t)((len * g.OC - oc0) * ES);
-            }
-            if (want_x) {
+                b = dz + ((int64_t)f * g.OW + w0) * g.OC + oc0;
+                bytes = (uint32_t)((len * g.OC - oc0) * ES);
+            } else if (valid) {
                 const int n = fdiv(f, g.fOH), oh = f - n * g.OH;
                 const int ih = oh + kh - g.ph;
                 if ((unsigned)ih < (unsigned)g.H) {
-                    xb = x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0;
-                    x_bytes = (uint32_t)((g.W * g.IC - ic0) * ES);
+                    b = x + ((int64_t)n * g.H + ih) * g.W * g.IC + ic0;
+                    bytes = (uint32_t)((g.W * g.IC - ic0) * ES);
                 }
-                xo = (w0 - g.pw) * g.IC * ES;
+                sg.xo = (w0 - g.pw) * g.IC * ES;
             }
+            sg.rs[q] = make_rsrc(b, bytes);
         }
-        dzr = make_rsrc(dzb, dz_bytes);
-        xr = make_rsrc(xb, x_bytes);
-    }
-    __device__ __forceinline__ Segs segs_of(const Dw3Geom& g, int st) const {
-        Segs sg;
-        const int gr = (s_begin + st) * g.RS;
-        sg.slot = smem_base + (uint32_t)((st & 1) * stage_bytes);
-        one_seg(g, gr, use_dz0, use_x0, sg.dz0, sg.x0, sg.xo0);
-        one_seg(g, g.RS == 2 ? gr + 1 : g.G, use_dz1, use_x1, sg.dz1, sg.x1, sg.xo1);
         return sg;
     }
-    // Copies [a, b) that fall in the stream [lo, hi): row RPI*(c - lo) of the stream's
-    // buffer, `stride` bytes per row, shifted by xo.
-    __device__ __forceinline__ void stream(dma_rsrc rs, int a, int b, int lo, int hi, uint32_t lane, int stride,
-                                           int xo, uint32_t slot) const {
-        const int c0 = max(a, lo), c1 = min(b, hi);
-        uint32_t voff = lane + (uint32_t)(RPI * (c0 - lo) * stride + xo);
-        for (int c = c0; c < c1; ++c) {
-            dma16_buf(voff, rs, __builtin_amdgcn_readfirstlane(slot + (uint32_t)c * 1024u));
-            voff += (uint32_t)(RPI * stride);
+    // this wave's copy instructions i0 .. i1-1 of a stage (counted over its streams in order)
+    __device__ __forceinline__ void issue(const Dw3Geom&, const Segs& sg, int i0, int i1) const {
+        int done = 0;
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) {
+            const int n = c_hi[q] - c_lo[q];
+            const int a = max(i0 - done, 0), b = min(i1 - done, n);
+            uint32_t voff = lane_off[q] + (uint32_t)((row_lo[q] + RPI * a) * stride[q] + (kind[q] >= 2 ? sg.xo : 0));
+            for (int i = a; i < b; ++i) {
+                dma16_buf(voff, sg.rs[q], __builtin_amdgcn_readfirstlane(sg.slot + (uint32_t)(c_lo[q] + i) * 1024u));
+                voff += (uint32_t)(RPI * stride[q]);
+            }
+            done += n;
         }
-    }
-    // this wave's copy instructions i0 .. i1-1 of a stage
-    __device__ __forceinline__ void issue(const Dw3Geom& g, const Segs& sg, int i0, int i1) const {
-        const int a = c_lo + i0, b = c_lo + i1;
-        if (use_dz0) stream(sg.dz0, a, b, 0, A0, lane_dz, g.OC * ES, 0, sg.slot);
-        if (use_dz1) stream(sg.dz1, a, b, A0, NA, lane_dz, g.OC * ES, 0, sg.slot);
-        if (use_x0) stream(sg.x0, a, b, NA, NA + B0, lane_x, g.IC * ES, sg.xo0, sg.slot);
-        if (use_x1) stream(sg.x1, a, b, NA + B0, NA + NB, lane_x, g.IC * ES, sg.xo1, sg.slot);
     }
 };
 
