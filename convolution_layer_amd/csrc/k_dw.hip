@@ -598,7 +598,7 @@ template <typename T, int CH, int NT> struct Dw3Copies {
     const T* dz;
     int kh, oc0, ic0, s_begin, seg, nmine, stage_bytes;
     int kind[SPW], c_lo[SPW], c_hi[SPW], row_lo[SPW];  // stream, copy range, row of its first copy
-    uint32_t lane_off[SPW];                             // per-lane source offset of the stream's row 0
+    uint32_t lane_off[SPW];                             // per-lane source offset of the first copy's row
     int stride[SPW];                                    // source bytes per row
 
     __device__ __forceinline__ Dw3Copies(const Dw3Geom& g, const T* x_, const T* dz_, int kh_, int oc0_, int ic0_,
@@ -621,9 +621,8 @@ template <typename T, int CH, int NT> struct Dw3Copies {
             c_lo[q] = min(hi[k], lo[k] + part * per);
             c_hi[q] = min(hi[k], c_lo[q] + per);
             row_lo[q] = RPI * (c_lo[q] - lo[k]);
-            const bool is_x = k >= 2;
-            stride[q] = (is_x ? g.IC : g.OC) * ES;
-            lane_off[q] = (uint32_t)(rsub * stride[q] + choff);
+            stride[q] = (k >= 2 ? g.IC : g.OC) * ES;
+            lane_off[q] = (uint32_t)(rsub * stride[q] + choff) + (uint32_t)(row_lo[q] * stride[q]);
             nmine += c_hi[q] - c_lo[q];
         }
         smem_base_ = smem_base;
@@ -643,9 +642,10 @@ template <typename T, int CH, int NT> struct Dw3Copies {
         }
 #pragma unroll
         for (int q = 0; q < SPW; ++q) {
-            const T* b = kind[q] >= 2 ? x : dz;
+            const bool is_x = SPW == 2 ? q == 1 : kind[q] >= 2;
+            const T* b = is_x ? x : dz;
             uint32_t bytes = 0;
-            if (valid && kind[q] < 2) {
+            if (valid && !is_x) {
                 const int len = min(g.SEG, g.OW - w0);
                 b = dz + ((int64_t)f * g.OW + w0) * g.OC + oc0;
                 bytes = (uint32_t)((len * g.OC - oc0) * ES);
@@ -667,9 +667,10 @@ template <typename T, int CH, int NT> struct Dw3Copies {
         int done = 0;
 #pragma unroll
         for (int q = 0; q < SPW; ++q) {
+            const bool is_x = SPW == 2 ? q == 1 : kind[q] >= 2;
             const int n = c_hi[q] - c_lo[q];
             const int a = max(i0 - done, 0), b = min(i1 - done, n);
-            uint32_t voff = lane_off[q] + (uint32_t)((row_lo[q] + RPI * a) * stride[q] + (kind[q] >= 2 ? sg.xo : 0));
+            uint32_t voff = lane_off[q] + (uint32_t)(RPI * a * stride[q] + (is_x ? sg.xo : 0));
             for (int i = a; i < b; ++i) {
                 dma16_buf(voff, sg.rs[q], __builtin_amdgcn_readfirstlane(sg.slot + (uint32_t)(c_lo[q] + i) * 1024u));
                 voff += (uint32_t)(RPI * stride[q]);
