@@ -692,32 +692,33 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     wait_dma(0);
     __syncthreads();
 
+    // Step st = (chunk c, tap (kh, kw)), advanced incrementally (no divisions per step).
+    int c = 0, kh = 0, kw = 0;
     auto step = [&](int st, const uint4 (&cur)[TN][KST], uint4 (&nxt)[TN][KST]) {
-        const int c = st / taps, tap = st - c * taps;
+        const int tap = kh * g.KW + kw;
         // Always issued (the last step reloads its own fragments): a load on only some
         // paths makes the compiler wait for it at the merge as if it were on every path,
         // which would stall each step on the next step's fragments.
         load_b(st + 1 < nsteps ? st + 1 : st, nxt);
-        const int kh = tap / g.KW, kw = tap - kh * g.KW;
         const int toff = g.sign > 0 ? kh * g.HQ + kw : (g.KH - 1 - kh) * g.HQ + (g.KW - 1 - kw);
-        const unsigned char* Hs = smem + (two ? (c & 1) : 0) * halo_bytes;
-        int pa[TM], ps[TM];
+        const int hbase = __builtin_amdgcn_readfirstlane((two ? (c & 1) : 0) * halo_bytes);
+        // LDS offset of the A fragment at k-step 0; the halo buffer and every 128-byte row
+        // start are 128-byte aligned, so k-step kk (chunk 2kk + lg = 2kk ^ lg) is the same
+        // offset XOR kk << 5.
+        uint32_t fo[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int p = hpos[i] + toff;
-            pa[i] = p * 128;
-            ps[i] = swz(p);
+            fo[i] = (uint32_t)(hbase + p * 128 + ((lg ^ swz(p)) << 4));
         }
         uint4 fa[2][TM];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[0][i] = *(const uint4*)(Hs + pa[i] + ((lg ^ ps[i]) << 4));
+        for (int i = 0; i < TM; ++i) fa[0][i] = *(const uint4*)(smem + fo[i]);
 #pragma unroll
         for (int kk = 0; kk < KST; ++kk) {
             if (kk + 1 < KST) {
-                const int lc = (kk + 1) * 2 + lg;
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    fa[(kk + 1) & 1][i] = *(const uint4*)(Hs + pa[i] + ((lc ^ ps[i]) << 4));
+                for (int i = 0; i < TM; ++i) fa[(kk + 1) & 1][i] = *(const uint4*)(smem + (fo[i] ^ ((kk + 1) << 5)));
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -735,6 +736,13 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
                 issue_halo(c + 1, 0, JH);
                 wait_dma(0);
                 __syncthreads();
+            }
+        }
+        if (++kw == g.KW) {
+            kw = 0;
+            if (++kh == g.KH) {
+                kh = 0;
+                ++c;
             }
         }
     };
