@@ -1057,7 +1057,7 @@ __global__ __launch_bounds__(NT) void dw_reduce4(const float* __restrict__ part,
     if ((int)blockIdx.x < nb_dw) {
         const int64_t i4 = (int64_t)blockIdx.x * 64 + o;
         float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i4 < n4) r = sum_strided<8>((const float4*)part + i4, n4, q, S);
+        if (i4 < n4) r = sum_strided<24>((const float4*)part + i4, n4, q, S);
         red[q][o] = r;
         __syncthreads();
         if (q == 0 && i4 < n4) {
