@@ -68,6 +68,16 @@ template <> struct HMma<bf16, 32> {
     static __device__ __forceinline__ int row(int lg, int e) { return 8 * (e >> 2) + 4 * lg + (e & 3); }
 };
 
+template <> struct HMma<bf16, 16> {
+    typedef floatx4 Acc;
+    static constexpr int NE = 4;
+    static __device__ __forceinline__ void run(Acc& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                    0, 0);
+    }
+    static __device__ __forceinline__ int row(int lg, int e) { return 4 * lg + e; }
+};
+
 // 16-byte chunk swizzle of a 128-byte LDS row: rows 2j and 2j+1 fall in different bank
 // halves, so any 16 consecutive rows read at one logical chunk hit distinct banks.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
@@ -597,16 +607,19 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 // boundaries, where each waits for all of its outstanding vector-memory operations:
 // LDS-DMA copies and register loads need not complete in issue order with respect to
 // each other, so a count that mixes the two kinds proves nothing.
-template <int BM, int BN, int WM, int WN, int ACT, class Out>
+template <int BM, int BN, int WM, int WN, int ACT, class Out, int MF>
 __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_rb_kernel(
     const bf16* __restrict__ A, HaloGeom g, const uint4* __restrict__ Bf, Out out, int tiles_n) {
-    using MM = HMma<bf16, 32>;
-    using Acc = MM::Acc;
-    constexpr int MF = 32, NWAVE = 4, NTH = kThreadsH;
+    using MM = HMma<bf16, MF>;
+    using Acc = typename MM::Acc;
+    constexpr int NWAVE = 4, NTH = kThreadsH;
     static_assert(WM * WN == NWAVE, "four waves");
     constexpr int TM = BM / (WM * MF), TN = BN / (WN * MF);
     static_assert(TM * WM * MF == BM && TN * WN * MF == BN, "tile shape");
-    constexpr int VEC = 8, CK = 64, KST = 4;  // 16-byte chunk = 8 bf16; 128-byte chunk = 4 MFMA k-steps
+    // 16-byte chunk = 8 bf16; a 128-byte chunk (64 channels) is 4 k-steps of 16 channels
+    // (32x32x16: lane groups of 32 take 2 chunks per k-step) or 2 k-steps of 32 (16x16x32:
+    // lane groups of 16 take 4 chunks)
+    constexpr int VEC = 8, CK = 64, KST = MF == 32 ? 4 : 2, LGS = MF == 32 ? 5 : 4;
     extern __shared__ __align__(1024) unsigned char smem[];
 
     const int t = threadIdx.x, lane = t & 63;
@@ -651,7 +664,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
         }
     };
     const int wm = wid / WN, wn = wid % WN;
-    const int lr = lane & 31, lg = lane >> 5;
+    const int lr = lane & (MF - 1), lg = lane >> LGS;
     int hpos[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -703,8 +716,8 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
         const int toff = g.sign > 0 ? kh * g.HQ + kw : (g.KH - 1 - kh) * g.HQ + (g.KW - 1 - kw);
         const int hbase = __builtin_amdgcn_readfirstlane((two ? (c & 1) : 0) * halo_bytes);
         // LDS offset of the A fragment at k-step 0; the halo buffer and every 128-byte row
-        // start are 128-byte aligned, so k-step kk (chunk 2kk + lg = 2kk ^ lg) is the same
-        // offset XOR kk << 5.
+        // start are 128-byte aligned, so k-step kk (chunk G*kk + lg = G*kk ^ lg, G = 2 or 4
+        // chunks per k-step) is the same offset XOR (G*kk) << 4.
         uint32_t fo[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -718,7 +731,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
         for (int kk = 0; kk < KST; ++kk) {
             if (kk + 1 < KST) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) fa[(kk + 1) & 1][i] = *(const uint4*)(smem + (fo[i] ^ ((kk + 1) << 5)));
+                for (int i = 0; i < TM; ++i) fa[(kk + 1) & 1][i] = *(const uint4*)(smem + (fo[i] ^ ((kk + 1) << (MF == 32 ? 5 : 6))));
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -780,25 +793,27 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     epilogue_store<bf16, ACT, BM, BN, NTH>(Cs, out, par, g, n, r0, c0, n0, sp);
 }
 
-// Weights in B-fragment order for halo_rb_kernel.  Output 16-byte unit
-//   ((group * nsteps + st) * 4 + kk) * 64 + lane,  st = chunk * KH*KW + tap
-// holds, for row = 32*group + lane%32, the 8 consecutive k of channel chunk
-// chunk*64 + kk*16 + (lane/32)*8 at tap.  Forward rows are output channels:
+// Weights in B-fragment order for halo_rb_kernel with fragments of mf = 32 or 16 rows.
+// Output 16-byte unit  ((group * nsteps + st) * kst + kk) * 64 + lane,  st = chunk * KH*KW
+// + tap, kst = 4 (mf 32) or 2 (mf 16), holds, for row = mf*group + lane%mf, the 8
+// consecutive k of channel chunk*64 + kk*16 + (lane/32)*8 (mf 32) or chunk*64 + kk*32 +
+// (lane/16)*8 (mf 16) at tap.  Forward rows are output channels:
 // w[row, tap, ch]; input-gradient rows are input channels: w[ch, tap, row].  Rows past
 // the matrix are zero.
 __global__ __launch_bounds__(256) void frag_weights(const bf16* __restrict__ w, uint4* __restrict__ dst, int Nn,
-                                                    int taps, int Cin, int nsteps, int groups, int fwd) {
-    const int64_t total = (int64_t)groups * nsteps * 4 * 64;
+                                                    int taps, int Cin, int nsteps, int groups, int fwd, int mf) {
+    const int kst = mf == 32 ? 4 : 2;
+    const int64_t total = (int64_t)groups * nsteps * kst * 64;
     for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
         const int l = (int)(u & 63);
         const int64_t q = u >> 6;
-        const int kk = (int)(q & 3);
-        const int64_t q2 = q >> 2;
+        const int kk = (int)(q % kst);
+        const int64_t q2 = q / kst;
         const int st = (int)(q2 % nsteps);
         const int grp = (int)(q2 / nsteps);
-        const int row = grp * 32 + (l & 31);
+        const int row = grp * mf + (l % mf);
         const int chunk = st / taps, tap = st - chunk * taps;
-        const int ch0 = chunk * 64 + kk * 16 + (l >> 5) * 8;
+        const int ch0 = chunk * 64 + kk * (64 / kst) + (l / mf) * 8;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (row < Nn) {
             if (fwd) {
@@ -821,7 +836,8 @@ constexpr int kCUs = 256;
 struct HaloPlan {
     int bm, bn, hb;
     int R, Q;
-    int lds;  // dynamic LDS bytes per workgroup
+    int lds;     // dynamic LDS bytes per workgroup
+    int mf = 32; // bf16 MFMA fragment height: 32 (32x32x16) or 16 (16x16x32, 224-row blocks)
 };
 
 int halo_groups(int R, int Q, int KH, int KW) { return ((R + KH - 1) * (Q + KW - 1) + 7) / 8; }
@@ -872,12 +888,9 @@ bool pick_halo(int dt, const ConvDims& d, const Sides& sd, HaloPlan* best) {
     if ((sd.Cin * es) % 128) return false;
     const int chunks = sd.Cin * es / 128;
     const int bn = sd.Nn <= 64 ? 64 : 128;
-    static const int bms_b128[] = {256, 128, 0}, bms_b64[] = {512, 256, 128, 0}, bms_f32[] = {256, 224, 0};
-    const int* bms = dt == DT_BF16 ? (bn == 128 ? bms_b128 : bms_b64) : bms_f32;
-    for (; *bms; ++bms) {
-        const int bm = *bms;
-        bool found = false;
-        double best_cost = 0.0;
+    bool found = false;
+    double best_cost = 0.0;
+    auto try_bm = [&](int bm, int mf) {
         for (int R = 1; R <= bm && R <= sd.Hout; ++R) {
             int Q = bm / R;
             if (Q > sd.Wout) Q = sd.Wout;
@@ -891,15 +904,24 @@ bool pick_halo(int dt, const ConvDims& d, const Sides& sd, HaloPlan* best) {
                 const int occ = lds <= kLdsMax / 2 ? 2 : 1;
                 const double cost = plan_cost(dt, d, sd, bm, bn, hb, R, Q, occ);
                 if (!found || cost < best_cost) {
-                    *best = HaloPlan{bm, bn, hb, R, Q, lds};
+                    *best = HaloPlan{bm, bn, hb, R, Q, lds, mf};
                     best_cost = cost;
                     found = true;
                 }
             }
         }
-        if (found) return true;
+    };
+    if (dt == DT_BF16 && bn == 128) {
+        // 256-row blocks of 32x32x16 fragments, or 224-row blocks of 16x16x32 ones (rows
+        // of 28 or 56 pixels fill 224 exactly): the cheaper estimate wins
+        try_bm(256, 32);
+        try_bm(224, 16);
+        if (!found) try_bm(128, 32);
+        return found;
     }
-    return false;
+    static const int bms_b64[] = {512, 256, 128, 0}, bms_f32[] = {256, 224, 0};
+    for (const int* bms = dt == DT_BF16 ? bms_b64 : bms_f32; *bms && !found; ++bms) try_bm(*bms, 32);
+    return found;
 }
 
 HaloGeom make_geom(const ConvDims& d, const Sides& sd, const HaloPlan& p, int dt, bool fwd) {
@@ -954,10 +976,10 @@ hipError_t launch_f32(const float* A, const HaloGeom& g, const float* B, const O
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int ACT, class Out>
+template <int BM, int BN, int WM, int WN, int ACT, class Out, int MF>
 hipError_t launch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, const Out& out, int images, int lds,
                        hipStream_t s) {
-    auto kern = halo_rb_kernel<BM, BN, WM, WN, ACT, Out>;
+    auto kern = halo_rb_kernel<BM, BN, WM, WN, ACT, Out, MF>;
     static bool raised = false;
     const hipError_t e = raise_lds(kern, raised);
     if (e != hipSuccess) return e;
@@ -977,15 +999,17 @@ hipError_t dispatch_f32(const float* A, const HaloGeom& g, const float* B, const
     return hipErrorInvalidValue;
 }
 
-// bf16 wave layouts: 128 output channels as 2 x 64 (TN = 2 fragments per wave, waves 2 x 2);
-// 64 output channels as 1 x 64 (waves 4 x 1).
+// bf16 wave layouts: 128 output channels as 2 x 64 (waves 2 x 2; TN = 2 fragments of 32 per
+// wave, or with 224-row blocks 7 x 4 fragments of 16); 64 output channels as 1 x 64 (waves
+// 4 x 1).
 template <int ACT, class Out>
 hipError_t dispatch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, const Out& out, const HaloPlan& p,
                          int images, hipStream_t s) {
-#define CONVMI_RB(BM_, BN_, WM_, WN_)                                                                       \
-    if (p.bm == BM_ && p.bn == BN_) return launch_bf16<BM_, BN_, WM_, WN_, ACT, Out>(A, g, Bf, out, images, p.lds, s);
-    CONVMI_RB(256, 128, 2, 2) CONVMI_RB(128, 128, 2, 2)
-    CONVMI_RB(512, 64, 4, 1) CONVMI_RB(256, 64, 4, 1) CONVMI_RB(128, 64, 4, 1)
+#define CONVMI_RB(BM_, BN_, WM_, WN_, MF_)                                                                  \
+    if (p.bm == BM_ && p.bn == BN_ && p.mf == MF_)                                                            \
+        return launch_bf16<BM_, BN_, WM_, WN_, ACT, Out, MF_>(A, g, Bf, out, images, p.lds, s);
+    CONVMI_RB(256, 128, 2, 2, 32) CONVMI_RB(224, 128, 2, 2, 16) CONVMI_RB(128, 128, 2, 2, 32)
+    CONVMI_RB(512, 64, 4, 1, 32) CONVMI_RB(256, 64, 4, 1, 32) CONVMI_RB(128, 64, 4, 1, 32)
 #undef CONVMI_RB
     return hipErrorInvalidValue;
 }
@@ -1003,10 +1027,10 @@ hipError_t launch_frag_weights(const bf16* w, uint4* dst, const ConvDims& d, con
                                bool fwd, hipStream_t s) {
     const int taps = d.KH * d.KW;
     const int nsteps = (sd.Cin / 64) * taps;
-    const int groups = (int)(ceil_div(sd.Nn, p.bn) * (p.bn / 32));
-    const int64_t units = (int64_t)groups * nsteps * 256;
+    const int groups = (int)(ceil_div(sd.Nn, p.bn) * (p.bn / p.mf));
+    const int64_t units = (int64_t)groups * nsteps * (p.mf == 32 ? 4 : 2) * 64;
     const int grid = (int)(ceil_div(units, 256) < 2048 ? ceil_div(units, 256) : 2048);
-    frag_weights<<<grid, 256, 0, s>>>(w, dst, sd.Nn, taps, sd.Cin, nsteps, groups, fwd ? 1 : 0);
+    frag_weights<<<grid, 256, 0, s>>>(w, dst, sd.Nn, taps, sd.Cin, nsteps, groups, fwd ? 1 : 0, p.mf);
     return hipGetLastError();
 }
 
