@@ -806,7 +806,10 @@ __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_
     // k, between MFMA groups, so their address arithmetic overlaps the MFMAs; the reads
     // of k-step kk + 1 are issued before the MFMAs of kk.
     const int nk = NK > 0 ? NK : g.SPp / 16;
-    const int spread = nk > 2 ? 2 : 1;  // k-steps that carry copies: early, to leave time for them to land
+    // k-steps that carry the next stage's copies, early to leave them time to land; the
+    // two-wave 64-channel workgroups issue theirs at once before the first MFMAs (measured
+    // ~2 us faster on c5, ~1 us slower for the eight-wave 128-channel kernel)
+    const int spread = CH == 64 ? 0 : (nk > 2 ? 2 : 1);
     if (KT > 0) issue(segs_of(0), 0, nmine);
     for (int k = 0; k < KT; ++k) {
         wait_dma(0);
@@ -815,6 +818,7 @@ __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_
         const Segs sg = segs_of(next ? k + 1 : k);
         const unsigned char* As = smem + (k & 1) * stage_bytes;
         const unsigned char* Xs = As + g.SPp * ROWB;
+        if (CH == 64 && next) issue(sg, 0, nmine);
         if (do_db) db_sum(As);
         dw_short8 fa[2][TM], fb[2][TN];
         read_frags(As, Xs, 0, fa[0], fb[0]);
