@@ -959,10 +959,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     };
 
-    // Stage k: the copies of stage k + 1 go out in slices over the first k-steps of stage
-    // k; the reads of k-step kk + 4 are issued before the MFMAs of kk.
+    // Stage k: the copies of stage k + 1 go out in slices over the first two k-steps of
+    // stage k (measured ~2% faster than four on c3); the reads of k-step kk + 4 are issued
+    // before the MFMAs of kk.
     const int nk = NK > 0 ? NK : g.SPp / 4;
-    const int spread = nk > 4 ? 4 : nk;
+    const int spread = nk > 2 ? 2 : nk;
     if (KT > 0) cp.issue(g, cp.segs_of(g, 0), 0, nmine);
     for (int k = 0; k < KT; ++k) {
         wait_dma(0);
