@@ -184,16 +184,6 @@ void oracle_apply_activation(const double* z, i64 M, i64 C, int act, int norm,
         }
 }
 
-/* ReLU decides an integer (the mask) from a floating-point value.  With batch norm the
- * library forms a in fp32 as fmaf(gamma, (z - mean) * inv_std, beta); the oracle takes
- * that one decision in the same fp32 operations so both sides agree on the mask.  All
- * other arithmetic stays fp64.  (Compiled with -ffp-contract=off.) */
-static int relu_mask_bn_f32(double z, double mean, double inv_std, double gamma, double beta) {
-    float zh = ((float)z - (float)mean) * (float)inv_std;
-    float a = fmaf((float)gamma, zh, (float)beta);
-    return a > 0.0f;
-}
-
 /* ------------------------------------------------------ a4 activation backward ---- */
 /* No norm:  dz = act'(z) * dy.
  * Batch norm, training mode, per channel c over M rows:
@@ -220,9 +210,7 @@ void oracle_activation_backward(const double* z, const double* dy, i64 M, i64 C,
             i64 i = m * C + c;
             double zh = (z[i] - mu) * is;
             double a = g * zh + beta[c];
-            double slope = (act == ACT_RELU) ? (double)relu_mask_bn_f32(z[i], mu, is, g, beta[c])
-                                             : act_slope(act, a);
-            double dno = slope * dy[i];
+            double dno = act_slope(act, a) * dy[i];
             double dzh = dno * g;
             s1 += dzh;
             s2 += dzh * zh;
@@ -233,9 +221,7 @@ void oracle_activation_backward(const double* z, const double* dy, i64 M, i64 C,
             i64 i = m * C + c;
             double zh = (z[i] - mu) * is;
             double a = g * zh + beta[c];
-            double slope = (act == ACT_RELU) ? (double)relu_mask_bn_f32(z[i], mu, is, g, beta[c])
-                                             : act_slope(act, a);
-            double dzh = slope * dy[i] * g;
+            double dzh = act_slope(act, a) * dy[i] * g;
             dz[i] = is / (double)M * ((double)M * dzh - s1 - zh * s2);
         }
         if (dgamma) dgamma[c] = sg;
@@ -261,9 +247,7 @@ void oracle_activation_backward_eval(const double* z, const double* dy, i64 M, i
             i64 i = m * C + c;
             double zh = (z[i] - mu) * is;
             double a = g * zh + beta[c];
-            double slope = (act == ACT_RELU) ? (double)relu_mask_bn_f32(z[i], mu, is, g, beta[c])
-                                             : act_slope(act, a);
-            double dno = slope * dy[i];
+            double dno = act_slope(act, a) * dy[i];
             dz[i] = dno * g * is;
             sg += dno * zh;
             sb += dno;

@@ -16,6 +16,10 @@ import workloads as WL
 TOL = {WL.F32: 1e-4, WL.BF16: 2e-2}
 BN_STAT_TOL = 1e-5
 
+# (what, observed normwise error, tolerance) of every comparison made in this process;
+# tests/conftest.py prints them at the end of the run so the headroom is visible.
+OBSERVED: list = []
+
 
 def tdtype(dt: str):
     return torch.bfloat16 if dt == WL.BF16 else torch.float32
@@ -48,11 +52,37 @@ def normwise(g, r) -> float:
     return err / scale if scale > 0 else err
 
 
-def assert_close(g, r, dt: str, what: str):
+def assert_close(g, r, dt: str, what: str, tol: float | None = None):
+    tol = TOL[dt] if tol is None else tol
     e = normwise(g, r)
+    OBSERVED.append((what, e, tol))
     assert np.all(np.isfinite(g)), f"{what}: non-finite values"
-    assert e <= TOL[dt], f"{what}: normwise error {e:.3e} > {TOL[dt]:.0e}"
+    assert e <= tol, f"{what}: normwise error {e:.3e} > {tol:.0e}"
     return e
+
+
+def relu_kink_ties(z, gamma, beta, mean, inv_std):
+    """Elements whose normalised activation input a = gamma*(z - mean)*inv_std + beta
+    (fp64, from the same fp32 statistics both sides receive) lies within 8 fp32 roundings
+    of the ReLU kink.  There the library's fp32 a and the oracle's fp64 a may fall on
+    different sides of 0, flipping that element's ReLU derivative (an integer decision
+    taken from a floating-point value).  The tests zero dy at these elements on BOTH
+    sides, so the decision no longer matters, and check that they are few."""
+    zh = (np.asarray(z, np.float64) - mean) * inv_std
+    a = gamma * zh + beta
+    return np.abs(a) <= 2.0 ** -21 * (np.abs(gamma * zh) + np.abs(beta))
+
+
+def untie_relu(dy, z, act, gamma, beta, mean, inv_std):
+    """dy with the ReLU-kink ties (relu_kink_ties) zeroed; other activations are smooth
+    and pass through unchanged."""
+    import workloads as WL_
+    if act != WL_.ACT_RELU:
+        return dy
+    ties = relu_kink_ties(z, gamma, beta, mean, inv_std)
+    n = int(ties.sum())
+    assert n <= 4 + 1e-5 * ties.size, f"{n} of {ties.size} activation inputs sit at the ReLU kink"
+    return np.where(ties, 0.0, dy)
 
 
 def assert_bn_stats(mean_g, inv_g, mean_r, var_r, inv_r, eps, what="", tol=BN_STAT_TOL):
@@ -60,8 +90,10 @@ def assert_bn_stats(mean_g, inv_g, mean_r, var_r, inv_r, eps, what="", tol=BN_ST
     resolution of the stored fp32 result) and |dinv_std| <= tol*inv_std."""
     dm = np.abs(np.asarray(mean_g) - mean_r)
     bound = tol * np.sqrt(var_r + eps) + np.abs(mean_r) * 2.0 ** -23
-    assert np.all(dm <= bound), f"{what} mean: {np.max(dm / bound):.3e} of bound"
     di = np.abs(np.asarray(inv_g) - inv_r) / inv_r
+    OBSERVED.append((f"{what} mean (of bound)", float(np.max(dm / bound)) * tol, tol))
+    OBSERVED.append((f"{what} inv_std", float(np.max(di)), tol))
+    assert np.all(dm <= bound), f"{what} mean: {np.max(dm / bound):.3e} of bound"
     assert np.all(di <= tol), f"{what} inv_std: {np.max(di):.3e}"
 
 

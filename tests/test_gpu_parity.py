@@ -5,8 +5,9 @@ seeded inputs.
   compared, shapes chosen to span several tiles with ragged tails, odd channel counts,
   strides, paddings, 1x1 and whole-image kernels, fp32 and bf16.
 * The workload configurations at full size, in the launch configuration the bench
-  times: full comparison where the oracle takes seconds, sampled outputs (random plus
-  every corner) where it would take longer.
+  times: every output element compared with the full oracle routines (the largest
+  products take the host's cores a second or two each).  Only tensors past 2^31
+  elements are checked at sampled outputs.
 * Edge and contract cases: accumulate, in-place activation backward, determinism.
 
 Inputs always come from workloads.py or from the oracle; nothing computed by the
@@ -172,7 +173,9 @@ def test_medium_batchnorm_layer(case):
     mean_r, var_r, inv_r, rm_r, rv_r = O.bn_stats(zs, mom, eps, rm0, rv0)
     # The forward's statistics are taken over the library's own stored z, which for
     # bf16 differs from the oracle's rounded z by up to one bf16 ulp per element: there
-    # they inherit the bf16 tolerance.  The 1e-5 bound is checked on identical z below.
+    # they inherit the bf16 data tolerance.  The 1e-5 bound on bf16 data is checked where
+    # both sides' z agree exactly by construction
+    # (test_batchnorm_statistics_exact_bf16) and on the oracle's z below.
     stat_tol = G.BN_STAT_TOL if dt == WL.F32 else G.TOL[dt]
     G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, eps, "fwd",
                       stat_tol)
@@ -184,6 +187,7 @@ def test_medium_batchnorm_layer(case):
     G.assert_close(G.host(out["y"]), y_r, dt, "y")
     # backward on oracle-made inputs: z (rounded), statistics rounded to fp32
     m32, i32 = WL.round_to(WL.F32, mean_r), WL.round_to(WL.F32, inv_r)
+    dy = WL.round_to(dt, G.untie_relu(dy, zs, act, gamma, beta, m32, i32))
     dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(zs, dt), G.dev(dy, dt), G.dev(gamma), G.dev(beta), G.dev(m32),
                                 G.dev(i32))
     dz_r, dg_r, db_r = O.activation_backward(zs, dy, act, WL.NORM_BATCH, gamma, beta, m32, i32)
@@ -217,6 +221,7 @@ def test_medium_batchnorm_evaluation(case):
     m32, i32 = WL.round_to(WL.F32, mean_r), WL.round_to(WL.F32, inv_r)
     y_r = O.apply_activation(zs, act, WL.NORM_BATCH, gamma, beta, m32, i32)
     G.assert_close(G.host(out["y"]), y_r, dt, "y")
+    dy = WL.round_to(dt, G.untie_relu(dy, zs, act, gamma, beta, m32, i32))
     dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(zs, dt), G.dev(dy, dt), G.dev(gamma), G.dev(beta), G.dev(m32),
                                 G.dev(i32))
     dz_r, dg_r, db_r = O.activation_backward(zs, dy, act, WL.NORM_BATCH, gamma, beta, m32, i32, evaluation=True)
@@ -245,9 +250,10 @@ def test_full_batchnorm_evaluation_c3():
     y_r = O.apply_activation(zs, wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32)
     G.assert_close(G.host(out["y"]), y_r, dt, "y")
     # backward on the oracle's z (rounded to the storage type), not the library's
-    dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(zs, dt), G.dev(d["dy"], dt), G.dev(d["gamma"]), G.dev(d["beta"]),
+    dy = WL.round_to(dt, G.untie_relu(d["dy"], zs, wl.act, d["gamma"], d["beta"], m32, i32))
+    dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(zs, dt), G.dev(dy, dt), G.dev(d["gamma"]), G.dev(d["beta"]),
                                 G.dev(m32), G.dev(i32))
-    dz_r, dg_r, db_r = O.activation_backward(zs, d["dy"], wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32,
+    dz_r, dg_r, db_r = O.activation_backward(zs, dy, wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32,
                                              evaluation=True)
     G.assert_close(G.host(dz), dz_r, dt, "dz")
     G.assert_close(G.host(dg), dg_r, dt, "dgamma")
@@ -283,7 +289,6 @@ def _inputs(name):
 
 
 FULL = ["c1", "c2a", "c2b", "c2c", "c3", "c4", "c5"]
-BIG = {"c4", "c5"}  # sampled comparisons for the forward and dX
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -298,14 +303,6 @@ def test_full_forward(name):
     out = G.run_forward(desc, dt, G.dev(d["x"], dt), G.dev(d["w"], dt), G.dev(d.get("b")),
                         G.dev(d.get("gamma")), G.dev(d.get("beta")), rm_d, rv_d)
     st, pd = (s.sh, s.sw), (s.ph, s.pw)
-    if name in BIG:
-        idx = G.sample_indices(s.y_shape, 4096, 7)
-        z_r = O.conv2d_forward_at(d["x"], d["w"], d.get("b"), idx, st, pd)
-        z_g = G.host(out["z"])[tuple(idx.T)]
-        G.assert_close(z_g, z_r, dt, f"{name} z (sampled)")
-        y_r = O.apply_activation(WL.round_to(dt, z_r).reshape(-1, 1), wl.act).reshape(-1)
-        G.assert_close(G.host(out["y"])[tuple(idx.T)], y_r, dt, f"{name} y (sampled)")
-        return
     z_r = d.get("z_oracle")
     if z_r is None:
         z_r = O.conv2d_forward(d["x"], d["w"], d.get("b"), st, pd)
@@ -338,6 +335,7 @@ def test_full_activation_backward(name):
     if wl.norm == WL.NORM_BATCH:
         mean_r, _, inv_r, *_ = O.bn_stats(z, wl.momentum, wl.eps)
         m32, i32 = WL.round_to(WL.F32, mean_r), WL.round_to(WL.F32, inv_r)
+        dy = WL.round_to(dt, G.untie_relu(dy, z, wl.act, d["gamma"], d["beta"], m32, i32))
         dz, dg, dbt = G.run_act_bwd(desc, dt, G.dev(z, dt), G.dev(dy, dt), G.dev(d["gamma"]), G.dev(d["beta"]),
                                     G.dev(m32), G.dev(i32))
         dz_r, dg_r, db_r = O.activation_backward(z, dy, wl.act, WL.NORM_BATCH, d["gamma"], d["beta"], m32, i32)
@@ -363,12 +361,7 @@ def test_full_backward_data(name):
     dz = _grad_input(name)
     dx = G.run_backward_data(G.desc_for(wl), dt, G.dev(dz, dt), G.dev(d["w"], dt))
     st, pd = (s.sh, s.sw), (s.ph, s.pw)
-    if name in BIG:
-        idx = G.sample_indices(s.x_shape, 4096, 8)
-        dx_r = O.conv2d_backward_data_at(dz, d["w"], s.x_shape, idx, st, pd)
-        G.assert_close(G.host(dx)[tuple(idx.T)], dx_r, dt, f"{name} dx (sampled)")
-    else:
-        G.assert_close(G.host(dx), O.conv2d_backward_data(dz, d["w"], s.x_shape, st, pd), dt, f"{name} dx")
+    G.assert_close(G.host(dx), O.conv2d_backward_data(dz, d["w"], s.x_shape, st, pd), dt, f"{name} dx")
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -379,15 +372,12 @@ def test_full_backward_weight(name):
     dz = _grad_input(name)
     dw, db = G.run_backward_weight(G.desc_for(wl), G.dev(d["x"], dt), G.dev(dz, dt))
     st, pd = (s.sh, s.sw), (s.ph, s.pw)
-    if name == "c4":
-        idx = G.sample_indices(s.w_shape, 1024, 9)
-        dw_r = O.conv2d_backward_weight_at(d["x"], dz, s.w_shape, idx, st, pd)
-        G.assert_close(G.host(dw)[tuple(idx.T)], dw_r, dt, f"{name} dw (sampled)")
-        G.assert_close(G.host(db), O.bias_grad(dz), dt, f"{name} db")
-    else:
-        dw_r, db_r = O.conv2d_backward_weight(d["x"], dz, s.w_shape, st, pd)
-        G.assert_close(G.host(dw), dw_r, dt, f"{name} dw")
-        G.assert_close(G.host(db), db_r, dt, f"{name} db")
+    dw_r, db_r = O.conv2d_backward_weight(d["x"], dz, s.w_shape, st, pd)
+    # dW and db are fp32 sums of exactly representable products (bf16 x bf16 is exact in
+    # fp32): only the summation order differs from the oracle, so they are held to the
+    # fp32 tolerance whatever the data type.
+    G.assert_close(G.host(dw), dw_r, WL.F32, f"{name} dw")
+    G.assert_close(G.host(db), db_r, WL.F32, f"{name} db")
 
 
 def test_rl_stack_chained():
@@ -529,6 +519,49 @@ def test_forward_batchnorm_large_offset():
     mean_r, var_r, inv_r, *_ = O.bn_stats(zs, 0.1, 1e-5)
     assert np.all(np.abs(mean_r) > 500 * np.sqrt(var_r))
     G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, 1e-5, "offset fwd")
+
+
+EXACT_BN = [
+    ((2, 15, 17, 64, 72, 3, 3, 1, 1, 1, 1), WL.ACT_TANH),     # stride 1: statistics from the conv epilogue
+    ((3, 30, 9, 128, 64, 3, 3, 1, 1, 1, 1), WL.ACT_RELU),     # stride 1, 128 input channels
+    ((4, 16, 16, 128, 128, 3, 3, 1, 1, 1, 1), WL.ACT_IDENTITY),
+    ((2, 20, 20, 64, 64, 3, 3, 2, 2, 1, 1), WL.ACT_SIGMOID),   # stride 2: separate statistics pass
+]
+
+
+@pytest.mark.parametrize("case", EXACT_BN, ids=lambda c: f"{'x'.join(map(str, c[0][:7]))}_s{c[0][7]}")
+def test_batchnorm_statistics_exact_bf16(case):
+    """bf16 training forward with batch norm on inputs whose pre-activations are small
+    integers: x, w in {-1, 0, 1} (mostly 0) and an integer bias, so every product and
+    partial sum is exact in fp32 and every z (|z| < 256) is exact in bf16.  Both sides
+    then hold the same z by construction, and the library's batch statistics (from its
+    own stored z) must meet the 1e-5 bound; z itself must be bit-exact."""
+    s, act = case
+    shape = WL.ConvShape(*s)
+    r = np.random.default_rng(95)
+    x = r.choice([-1.0, 0.0, 0.0, 0.0, 0.0, 0.0, 1.0], size=shape.x_shape)
+    w = r.choice([-1.0, 0.0, 0.0, 0.0, 0.0, 0.0, 1.0], size=shape.w_shape)
+    b = r.integers(-8, 9, size=shape.OC).astype(np.float64)
+    gamma = WL.round_to(WL.F32, r.uniform(0.5, 1.5, shape.OC))
+    beta = WL.round_to(WL.F32, r.normal(0.0, 0.1, shape.OC))
+    rm0 = WL.round_to(WL.F32, r.normal(0.0, 0.2, shape.OC))
+    rv0 = WL.round_to(WL.F32, r.uniform(0.5, 2.0, shape.OC))
+    mom, eps = 0.1, 1e-5
+    st, pd = (shape.sh, shape.sw), (shape.ph, shape.pw)
+    z_r = O.conv2d_forward(x, w, b, st, pd)
+    assert np.max(np.abs(z_r)) < 256 and np.array_equal(z_r, np.round(z_r)), "z must be exact in bf16"
+    desc = G.shape_desc(shape, WL.BF16, act, WL.NORM_BATCH, mom, eps)
+    rm_d, rv_d = G.dev(rm0), G.dev(rv0)
+    out = G.run_forward(desc, WL.BF16, G.dev(x, WL.BF16), G.dev(w, WL.BF16), G.dev(b), G.dev(gamma), G.dev(beta),
+                        rm_d, rv_d)
+    np.testing.assert_array_equal(G.host(out["z"]), z_r)
+    mean_r, var_r, inv_r, rm_r, rv_r = O.bn_stats(z_r, mom, eps, rm0, rv0)
+    G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, eps,
+                      "exact bf16 fwd")
+    G.assert_close(G.host(rm_d), rm_r, WL.F32, "exact bf16 running_mean")
+    G.assert_close(G.host(rv_d), rv_r, WL.F32, "exact bf16 running_var")
+    y_r = O.apply_activation(z_r, act, WL.NORM_BATCH, gamma, beta, mean_r, inv_r)
+    G.assert_close(G.host(out["y"]), y_r, WL.BF16, "exact bf16 y")
 
 
 def test_bn_stats_large_offset():

@@ -39,6 +39,10 @@ MUTANTS = [
      "dz[i] = is / (double)M * ((double)M * dzh + s1 - zh * s2);", 0),
     ("bnbwd_gamma_missing", "double dzh = dno * g;", "double dzh = dno;", 0),
     ("bnbwd_dgamma_no_zhat", "sg += dno * zh;", "sg += dno;", 0),
+    ("bnbwd_mask_at_z", "double dno = act_slope(act, a) * dy[i];", "double dno = act_slope(act, z[i]) * dy[i];", 0),
+    ("bnbwd_dz_mask_at_z", "double dzh = act_slope(act, a) * dy[i] * g;", "double dzh = act_slope(act, z[i]) * dy[i] * g;",
+     0),
+    ("bneval_mask_at_z", "double dno = act_slope(act, a) * dy[i];", "double dno = act_slope(act, z[i]) * dy[i];", 1),
     ("dx_flipped_kernel", "const double* wp = w + ((oc * KH + kh) * KW + kw) * IC;",
      "const double* wp = w + ((oc * KH + (KH - 1 - kh)) * KW + (KW - 1 - kw)) * IC;", 1),
     ("dx_pad_sign", "i64 ih = oh * sh - ph + kh;", "i64 ih = oh * sh + ph - kh;", 1),
