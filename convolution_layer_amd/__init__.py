@@ -29,7 +29,8 @@ OP_FORWARD, OP_BACKWARD_DATA, OP_BACKWARD_WEIGHT, OP_BN_STATS, OP_ACTIVATION_BAC
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "MISALIGNED", 5: "HIP"}
 
 # Every symbol include/convmi.h declares.
-EXPORTS = ("convmi_output_dims", "convmi_workspace_size", "conv2d_forward", "conv2d_backward_data",
+EXPORTS = ("convmi_output_dims", "convmi_workspace_size", "conv2d_forward", "conv2d_forward_noalloc",
+           "conv2d_backward_data",
            "conv2d_backward_weight", "bn_stats_training", "activation_backward", "convmi_last_error",
            "convmi_version")
 
@@ -61,6 +62,7 @@ def _load():
     L.convmi_output_dims.argtypes = [dp, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]
     L.convmi_workspace_size.argtypes = [dp, i32, C.POINTER(sz)]
     L.conv2d_forward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.conv2d_forward_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.conv2d_backward_data.argtypes = [dp, vp, vp, vp, vp, sz, vp]
     L.conv2d_backward_weight.argtypes = [dp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.bn_stats_training.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -138,6 +140,16 @@ def conv2d_forward(desc, x, w, bias, gamma, beta, running_mean, running_var, sav
     _check(lib.conv2d_forward(C.byref(desc), _ptr(x), _ptr(w), _ptr(bias), _ptr(gamma), _ptr(beta),
                               _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_inv_std),
                               _ptr(z), _ptr(y), wp, wn, _stream(stream)))
+
+
+def conv2d_forward_noalloc(desc, x, w, bias, gamma, beta, running_mean, running_var, save_mean, save_inv_std, z,
+                           y, stream=None):
+    _check(lib.conv2d_forward_noalloc(C.byref(desc), _ptr(x), _ptr(w), _ptr(bias), _ptr(gamma), _ptr(beta),
+                                      _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_inv_std),
+                                      _ptr(z), _ptr(y), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # CONVMI_NOALLOC_SCRATCH_BYTES
 
 
 def conv2d_backward_data(desc, dz, w, dx, workspace=None, stream=None):

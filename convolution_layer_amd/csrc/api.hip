@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/convmi.h"
@@ -179,12 +180,16 @@ CONVMI_API convmi_status convmi_workspace_size(const convmi_desc* desc, int32_t 
     return CONVMI_OK;
 }
 
-CONVMI_API convmi_status conv2d_forward(const convmi_desc* desc, const void* x, const void* w, const float* bias,
-                             const float* gamma, const float* beta, float* running_mean, float* running_var,
-                             float* save_mean, float* save_inv_std, void* z, void* y,
-                             void* workspace, size_t workspace_bytes, void* stream) {
-    ConvDims d;
-    CHECK(check_desc(desc, &d));
+}  // extern "C"
+
+namespace {
+
+// conv2d_forward after the descriptor check; shared by the allocation-free variant,
+// which passes its static scratch array as the workspace.
+convmi_status forward_impl(const convmi_desc* desc, const ConvDims& d, const void* x, const void* w,
+                           const float* bias, const float* gamma, const float* beta, float* running_mean,
+                           float* running_var, float* save_mean, float* save_inv_std, void* z, void* y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
     CHECK(need(x, "x"));
     CHECK(need(w, "w"));
     CHECK(need(y, "y"));
@@ -257,6 +262,68 @@ CONVMI_API convmi_status conv2d_forward(const convmi_desc* desc, const void* x, 
         if (e != hipSuccess) return hip_fail(e, "conv2d_forward: normalise/activate launch");
     }
     return CONVMI_OK;
+}
+
+// Scratch for conv2d_forward_noalloc: one copy per GPU, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (in host code the name is a
+// host-side stand-in): it uses the device address hipGetSymbolAddress returns, looked
+// up once per device.
+constexpr size_t kScratchBytes = CONVMI_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's `scratch`, resolved on the first call made with the
+// device current.
+convmi_status scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_forward_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CONVMI_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward_noalloc: hipGetSymbolAddress(scratch)");
+        if (!p || !aligned(p, 256)) return fail(CONVMI_ERR_HIP, "scratch array has no usable device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CONVMI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+CONVMI_API convmi_status conv2d_forward(const convmi_desc* desc, const void* x, const void* w, const float* bias,
+                             const float* gamma, const float* beta, float* running_mean, float* running_var,
+                             float* save_mean, float* save_inv_std, void* z, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    return forward_impl(desc, d, x, w, bias, gamma, beta, running_mean, running_var, save_mean, save_inv_std, z, y,
+                        workspace, workspace_bytes, stream);
+}
+
+CONVMI_API convmi_status conv2d_forward_noalloc(const convmi_desc* desc, const void* x, const void* w,
+                                                const float* bias, const float* gamma, const float* beta,
+                                                float* running_mean, float* running_var, float* save_mean,
+                                                float* save_inv_std, void* z, void* y, void* stream) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    const size_t want = ws_forward(desc, d);
+    if (want > kScratchBytes)
+        return fail(CONVMI_ERR_WORKSPACE,
+                    "conv2d_forward_noalloc: this layer needs %zu bytes of scratch, above the static limit of %zu; "
+                    "use conv2d_forward with a caller-owned workspace",
+                    want, kScratchBytes);
+    void* ws = nullptr;
+    if (want > 0) CHECK(scratch_for_current_device(&ws));
+    return forward_impl(desc, d, x, w, bias, gamma, beta, running_mean, running_var, save_mean, save_inv_std, z, y,
+                        ws, want, stream);
 }
 
 CONVMI_API convmi_status conv2d_backward_data(const convmi_desc* desc, const void* dz, const void* w, void* dx,

@@ -133,6 +133,23 @@ convmi_status conv2d_forward(const convmi_desc* desc, const void* x, const void*
                              float* save_mean, float* save_inv_std, void* z, void* y,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as conv2d_forward, minus the workspace: its scratch is a
+ * static device array of CONVMI_NOALLOC_SCRATCH_BYTES that the library holds on each GPU
+ * it runs on until the process ends (its address is looked up on the first call made
+ * with that device current).  A layer needing more scratch than that returns
+ * CONVMI_ERR_WORKSPACE before any device work; use conv2d_forward with a workspace then.
+ * The call allocates nothing and calls no allocating routine.  Every call on one GPU
+ * shares that GPU's array (whose contents on entry do not matter): calls that overlap
+ * in time on the same GPU, from any stream or thread, race on it and must be ordered by
+ * the caller. */
+#define CONVMI_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+convmi_status conv2d_forward_noalloc(const convmi_desc* desc, const void* x, const void* w, const float* bias,
+                                     const float* gamma, const float* beta, float* running_mean,
+                                     float* running_var, float* save_mean, float* save_inv_std, void* z, void* y,
+                                     void* stream);
+
 /* a5: dx[n,ih,iw,ic] = sum over (oc,kh,kw) with oh*stride_h - pad_h + kh == ih and
  * ow*stride_w - pad_w + kw == iw of w[oc,kh,kw,ic] * dz[n,oh,ow,oc].  Linear in dz:
  * the activation / batch-norm derivative is applied beforehand by

@@ -174,3 +174,19 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+
+
+def test_noalloc_forward_rejects_layers_beyond_its_scratch(cm):
+    """A layer whose forward needs more scratch than the static array: WORKSPACE status,
+    returned on the host before any device call (so this runs without a GPU)."""
+    d = cm.make_desc(2, 32, 32, 8, 4096, 1, 1, (2, 2), (0, 0), cm.ACT_RELU, cm.NORM_BATCH, dtype=cm.BF16)
+    assert cm.workspace_size(d, cm.OP_FORWARD) > cm.NOALLOC_SCRATCH_BYTES
+    p = 1 << 20  # never dereferenced: the size check comes first
+    st = cm.lib.conv2d_forward_noalloc(C.byref(d), p, p, None, p, p, None, None, p, p, p, p, None)
+    assert st == cm.ERR_WORKSPACE
+    assert b"static limit" in cm.lib.convmi_last_error()
+
+
+def test_noalloc_scratch_limit_matches_header(cm):
+    m = re.search(r"#define CONVMI_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == cm.NOALLOC_SCRATCH_BYTES
