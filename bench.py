@@ -11,14 +11,19 @@ Per-call durations come from HIP events recorded on the stream the library launc
 (torch's current stream) around every call of the timed steps.  The fp64 oracle is
 timed on a bounded sample of the same layer on the host cores (cpu_baseline).
 
-HBM traffic of the dominant call comes from rocprofv3 counter runs of this script
-(FETCH_SIZE, WRITE_SIZE), scaled by what the same counters read for a plain device copy
-of known size; the figures live in profiles/traffic.json together with a hash of the
-kernel sources they were taken on, and are reported as null once the sources change.
-Modes for producing them:
-  python bench.py --only CALL --steps 3 --warmup 1 --no-cpu-baseline --no-bn   (counter runs)
+HBM traffic and MFMA utilisation of the dominant call come from rocprofv3 counter runs
+of this script: FETCH_SIZE and WRITE_SIZE (scaled by what the same counters read for a
+plain device copy of known size), and SQ_VALU_MFMA_BUSY_CYCLES over the kernel's GPU
+cycles (GRBM_GUI_ACTIVE of one XCD: the reported sum over the 8 XCDs / 8) times the 1024
+SIMDs -- the fraction of SIMD cycles the matrix pipe is busy, rocprofv3's MfmaUtil, i.e.
+the MFMA rate as a fraction of the peak at the clock the kernel actually ran at -- with
+SQ_INSTS_VALU_MFMA_MOPS_* x 512 (the flops the matrix pipe executed).  The
+figures live in profiles/traffic.json, per workload, with a hash of the kernel sources
+they were taken on, and are reported as null once the sources change.  Modes for
+producing them:
+  python bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --no-bn  (counter runs)
   python bench.py --calibrate-copy                                              (copy kernel)
-  python bench.py --summarize DIR                          (rocprofv3 CSVs -> summary text)
+  python bench.py --summarize DIR --workload W   (rocprofv3 CSVs -> summary text, traffic.json)
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -40,6 +45,8 @@ import workloads as WL  # noqa: E402
 
 PEAK_TFLOPS = {WL.BF16: 2516.6, WL.F32: 157.3}  # MI355X dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
+SIMD_NUM = 1024  # 256 CUs x 4 SIMDs
+XCD_NUM = 8  # rocprofv3's per-dispatch GRBM_GUI_ACTIVE is the sum over the 8 XCDs
 METRIC = "conv2d fwd+dX+dW TFLOP/s and % MFMA peak; BN-stats GB/s (1 MI355X)"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
@@ -379,15 +386,24 @@ def _read_counters(d):
     return out
 
 
-def summarize(d):
-    """Summarise rocprofv3 output under d (kt/, fetch/, write/, copy_fetch/, copy_write/):
-    kernel durations, and FETCH_SIZE/WRITE_SIZE per dispatch scaled by the copy
-    calibration.  Writes d/traffic.json and prints the text summary."""
-    lines = [f"rocprofv3 summary of {d} (library sources {source_hash()})", ""]
-    stats = glob.glob(os.path.join(d, "kt", "**", "*kernel_stats.csv"), recursive=True)
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32")
+
+
+def summarize(d, workload):
+    """Summarise rocprofv3 output of one workload under d/<workload>/ (kt/, fetch/, write/,
+    mfma/) with the copy calibration in d/copy_fetch/, d/copy_write/: kernel durations,
+    FETCH_SIZE / WRITE_SIZE per dispatch scaled by the copy calibration, and per kernel
+    the matrix pipe's busy fraction and executed flops.  Updates the workload's entry of
+    d/traffic.json and prints the text summary."""
+    lines = [f"rocprofv3 summary of {d}, workload {workload} (library sources {source_hash()})", ""]
+    wd = os.path.join(d, workload)
+    stats = glob.glob(os.path.join(wd, "kt", "**", "*kernel_stats.csv"), recursive=True)
+    avg_us = {}
     if stats:
         lines.append(f"{'kernel':90s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}")
         for r in csv.DictReader(open(stats[0])):
+            avg_us[r["Name"]] = float(r["AverageNs"]) / 1e3
             lines.append(f"{r['Name'][:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.2f} "
                          f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
         lines.append("")
@@ -400,10 +416,18 @@ def summarize(d):
             scale[cnt] = (COPY_BYTES / 1024.0) / kib
             lines.append(f"copy calibration {cnt}: {kib:.0f} KiB per {COPY_BYTES >> 20} MiB copy -> factor "
                          f"{scale[cnt]:.4f}")
-    traffic = {"sources": source_hash(), "scale": scale, "calls": {}}
+    path = os.path.join(d, "traffic.json")
+    try:
+        traffic = json.load(open(path))
+    except (OSError, ValueError):
+        traffic = {}
+    if traffic.get("sources") != source_hash():
+        traffic = {"sources": source_hash(), "workloads": {}}
+    if scale:
+        traffic["scale"] = scale
     per_kernel = {}
     for cnt, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
-        c = _read_counters(os.path.join(d, sub))
+        c = _read_counters(os.path.join(wd, sub))
         for (k, n), vs in c.items():
             if n == cnt:
                 per_kernel.setdefault(k, {})[cnt] = float(np.median(vs))
@@ -413,29 +437,80 @@ def summarize(d):
         for k, v in sorted(per_kernel.items()):
             lines.append(f"{k[:90]:90s} {v.get('FETCH_SIZE', float('nan')):12.0f} "
                          f"{v.get('WRITE_SIZE', float('nan')):12.0f}")
-        traffic["kernels"] = {k: v for k, v in per_kernel.items()}
-    with open(os.path.join(d, "traffic.json"), "w") as f:
+    c = _read_counters(os.path.join(wd, "mfma"))
+    mf = {}
+    for (k, n), vs in c.items():
+        if n in MFMA_COUNTERS:
+            mf.setdefault(k, {})[n] = float(np.median(vs))
+    mfma = {}
+    for k, v in sorted(mf.items()):
+        if v.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+            mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + v.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
+            if mops == 0:
+                continue
+            cycles = v["GRBM_GUI_ACTIVE"] / XCD_NUM
+            mfma[k] = {"busy": v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMD_NUM), "mfma_flops": mops * 512.0,
+                       "gpu_cycles": cycles, **v}
+    if mfma:
+        lines.append("")
+        lines.append(f"{'kernel':90s} {'MFMA busy':>10s} {'MFMA GFLOP':>11s} {'TFLOP/s':>9s} {'GHz':>6s} (per "
+                     f"dispatch; busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCD_NUM} x {SIMD_NUM} SIMDs); "
+                     "TFLOP/s from the trace's average duration; GHz = cycles / duration)")
+        for k, v in mfma.items():
+            t = avg_us.get(k)
+            rate = f"{v['mfma_flops'] / (t * 1e-6) / 1e12:9.1f}" if t else f"{'':9s}"
+            ghz = f"{v['gpu_cycles'] / (t * 1e3):6.2f}" if t else f"{'':6s}"
+            lines.append(f"{k[:90]:90s} {100 * v['busy']:9.1f}% {v['mfma_flops'] / 1e9:11.2f} {rate} {ghz}")
+    traffic.setdefault("workloads", {})[workload] = {"kernels": per_kernel, "mfma": mfma, "avg_us": avg_us}
+    with open(path, "w") as f:
         json.dump(traffic, f, indent=1)
     print("\n".join(lines))
 
 
-def call_traffic(call: str):
-    """HBM bytes per launch of one library call from profiles/traffic.json, or None when
+def _counters(workload: str):
+    """The workload's entry of profiles/traffic.json and the copy scale, or None when
     absent or taken on different sources."""
     try:
         t = json.load(open(TRAFFIC_JSON))
     except (OSError, ValueError):
+        return None, None
+    if t.get("sources") != source_hash() or len(t.get("scale", {})) != 2:
+        return None, None
+    return t.get("workloads", {}).get(workload), t["scale"]
+
+
+def _of_call(k: str, call: str) -> bool:
+    shared = "igemm" in k or "halo" in k  # one template for both directions: FwdOut / DxOut
+    return any(f in k for f in KERNEL_OF_CALL[call]) and (not shared or ("FwdOut" in k) == (call == "forward"))
+
+
+def call_traffic(call: str, workload: str):
+    """HBM bytes per launch of one library call (all its kernels), or None."""
+    w, scale = _counters(workload)
+    if not w or not w.get("kernels"):
         return None
-    if t.get("sources") != source_hash() or "kernels" not in t or len(t.get("scale", {})) != 2:
-        return None
-    frags = KERNEL_OF_CALL[call]
     total, seen = 0.0, False
-    for k, v in t["kernels"].items():
-        shared = "igemm" in k or "halo" in k  # one template for both directions: FwdOut / DxOut
-        if any(f in k for f in frags) and (not shared or ("FwdOut" in k) == (call == "forward")):
-            total += v.get("FETCH_SIZE", 0) * t["scale"]["FETCH_SIZE"] + v.get("WRITE_SIZE", 0) * t["scale"]["WRITE_SIZE"]
+    for k, v in w["kernels"].items():
+        if _of_call(k, call):
+            total += v.get("FETCH_SIZE", 0) * scale["FETCH_SIZE"] + v.get("WRITE_SIZE", 0) * scale["WRITE_SIZE"]
             seen = True
     return total * 1024.0 if seen else None
+
+
+def call_mfma(call: str, workload: str):
+    """Matrix-pipe busy fraction and flops of the call's longest kernel, or None."""
+    w, _ = _counters(workload)
+    if not w or not w.get("mfma"):
+        return None
+    ks = [k for k in w["mfma"] if _of_call(k, call)]
+    if not ks:
+        return None
+    k = max(ks, key=lambda k_: w.get("avg_us", {}).get(k_, 0.0))
+    v = w["mfma"][k]
+    t = w.get("avg_us", {}).get(k)
+    name = k.replace("(anonymous namespace)::", "").replace("void ", "")
+    return {"kernel": name.split("(")[0][:100], "busy": round(v["busy"], 4), "mfma_gflop": round(v["mfma_flops"] / 1e9, 3),
+            "kernel_us": None if t is None else round(t, 2)}
 
 
 def main():
@@ -454,7 +529,7 @@ def main():
                     help="time every call of every configuration (warm and cold) instead of the bench step")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize)
+        summarize(args.summarize, args.workload)
         return
     if args.report:
         report()
@@ -488,12 +563,16 @@ def main():
     dom = max(conv_calls, key=conv_calls.get)
     achieved = s.flops() / (conv_calls[dom] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
-    tr = call_traffic(dom)
+    tr = call_traffic(dom, wl.name)
+    mf = call_mfma(dom, wl.name)
     roofline = {"bound": "mfma", "kernel": f"conv2d_{dom}", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None if tr is None else round(tr),
+                "mfma_busy": None if mf is None else mf["busy"], "mfma_counters": mf,
                 "per_call_ms": {k: round(v, 4) for k, v in ms.items()},
                 "per_call_tflops": {k: round(s.flops() / (v * 1e-3) / 1e12, 2) for k, v in conv_calls.items()},
-                "per_call_hbm_bytes": {k: call_traffic(k) for k in CONV_CALLS}}
+                "per_call_hbm_bytes": {k: call_traffic(k, wl.name) for k in CONV_CALLS},
+                "per_call_mfma_busy": {k: (lambda m: None if m is None else m["busy"])(call_mfma(k, wl.name))
+                                       for k in CONV_CALLS}}
 
     bn = None
     if not args.no_bn:
