@@ -15,8 +15,8 @@ import numpy as np
 
 from . import build as _build
 
-ACT_IDENTITY, ACT_RELU, ACT_TANH, ACT_SIGMOID = 0, 1, 2, 3
-NORM_NONE, NORM_BATCH = 0, 1
+ACT_IDENTITY, ACT_RELU, ACT_TANH, ACT_SIGMOID, ACT_GELU = 0, 1, 2, 3, 4
+NORM_NONE, NORM_BATCH, NORM_LAYER, NORM_GROUP = 0, 1, 2, 3
 
 _lib = None
 _D = C.POINTER(C.c_double)
@@ -53,6 +53,9 @@ def _load(path: str, rebuild: bool = False):
     L.oracle_conv2d_backward_weight.argtypes = [_D, _D, _D, _D] + dims
     L.oracle_conv2d_backward_weight_at.argtypes = [_D, _D, _L, _i, _D] + dims
     L.oracle_bias_grad.argtypes = [_D, _i, _i, _D]
+    L.oracle_group_stats.argtypes = [_D, _i, _i, _i, _i, C.c_double, _D, _D, _D]
+    L.oracle_apply_group_norm.argtypes = [_D, _i, _i, _i, _i, C.c_int, _D, _D, _D, _D, _D]
+    L.oracle_group_norm_backward.argtypes = [_D, _D, _i, _i, _i, _i, C.c_int, _D, _D, _D, _D, _D, _D, _D]
     return L
 
 
@@ -224,3 +227,44 @@ def bias_grad(dz):
     db = np.zeros(C_)
     lib().oracle_bias_grad(_p(dz), dz.size // C_, C_, _p(db))
     return db
+
+
+# ------------------------------------------------------------ layer norm / group norm
+def _nsc(z):
+    """[N, OH, OW, C] -> (N, S = OH*OW, C)."""
+    N, C_ = z.shape[0], z.shape[-1]
+    return N, z.size // (N * C_), C_
+
+
+def group_stats(z, groups=1, eps=1e-5):
+    """Per-sample, per-channel-group statistics of z [N, OH, OW, C] (groups=1: layer norm).
+    Returns (mean, var, inv_std), each [N, groups]."""
+    z = _f64(z)
+    N, S, C_ = _nsc(z)
+    assert C_ % groups == 0
+    mean, var, inv = np.zeros((N, groups)), np.zeros((N, groups)), np.zeros((N, groups))
+    lib().oracle_group_stats(_p(z), N, S, C_, groups, eps, _p(mean), _p(var), _p(inv))
+    return mean, var, inv
+
+
+def apply_group_norm(z, act, gamma, beta, mean, inv_std):
+    """y = act(gamma[c] * (z - mean[n, g]) * inv_std[n, g] + beta[c]); groups from mean's shape."""
+    z = _f64(z)
+    N, S, C_ = _nsc(z)
+    mean, inv_std = _f64(mean).reshape(N, -1), _f64(inv_std).reshape(N, -1)
+    y = np.zeros_like(z)
+    lib().oracle_apply_group_norm(_p(z), N, S, C_, mean.shape[1], act, _p(_f64(gamma)), _p(_f64(beta)), _p(mean),
+                                  _p(inv_std), _p(y))
+    return y
+
+
+def group_norm_backward(z, dy, act, gamma, beta, mean, inv_std):
+    """Training backward through group (layer) norm + activation: (dz, dgamma, dbeta)."""
+    z, dy = _f64(z), _f64(dy)
+    assert z.shape == dy.shape
+    N, S, C_ = _nsc(z)
+    mean, inv_std = _f64(mean).reshape(N, -1), _f64(inv_std).reshape(N, -1)
+    dz, dg, dbt = np.zeros_like(z), np.zeros(C_), np.zeros(C_)
+    lib().oracle_group_norm_backward(_p(z), _p(dy), N, S, C_, mean.shape[1], act, _p(_f64(gamma)), _p(_f64(beta)),
+                                     _p(mean), _p(inv_std), _p(dz), _p(dg), _p(dbt))
+    return dz, dg, dbt

@@ -17,6 +17,8 @@
  *   [cuda]    "rl_tools/nn/layers/conv2d/operations_cuda.h"    (hyperray 0.0.1 wheel)
  *   [mkl]     "rl_tools/nn/layers/conv2d/operations_cpu_mkl.h" (hyperray 0.0.1 wheel)
  *   [wgsl]    "conv2d_backward_weight.wgsl" (@simulatte/doppler 0.1.0)
+ *   [doppler] the @simulatte/doppler 0.1.0 backward kernels "groupnorm_backward.wgsl"
+ *             and "gelu_backward.wgsl" (same page as [wgsl])
  *
  * Layouts (the pages' dense row-major NHWC activations and OHWI weights):
  *   x  [N][H][W][IC], w [OC][KH][KW][IC], z/y/dy/dz [N][OH][OW][OC], dx like x,
@@ -37,8 +39,8 @@
 
 typedef int64_t i64;
 
-enum { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_TANH = 2, ACT_SIGMOID = 3 };
-enum { NORM_NONE = 0, NORM_BATCH = 1 };
+enum { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_TANH = 2, ACT_SIGMOID = 3, ACT_GELU = 4 };
+enum { NORM_NONE = 0, NORM_BATCH = 1, NORM_LAYER = 2, NORM_GROUP = 3 };
 
 int oracle_num_threads(void) {
 #ifdef _OPENMP
@@ -60,23 +62,39 @@ i64 oracle_out_extent(i64 in, i64 k, i64 s, i64 p) {
 }
 
 /* ---------------------------------------------------------------- activations ---- */
-/* [mkl] make_activation_post_ops: the activation set is identity, relu, tanh, sigmoid. */
+/* [mkl] make_activation_post_ops: the activation set is identity, relu, tanh, sigmoid.
+ * [doppler] gelu_backward adds GELU in its tanh form:
+ *   gelu(a) = a/2 * (1 + tanh(u)),  u = sqrt(2/pi) * (a + 0.044715 a^3). */
+static const double GELU_K1 = 0.044715;
+static const double ORACLE_PI = 3.14159265358979323846;
+
+static double gelu_u(double a) { return sqrt(2.0 / ORACLE_PI) * (a + GELU_K1 * a * a * a); }
+
 static double act_value(int act, double a) {
     switch (act) {
     case ACT_RELU: return a > 0.0 ? a : 0.0;
     case ACT_TANH: return tanh(a);
     case ACT_SIGMOID: return 1.0 / (1.0 + exp(-a));
+    case ACT_GELU: return 0.5 * a * (1.0 + tanh(gelu_u(a)));
     default: return a;
     }
 }
 
 /* Derivative d act(a) / da, evaluated at the activation input a ([generic]
- * backward_input applies d_activation_d_x to the pre-activation).  relu'(0) = 0. */
+ * backward_input applies d_activation_d_x to the pre-activation).  relu'(0) = 0.
+ * GELU, by the product and chain rules on the definition above:
+ *   gelu'(a) = (1 + t)/2 + a/2 * (1 - t^2) * du/da,  t = tanh(u),
+ *   du/da = sqrt(2/pi) * (1 + 3 * 0.044715 a^2). */
 static double act_slope(int act, double a) {
     switch (act) {
     case ACT_RELU: return a > 0.0 ? 1.0 : 0.0;
     case ACT_TANH: { double t = tanh(a); return 1.0 - t * t; }
     case ACT_SIGMOID: { double s = 1.0 / (1.0 + exp(-a)); return s * (1.0 - s); }
+    case ACT_GELU: {
+        double t = tanh(gelu_u(a));
+        double du = sqrt(2.0 / ORACLE_PI) * (1.0 + 3.0 * GELU_K1 * a * a);
+        return 0.5 * (1.0 + t) + 0.5 * a * (1.0 - t * t) * du;
+    }
     default: return 1.0;
     }
 }
@@ -252,6 +270,108 @@ void oracle_activation_backward_eval(const double* z, const double* dy, i64 M, i
             sg += dno * zh;
             sb += dno;
         }
+        if (dgamma) dgamma[c] = sg;
+        if (dbeta) dbeta[c] = sb;
+    }
+}
+
+/* ------------------------------------------- layer norm and group norm ---- */
+/* Statistics per sample n and channel group g (channels g*C/G .. (g+1)*C/G - 1) over the
+ * S = OH*OW pixels of the sample, z [N][S][C]:
+ *   cnt = S*C/G,  mean = sum z / cnt,  var = sum (z - mean)^2 / cnt (biased),
+ *   inv_std = 1/sqrt(var + eps);  stored at [n*G + g].
+ * LayerNorm is G = 1: all OH*OW*OC values of a sample ([generic] forward, layer-norm
+ * branch: per-sample mean, then variance, two passes).  [doppler] groupnorm_backward
+ * recomputes the same per-group statistics of its input.  No running statistics. */
+void oracle_group_stats(const double* z, i64 N, i64 S, i64 C, i64 G, double eps,
+                        double* mean, double* var, double* inv_std) {
+    const i64 cg = C / G;
+    const double cnt = (double)(S * cg);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (i64 n = 0; n < N; ++n)
+        for (i64 g = 0; g < G; ++g) {
+            double s = 0.0;
+            for (i64 p = 0; p < S; ++p)
+                for (i64 k = 0; k < cg; ++k) s += z[(n * S + p) * C + g * cg + k];
+            double mu = s / cnt;
+            double q = 0.0;
+            for (i64 p = 0; p < S; ++p)
+                for (i64 k = 0; k < cg; ++k) {
+                    double d = z[(n * S + p) * C + g * cg + k] - mu;
+                    q += d * d;
+                }
+            double v = q / cnt;
+            mean[n * G + g] = mu;
+            if (var) var[n * G + g] = v;
+            inv_std[n * G + g] = 1.0 / sqrt(v + eps);
+        }
+}
+
+/* a = gamma[c] * (z - mean[n,g]) * inv_std[n,g] + beta[c];  y = act(a), g = c / (C/G).
+ * gamma and beta are per channel, as the [generic] layer-norm branch indexes them. */
+void oracle_apply_group_norm(const double* z, i64 N, i64 S, i64 C, i64 G, int act,
+                             const double* gamma, const double* beta,
+                             const double* mean, const double* inv_std, double* y) {
+    const i64 cg = C / G;
+#pragma omp parallel for schedule(static)
+    for (i64 n = 0; n < N; ++n)
+        for (i64 p = 0; p < S; ++p)
+            for (i64 c = 0; c < C; ++c) {
+                i64 i = (n * S + p) * C + c, st = n * G + c / cg;
+                double a = gamma[c] * ((z[i] - mean[st]) * inv_std[st]) + beta[c];
+                y[i] = act_value(act, a);
+            }
+}
+
+/* Training backward through the group normalisation and the activation, per sample n
+ * and group g over its cnt = S*C/G values ([generic] backward_input / backward,
+ * two-phase normalisation backward with the per-sample statistics index; [doppler]
+ * groupnorm_backward, whose dx has the same form):
+ *   zhat = (z - mean) * inv_std,  a = gamma[c]*zhat + beta[c],  dno = act'(a) * dy,
+ *   dzhat = dno * gamma[c],  S1 = sum dzhat,  S2 = sum dzhat*zhat   (over the group),
+ *   dz = inv_std / cnt * (cnt*dzhat - S1 - zhat*S2);
+ *   per channel over all samples and pixels: dgamma = sum dno*zhat, dbeta = sum dno
+ * (written, not accumulated).  dgamma/dbeta may be NULL. */
+void oracle_group_norm_backward(const double* z, const double* dy, i64 N, i64 S, i64 C, i64 G, int act,
+                                const double* gamma, const double* beta,
+                                const double* mean, const double* inv_std,
+                                double* dz, double* dgamma, double* dbeta) {
+    const i64 cg = C / G;
+    const double cnt = (double)(S * cg);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (i64 n = 0; n < N; ++n)
+        for (i64 g = 0; g < G; ++g) {
+            const i64 st = n * G + g;
+            const double mu = mean[st], is = inv_std[st];
+            double s1 = 0.0, s2 = 0.0;
+            for (i64 p = 0; p < S; ++p)
+                for (i64 k = 0; k < cg; ++k) {
+                    i64 c = g * cg + k, i = (n * S + p) * C + c;
+                    double zh = (z[i] - mu) * is;
+                    double dzh = act_slope(act, gamma[c] * zh + beta[c]) * dy[i] * gamma[c];
+                    s1 += dzh;
+                    s2 += dzh * zh;
+                }
+            for (i64 p = 0; p < S; ++p)
+                for (i64 k = 0; k < cg; ++k) {
+                    i64 c = g * cg + k, i = (n * S + p) * C + c;
+                    double zh = (z[i] - mu) * is;
+                    double dzh = act_slope(act, gamma[c] * zh + beta[c]) * dy[i] * gamma[c];
+                    dz[i] = is / cnt * (cnt * dzh - s1 - zh * s2);
+                }
+        }
+    if (!dgamma && !dbeta) return;
+#pragma omp parallel for schedule(static)
+    for (i64 c = 0; c < C; ++c) {
+        double sg = 0.0, sb = 0.0;
+        for (i64 n = 0; n < N; ++n)
+            for (i64 p = 0; p < S; ++p) {
+                i64 i = (n * S + p) * C + c, st = n * G + c / cg;
+                double zh = (z[i] - mean[st]) * inv_std[st];
+                double dno = act_slope(act, gamma[c] * zh + beta[c]) * dy[i];
+                sg += dno * zh;
+                sb += dno;
+            }
         if (dgamma) dgamma[c] = sg;
         if (dbeta) dbeta[c] = sb;
     }

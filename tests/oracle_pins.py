@@ -466,4 +466,150 @@ def pin_bn_eval_backward_fd_and_closed_form():
     _close(dg1, (dy * (z - rm)).reshape(-1, 3).sum(0), 1e-13, "eval dgamma closed form")
 
 
+# ---------------------------------------------------------------- GELU (tanh form)
+def pin_gelu_values_and_slope():
+    """gelu against torch's tanh-form GELU in fp64 (values, autograd slope); closed forms
+    gelu(0) = 0, gelu'(0) = 1/2; far tails: gelu(a) -> a and slope -> 1 for a >> 0,
+    gelu(a) -> 0 and slope -> 0 for a << 0."""
+    a = np.linspace(-7, 7, 141).reshape(1, 141, 1, 1)
+    at = torch.from_numpy(a).clone().requires_grad_(True)
+    ref = F.gelu(at, approximate="tanh")
+    _close(O.apply_activation(a, O.ACT_GELU), ref.detach().numpy(), 1e-15, "gelu values")
+    dy = _rng(60).standard_normal(a.shape)
+    ref.backward(torch.from_numpy(dy))
+    dz, *_ = O.activation_backward(a, dy, O.ACT_GELU)
+    _close(dz, at.grad.numpy(), 1e-14, "gelu slope")
+    one = np.ones((1, 1, 1, 1))
+    assert O.apply_activation(0 * one, O.ACT_GELU)[0, 0, 0, 0] == 0.0
+    assert abs(O.activation_backward(0 * one, one, O.ACT_GELU)[0][0, 0, 0, 0] - 0.5) < 1e-16
+    big = np.array([8.0, 12.0, -8.0, -12.0]).reshape(1, 4, 1, 1)
+    np.testing.assert_allclose(O.apply_activation(big, O.ACT_GELU).ravel(), [8.0, 12.0, 0.0, 0.0], atol=1e-12)
+    np.testing.assert_allclose(O.activation_backward(big, np.ones_like(big), O.ACT_GELU)[0].ravel(),
+                               [1.0, 1.0, 0.0, 0.0], atol=1e-12)
+
+
+def pin_gelu_slope_finite_differences():
+    a = np.linspace(-4, 4, 33).reshape(1, 33, 1, 1)
+    h = 1e-6
+    fd = (O.apply_activation(a + h, O.ACT_GELU) - O.apply_activation(a - h, O.ACT_GELU)) / (2 * h)
+    dz, *_ = O.activation_backward(a, np.ones_like(a), O.ACT_GELU)
+    _close(dz, fd, 1e-8, "gelu slope vs central differences")
+
+
+# ---------------------------------------------------------------- layer norm / group norm
+ACT_FNS = ((O.ACT_IDENTITY, lambda t: t), (O.ACT_RELU, torch.relu), (O.ACT_TANH, torch.tanh),
+           (O.ACT_SIGMOID, torch.sigmoid), (O.ACT_GELU, lambda t: F.gelu(t, approximate="tanh")))
+
+
+def _gn_problem(seed, shape=(3, 4, 5, 6)):
+    r = _rng(seed)
+    C = shape[-1]
+    z = r.standard_normal(shape) * r.uniform(0.3, 3, C) + r.uniform(-1, 1, C)
+    z += r.uniform(-2, 2, (shape[0], 1, 1, 1))  # per-sample offsets
+    g, bt = r.uniform(0.5, 1.5, C), r.normal(0, 0.3, C)
+    dy = r.standard_normal(shape)
+    return z, g, bt, dy
+
+
+def pin_group_stats_vs_numpy():
+    """Per (sample, group) mean / biased var / inv_std against numpy on the reshaped
+    tensor; layer norm (one group) over each sample's whole OH*OW*C block."""
+    z, *_ = _gn_problem(61)
+    N, C = z.shape[0], z.shape[-1]
+    for G in (1, 2, 3, 6):
+        mean, var, inv = O.group_stats(z, G, 1e-5)
+        blk = z.reshape(N, -1, G, C // G).transpose(0, 2, 1, 3).reshape(N, G, -1)
+        _close(mean, blk.mean(-1), 1e-13, f"group mean G={G}")
+        _close(var, blk.var(-1, ddof=0), 1e-13, f"group var G={G}")
+        _close(inv, 1.0 / np.sqrt(blk.var(-1) + 1e-5), 1e-13, f"group inv_std G={G}")
+    mean, var, _ = O.group_stats(z, 1)
+    _close(mean[:, 0], z.reshape(N, -1).mean(1), 1e-13, "layer-norm mean")
+    _close(var[:, 0], z.reshape(N, -1).var(1), 1e-13, "layer-norm var")
+
+
+def pin_group_stats_one_channel_groups_are_batch_stats_per_sample():
+    """With one channel per group (G = C) the statistics of sample n are the batch-norm
+    statistics of that sample alone (another oracle routine, pinned on its own)."""
+    z, *_ = _gn_problem(62)
+    C = z.shape[-1]
+    mean, var, inv = O.group_stats(z, C, 1e-5)
+    for n in range(z.shape[0]):
+        bm, bv, bi, *_ = O.bn_stats(z[n:n + 1], 0.1, 1e-5)
+        _close(mean[n], bm, 1e-13, "G=C mean")
+        _close(var[n], bv, 1e-13, "G=C var")
+        _close(inv[n], bi, 1e-13, "G=C inv_std")
+
+
+def pin_group_norm_forward_vs_torch():
+    """y against torch fp64 group_norm (per-channel affine) + activation; layer norm also
+    against layer_norm over (C, H, W) with the per-channel affine applied after."""
+    z, g, bt, _ = _gn_problem(63)
+    zt = torch.from_numpy(z).permute(0, 3, 1, 2)
+    for G in (1, 2, 6):
+        mean, _, inv = O.group_stats(z, G, 1e-5)
+        for act, fn in ACT_FNS:
+            ref = fn(F.group_norm(zt, G, torch.from_numpy(g), torch.from_numpy(bt), eps=1e-5))
+            _close(O.apply_group_norm(z, act, g, bt, mean, inv), ref.permute(0, 2, 3, 1).numpy(), 1e-12,
+                   f"group norm G={G} act {act}")
+    mean, _, inv = O.group_stats(z, 1, 1e-5)
+    ln = F.layer_norm(zt, zt.shape[1:], eps=1e-5) * torch.from_numpy(g)[:, None, None] + \
+        torch.from_numpy(bt)[:, None, None]
+    _close(O.apply_group_norm(z, O.ACT_IDENTITY, g, bt, mean, inv), ln.permute(0, 2, 3, 1).numpy(), 1e-12,
+           "layer norm vs torch layer_norm")
+
+
+def pin_group_norm_normalises():
+    """Identity activation, gamma = 1, beta = 0: each (sample, group) block has mean 0 and
+    variance var/(var + eps)."""
+    z, *_ = _gn_problem(64)
+    N, C = z.shape[0], z.shape[-1]
+    for G in (1, 3):
+        mean, var, inv = O.group_stats(z, G, 1e-5)
+        y = O.apply_group_norm(z, O.ACT_IDENTITY, np.ones(C), np.zeros(C), mean, inv)
+        blk = y.reshape(N, -1, G, C // G).transpose(0, 2, 1, 3).reshape(N, G, -1)
+        np.testing.assert_allclose(blk.mean(-1), 0.0, atol=1e-13)
+        np.testing.assert_allclose(blk.var(-1), var / (var + 1e-5), rtol=1e-12)
+
+
+def pin_group_norm_backward_vs_torch_autograd():
+    """dz, dgamma, dbeta against torch fp64 autograd through group_norm + activation."""
+    for G in (1, 2, 6):
+        for act, fn in ACT_FNS:
+            z, g, bt, dy = _gn_problem(70 + 7 * G + act)
+            mean, _, inv = O.group_stats(z, G, 1e-5)
+            dz, dg, dbt = O.group_norm_backward(z, dy, act, g, bt, mean, inv)
+            zt = torch.from_numpy(z).permute(0, 3, 1, 2).clone().requires_grad_(True)
+            gt = torch.from_numpy(g).clone().requires_grad_(True)
+            btt = torch.from_numpy(bt).clone().requires_grad_(True)
+            fn(F.group_norm(zt, G, gt, btt, eps=1e-5)).backward(torch.from_numpy(dy).permute(0, 3, 1, 2))
+            _close(dz, zt.grad.permute(0, 2, 3, 1).numpy(), 1e-11, f"gn dz G={G} act {act}")
+            _close(dg, gt.grad.numpy(), 1e-11, f"gn dgamma G={G} act {act}")
+            _close(dbt, btt.grad.numpy(), 1e-11, f"gn dbeta G={G} act {act}")
+
+
+def pin_group_norm_backward_fd_and_invariants():
+    """Central differences of L(z, gamma, beta) = <act(GN(z)), dy> (statistics recomputed
+    from z) match dz, dgamma, dbeta; per (sample, group) sum dz = 0."""
+    act, G = O.ACT_GELU, 2
+    z, g, bt, dy = _gn_problem(90, (2, 2, 3, 4))
+    mean, _, inv = O.group_stats(z, G, 1e-5)
+    dz, dg, dbt = O.group_norm_backward(z, dy, act, g, bt, mean, inv)
+    blk = dz.reshape(2, -1, G, 2).transpose(0, 2, 1, 3).reshape(2, G, -1)
+    np.testing.assert_allclose(blk.sum(-1), 0.0, atol=1e-12)
+
+    def L(z_, g_, b_):
+        m_, _, i_ = O.group_stats(z_, G, 1e-5)
+        return float(np.sum(O.apply_group_norm(z_, act, g_, b_, m_, i_) * dy))
+
+    h = 1e-6
+    for idx in np.ndindex(*z.shape):
+        e = np.zeros_like(z); e[idx] = h
+        fd = (L(z + e, g, bt) - L(z - e, g, bt)) / (2 * h)
+        assert abs(fd - dz[idx]) < 1e-7, ("gn dz", idx, fd, dz[idx])
+    for c in range(4):
+        e = np.zeros(4); e[c] = h
+        assert abs((L(z, g + e, bt) - L(z, g - e, bt)) / (2 * h) - dg[c]) < 1e-7, ("gn dgamma", c)
+        assert abs((L(z, g, bt + e) - L(z, g, bt - e)) / (2 * h) - dbt[c]) < 1e-7, ("gn dbeta", c)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -57,6 +57,23 @@ MUTANTS = [
      "inv_std[c] = 1.0 / sqrt(running_var[c]);", 0),
     ("bneval_inv_std_missing", "dz[i] = dno * g * is;", "dz[i] = dno * g;", 0),
     ("bneval_dgamma_no_zhat", "sg += dno * zh;", "sg += dno;", 1),
+    ("gelu_value_cubic_dropped", "(a + GELU_K1 * a * a * a)", "(a)", 0),
+    ("gelu_slope_cubic_factor", "(1.0 + 3.0 * GELU_K1 * a * a)", "(1.0 + GELU_K1 * a * a)", 0),
+    ("gelu_slope_half_dropped", "return 0.5 * (1.0 + t) + 0.5 * a", "return (1.0 + t) + 0.5 * a", 0),
+    ("gelu_slope_sech_sign", "0.5 * a * (1.0 - t * t) * du", "0.5 * a * (1.0 + t * t) * du", 0),
+    ("gn_count_all_channels", "const double cnt = (double)(S * cg);", "const double cnt = (double)(S * C);", 0),
+    ("gn_var_unbiased", "double v = q / cnt;", "double v = q / (cnt - 1.0);", 0),
+    ("gn_group_of_channel", "i64 i = (n * S + p) * C + c, st = n * G + c / cg;",
+     "i64 i = (n * S + p) * C + c, st = n * G + c % G;", 0),
+    ("gn_apply_beta_dropped", "double a = gamma[c] * ((z[i] - mean[st]) * inv_std[st]) + beta[c];",
+     "double a = gamma[c] * ((z[i] - mean[st]) * inv_std[st]);", 0),
+    ("gn_bwd_count", "const double cnt = (double)(S * cg);", "const double cnt = (double)S;", 1),
+    ("gn_bwd_term_dropped", "dz[i] = is / cnt * (cnt * dzh - s1 - zh * s2);", "dz[i] = is / cnt * (cnt * dzh - s1);", 0),
+    ("gn_bwd_gamma_dropped", "double dzh = act_slope(act, gamma[c] * zh + beta[c]) * dy[i] * gamma[c];",
+     "double dzh = act_slope(act, gamma[c] * zh + beta[c]) * dy[i];", 0),
+    ("gn_bwd_dgamma_no_zhat", "sg += dno * zh;\n                sb += dno;", "sg += dno;\n                sb += dno;", 0),
+    ("gn_bwd_mask_at_z", "double dno = act_slope(act, gamma[c] * zh + beta[c]) * dy[i];",
+     "double dno = act_slope(act, z[i]) * dy[i];", 0),
 ]
 
 
