@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(HERE, "libconvmi.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_MISALIGNED, ERR_HIP = range(6)
 F32, BF16 = 0, 1
-ACT_IDENTITY, ACT_RELU, ACT_TANH, ACT_SIGMOID = 0, 1, 2, 3
-NORM_NONE, NORM_BATCH = 0, 1
+ACT_IDENTITY, ACT_RELU, ACT_TANH, ACT_SIGMOID, ACT_GELU = 0, 1, 2, 3, 4
+NORM_NONE, NORM_BATCH, NORM_LAYER, NORM_GROUP = 0, 1, 2, 3
 MODE_TRAIN, MODE_EVAL = 0, 1
 OP_FORWARD, OP_BACKWARD_DATA, OP_BACKWARD_WEIGHT, OP_BN_STATS, OP_ACTIVATION_BACKWARD = range(5)
 
@@ -41,7 +41,7 @@ class ConvDesc(C.Structure):
                 ("KH", C.c_int64), ("KW", C.c_int64),
                 ("stride_h", C.c_int32), ("stride_w", C.c_int32), ("pad_h", C.c_int32), ("pad_w", C.c_int32),
                 ("activation", C.c_int32), ("normalization", C.c_int32), ("mode", C.c_int32),
-                ("dtype", C.c_int32), ("momentum", C.c_float), ("eps", C.c_float)]
+                ("dtype", C.c_int32), ("momentum", C.c_float), ("eps", C.c_float), ("groups", C.c_int32)]
 
 
 class ConvmiError(RuntimeError):
@@ -81,9 +81,16 @@ def version() -> str:
 
 
 def make_desc(N, H, W, IC, OC, KH, KW, stride=(1, 1), pad=(0, 0), activation=ACT_IDENTITY,
-              normalization=NORM_NONE, mode=MODE_TRAIN, dtype=F32, momentum=0.1, eps=1e-5) -> ConvDesc:
+              normalization=NORM_NONE, mode=MODE_TRAIN, dtype=F32, momentum=0.1, eps=1e-5, groups=1) -> ConvDesc:
     return ConvDesc(N, H, W, IC, OC, KH, KW, stride[0], stride[1], pad[0], pad[1], activation, normalization,
-                    mode, dtype, momentum, eps)
+                    mode, dtype, momentum, eps, groups)
+
+
+def stat_count(desc: ConvDesc) -> int:
+    """Entries of save_mean / save_inv_std: OC (batch norm) or N * groups (layer, group)."""
+    if desc.normalization == NORM_BATCH:
+        return desc.OC
+    return desc.N * (desc.groups if desc.normalization == NORM_GROUP else 1)
 
 
 def _check(status: int):

@@ -49,17 +49,19 @@ convmi_status check_desc(const convmi_desc* d, ConvDims* out) {
     if (d->pad_h < 0 || d->pad_w < 0) return fail(CONVMI_ERR_INVALID_ARG, "padding must be >= 0");
     if (d->dtype != CONVMI_F32 && d->dtype != CONVMI_BF16)
         return fail(CONVMI_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
-    if (d->activation < CONVMI_ACT_IDENTITY || d->activation > CONVMI_ACT_SIGMOID)
+    if (d->activation < CONVMI_ACT_IDENTITY || d->activation > CONVMI_ACT_GELU)
         return fail(CONVMI_ERR_INVALID_ARG, "unknown activation %d", d->activation);
-    if (d->normalization != CONVMI_NORM_NONE && d->normalization != CONVMI_NORM_BATCH)
+    if (d->normalization < CONVMI_NORM_NONE || d->normalization > CONVMI_NORM_GROUP)
         return fail(CONVMI_ERR_INVALID_ARG, "unknown normalization %d", d->normalization);
     if (d->mode != CONVMI_MODE_TRAIN && d->mode != CONVMI_MODE_EVAL)
         return fail(CONVMI_ERR_INVALID_ARG, "unknown mode %d", d->mode);
-    if (d->normalization == CONVMI_NORM_BATCH) {
-        if (!(d->momentum >= 0.0f && d->momentum <= 1.0f))
-            return fail(CONVMI_ERR_INVALID_ARG, "momentum must be in [0, 1]");
-        if (!(d->eps > 0.0f)) return fail(CONVMI_ERR_INVALID_ARG, "eps must be > 0");
-    }
+    if (d->normalization == CONVMI_NORM_BATCH && !(d->momentum >= 0.0f && d->momentum <= 1.0f))
+        return fail(CONVMI_ERR_INVALID_ARG, "momentum must be in [0, 1]");
+    if (d->normalization != CONVMI_NORM_NONE && !(d->eps > 0.0f))
+        return fail(CONVMI_ERR_INVALID_ARG, "eps must be > 0");
+    if (d->normalization == CONVMI_NORM_GROUP && (d->groups < 1 || d->OC % d->groups != 0))
+        return fail(CONVMI_ERR_INVALID_ARG, "groups (%d) must be >= 1 and divide OC (%lld)", d->groups,
+                    (long long)d->OC);
     const int64_t OH = out_extent(d->H, d->KH, d->stride_h, d->pad_h);
     const int64_t OW = out_extent(d->W, d->KW, d->stride_w, d->pad_w);
     if (OH < 1 || OW < 1)
@@ -109,6 +111,12 @@ convmi_status check_ws(void* ws, size_t have, size_t want, const char* op) {
 
 int64_t rows_of(const ConvDims& d) { return (int64_t)d.N * d.OH * d.OW; }
 
+// Layer norm and group norm: per-sample statistics over channel groups.
+bool per_sample_norm(const convmi_desc* desc) {
+    return desc->normalization == CONVMI_NORM_LAYER || desc->normalization == CONVMI_NORM_GROUP;
+}
+int norm_groups(const convmi_desc* desc) { return desc->normalization == CONVMI_NORM_GROUP ? desc->groups : 1; }
+
 // Per-tile batch-norm statistics of the fused training forward, after its weight copy.
 size_t stats_offset(const convmi_desc* desc, const ConvDims& d) { return halo_fwd_ws_bytes(desc->dtype, d); }
 size_t stats_bytes(const convmi_desc* desc, const ConvDims& d) {
@@ -118,8 +126,9 @@ size_t stats_bytes(const convmi_desc* desc, const ConvDims& d) {
 size_t ws_forward(const convmi_desc* desc, const ConvDims& d) {
     size_t a = igemm_fwd_supported(desc->dtype, d) ? igemm_fwd_ws_bytes(desc->dtype, d) : 0;
     size_t b = 0;
-    if (desc->normalization == CONVMI_NORM_BATCH) {
-        b = bn_stats_ws_bytes(rows_of(d), d.OC, desc->dtype);
+    if (desc->normalization != CONVMI_NORM_NONE) {
+        b = per_sample_norm(desc) ? grp_stats_ws_bytes(d.N, (int64_t)d.OH * d.OW, d.OC, desc->dtype)
+                                  : bn_stats_ws_bytes(rows_of(d), d.OC, desc->dtype);
         if (halo_fwd_supported(desc->dtype, d)) {
             const size_t c = stats_offset(desc, d) + stats_bytes(desc, d);
             if (c > b) b = c;
@@ -134,9 +143,12 @@ size_t ws_backward_weight(const convmi_desc* desc, const ConvDims& d) {
     return igemm_dw_supported(desc->dtype, d) ? igemm_dw_ws_bytes(desc->dtype, d) : 0;
 }
 size_t ws_bn_stats(const convmi_desc* desc, const ConvDims& d) {
+    if (per_sample_norm(desc)) return grp_stats_ws_bytes(d.N, (int64_t)d.OH * d.OW, d.OC, desc->dtype);
     return bn_stats_ws_bytes(rows_of(d), d.OC, desc->dtype);
 }
 size_t ws_act_bwd(const convmi_desc* desc, const ConvDims& d) {
+    if (per_sample_norm(desc))
+        return grp_bwd_ws_bytes(d.N, (int64_t)d.OH * d.OW, d.OC, norm_groups(desc), desc->dtype);
     return desc->normalization == CONVMI_NORM_BATCH ? bn_bwd_ws_bytes(rows_of(d), d.OC, desc->dtype) : 0;
 }
 
@@ -195,6 +207,7 @@ convmi_status forward_impl(const convmi_desc* desc, const ConvDims& d, const voi
     CHECK(need(y, "y"));
     if (bias) CHECK(need_vec(bias, "bias"));
     const bool bn = desc->normalization == CONVMI_NORM_BATCH;
+    const bool psn = per_sample_norm(desc);
     const size_t es = dtype_size(desc->dtype);
     const size_t ybytes = (size_t)rows_of(d) * d.OC * es;
     if (bn) {
@@ -211,6 +224,14 @@ convmi_status forward_impl(const convmi_desc* desc, const ConvDims& d, const voi
             CHECK(need_vec(running_mean, "running_mean"));
             CHECK(need_vec(running_var, "running_var"));
         }
+    } else if (psn) {
+        CHECK(need(z, "z (required with layer / group norm)"));
+        CHECK(need_vec(gamma, "gamma"));
+        CHECK(need_vec(beta, "beta"));
+        CHECK(need_vec(save_mean, "save_mean"));
+        CHECK(need_vec(save_inv_std, "save_inv_std"));
+        if (running_mean || running_var)
+            return fail(CONVMI_ERR_INVALID_ARG, "layer / group norm keep no running statistics: pass NULL");
     } else if (z) {
         CHECK(need(z, "z"));
     }
@@ -221,6 +242,29 @@ convmi_status forward_impl(const convmi_desc* desc, const ConvDims& d, const voi
     hipStream_t s = (hipStream_t)stream;
     const int act = desc->activation;
     hipError_t e;
+    // Layer / group norm: z (with per-tile statistics from the stride-1 epilogue when that
+    // path runs), the per-sample group statistics, then normalise + activate.
+    if (psn) {
+        const int G = norm_groups(desc);
+        const int64_t S = (int64_t)d.OH * d.OW;
+        if (halo_fwd_supported(desc->dtype, d)) {
+            float* part = (float*)((char*)workspace + stats_offset(desc, d));
+            e = launch_halo_fwd(desc->dtype, x, w, bias, z, nullptr, d, act, workspace, s, nullptr, part);
+            if (e != hipSuccess) return hip_fail(e, "conv2d_forward: convolution launch");
+            e = launch_grp_tiles_finalize(part, halo_fwd_stat_tiles(desc->dtype, d), d.N, d.OC, G, S, desc->eps,
+                                          save_mean, save_inv_std, s);
+        } else {
+            e = igemm_fwd_supported(desc->dtype, d)
+                    ? launch_igemm_fwd(desc->dtype, x, w, bias, z, nullptr, d, act, workspace, s)
+                    : launch_conv_fwd_direct(desc->dtype, x, w, bias, z, nullptr, d, act, s);
+            if (e != hipSuccess) return hip_fail(e, "conv2d_forward: convolution launch");
+            e = launch_grp_stats(desc->dtype, z, d.N, S, d.OC, G, desc->eps, save_mean, save_inv_std, workspace, s);
+        }
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: normalisation statistics launch");
+        e = launch_grp_apply(desc->dtype, z, y, d.N, S, d.OC, G, act, gamma, beta, save_mean, save_inv_std, s);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_forward: normalise/activate launch");
+        return CONVMI_OK;
+    }
     // Without batch norm the activation is fused into the convolution's epilogue; so is
     // evaluation-mode batch norm on the input-tile-reuse path (its statistics are known
     // before the convolution runs).
@@ -370,8 +414,20 @@ CONVMI_API convmi_status bn_stats_training(const convmi_desc* desc, const void* 
                                 void* workspace, size_t workspace_bytes, void* stream) {
     ConvDims d;
     CHECK(check_desc(desc, &d));
-    if (desc->normalization != CONVMI_NORM_BATCH)
-        return fail(CONVMI_ERR_INVALID_ARG, "bn_stats_training needs normalization = BATCH");
+    if (desc->normalization == CONVMI_NORM_NONE)
+        return fail(CONVMI_ERR_INVALID_ARG, "bn_stats_training needs a normalization");
+    if (per_sample_norm(desc)) {
+        CHECK(need(z, "z"));
+        CHECK(need_vec(save_mean, "save_mean"));
+        CHECK(need_vec(save_inv_std, "save_inv_std"));
+        if (running_mean || running_var)
+            return fail(CONVMI_ERR_INVALID_ARG, "layer / group norm keep no running statistics: pass NULL");
+        CHECK(check_ws(workspace, workspace_bytes, ws_bn_stats(desc, d), "bn_stats_training"));
+        hipError_t e = launch_grp_stats(desc->dtype, z, d.N, (int64_t)d.OH * d.OW, d.OC, norm_groups(desc), desc->eps,
+                                        save_mean, save_inv_std, workspace, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "bn_stats_training launch");
+        return CONVMI_OK;
+    }
     if (desc->mode != CONVMI_MODE_TRAIN)
         return fail(CONVMI_ERR_INVALID_ARG,
                     "bn_stats_training computes training statistics; in evaluation mode conv2d_forward uses the "
@@ -408,7 +464,18 @@ CONVMI_API convmi_status activation_backward(const convmi_desc* desc, const void
     if (overlaps(dz, bytes, z, bytes)) return fail(CONVMI_ERR_INVALID_ARG, "dz overlaps z");
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (desc->normalization == CONVMI_NORM_BATCH) {
+    if (per_sample_norm(desc)) {
+        CHECK(need_vec(gamma, "gamma"));
+        CHECK(need_vec(beta, "beta"));
+        CHECK(need_vec(save_mean, "save_mean"));
+        CHECK(need_vec(save_inv_std, "save_inv_std"));
+        if (dgamma) CHECK(need_vec(dgamma, "dgamma"));
+        if (dbeta) CHECK(need_vec(dbeta, "dbeta"));
+        CHECK(check_ws(workspace, workspace_bytes, ws_act_bwd(desc, d), "activation_backward"));
+        e = launch_grp_bwd(desc->dtype, z, dy, dz, d.N, (int64_t)d.OH * d.OW, d.OC, norm_groups(desc),
+                           desc->activation, gamma, beta, save_mean, save_inv_std, dgamma, dbeta, accumulate,
+                           workspace, s);
+    } else if (desc->normalization == CONVMI_NORM_BATCH) {
         CHECK(need_vec(gamma, "gamma"));
         CHECK(need_vec(beta, "beta"));
         CHECK(need_vec(save_mean, "save_mean"));

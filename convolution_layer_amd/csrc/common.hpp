@@ -6,7 +6,7 @@
 
 namespace convmi {
 
-enum Act : int { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_TANH = 2, ACT_SIGMOID = 3 };
+enum Act : int { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_TANH = 2, ACT_SIGMOID = 3, ACT_GELU = 4 };
 
 // bf16 values travel as raw 16-bit patterns.
 typedef uint16_t bf16;
@@ -69,19 +69,33 @@ __device__ __forceinline__ float fast_tanh(float a) {
 // 1 / (1 + exp(-a)); the exponential saturates to inf for a < -88, giving 0.
 __device__ __forceinline__ float fast_sigmoid(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
+// GELU, tanh form (the @simulatte/doppler "gelu_backward.wgsl" kernel):
+// gelu(a) = a/2 (1 + tanh(u)), u = sqrt(2/pi) (a + 0.044715 a^3).  fast_tanh saturates
+// to +-1 for large |u| without overflow, so no clamp of u is needed.
+constexpr float kGeluK0 = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float kGeluK1 = 0.044715f;
+__device__ __forceinline__ float gelu_t(float a) { return fast_tanh(kGeluK0 * __builtin_fmaf(kGeluK1 * a, a * a, a)); }
+
 // act(a)
 template <int ACT> __device__ __forceinline__ float act_fwd(float a) {
     if constexpr (ACT == ACT_RELU) return a > 0.0f ? a : 0.0f;
     else if constexpr (ACT == ACT_TANH) return fast_tanh(a);
     else if constexpr (ACT == ACT_SIGMOID) return fast_sigmoid(a);
+    else if constexpr (ACT == ACT_GELU) { const float h = 0.5f * a; return __builtin_fmaf(h, gelu_t(a), h); }
     else return a;
 }
 
-// d act / d a at a.  relu'(0) = 0.
+// d act / d a at a.  relu'(0) = 0.  gelu'(a) = (1 + t)/2 + a/2 (1 - t^2) du/da with
+// du/da = sqrt(2/pi) (1 + 3 * 0.044715 a^2) (product and chain rules on the form above).
 template <int ACT> __device__ __forceinline__ float act_slope(float a) {
     if constexpr (ACT == ACT_RELU) return a > 0.0f ? 1.0f : 0.0f;
     else if constexpr (ACT == ACT_TANH) { float t = fast_tanh(a); return 1.0f - t * t; }
     else if constexpr (ACT == ACT_SIGMOID) { float s = fast_sigmoid(a); return s * (1.0f - s); }
+    else if constexpr (ACT == ACT_GELU) {
+        const float t = gelu_t(a);
+        const float du = kGeluK0 * __builtin_fmaf(3.0f * kGeluK1 * a, a, 1.0f);
+        return __builtin_fmaf(0.5f * a * du, __builtin_fmaf(-t, t, 1.0f), 0.5f + 0.5f * t);
+    }
     else return 1.0f;
 }
 
@@ -100,6 +114,7 @@ __device__ __forceinline__ float bn_affine(float z, float mean, float inv_std, f
     case ACT_RELU: { constexpr int ACTV = ACT_RELU; __VA_ARGS__; } break;   \
     case ACT_TANH: { constexpr int ACTV = ACT_TANH; __VA_ARGS__; } break;   \
     case ACT_SIGMOID: { constexpr int ACTV = ACT_SIGMOID; __VA_ARGS__; } break; \
+    case ACT_GELU: { constexpr int ACTV = ACT_GELU; __VA_ARGS__; } break;   \
     default: { constexpr int ACTV = ACT_IDENTITY; __VA_ARGS__; } break;     \
     }
 

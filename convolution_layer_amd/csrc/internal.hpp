@@ -38,8 +38,12 @@ struct RowPlan {
     int chunks;           // channel slices (grid.y)
     int64_t rows_per_block;
     int blocks;           // row slabs (grid.x)
+    int bps;              // slabs per segment (all of them for batch norm)
+    int64_t seg;          // rows per segment: 0 = all M rows (batch norm), S (per-sample norms)
 };
 RowPlan row_plan(int64_t M, int C, int dt);
+// Layer / group norm: each sample's S = OH*OW rows are a segment of their own.
+RowPlan seg_plan(int N, int64_t S, int C, int dt);
 size_t bn_stats_ws_bytes(int64_t M, int C, int dt);
 size_t bn_bwd_ws_bytes(int64_t M, int C, int dt);
 
@@ -58,6 +62,24 @@ hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_
                          float* dgamma, float* dbeta, int accumulate, int evaluation, void* ws, hipStream_t s);
 hipError_t launch_bn_eval_stats(const float* run_mean, const float* run_var, int C, float eps, float* mean,
                                 float* inv_std, hipStream_t s);
+
+// Layer norm (G = 1) and group norm: statistics per sample n and group of C/G
+// consecutive channels over the sample's S = OH*OW rows of z [N][S][C], stored at
+// [n*G + g]; gamma/beta per channel.
+size_t grp_stats_ws_bytes(int N, int64_t S, int C, int dt);
+size_t grp_bwd_ws_bytes(int N, int64_t S, int C, int G, int dt);
+hipError_t launch_grp_stats(int dt, const void* z, int N, int64_t S, int C, int G, float eps, float* mean,
+                            float* inv_std, void* ws, hipStream_t s);
+// From the per-tile statistics of the stride-1 forward's epilogue (tiles of one image
+// are consecutive, ntiles / N of them per image).
+hipError_t launch_grp_tiles_finalize(const float* part, int ntiles, int N, int C, int G, int64_t S, float eps,
+                                     float* mean, float* inv_std, hipStream_t s);
+hipError_t launch_grp_apply(int dt, const void* z, void* y, int N, int64_t S, int C, int G, int act,
+                            const float* gamma, const float* beta, const float* mean, const float* inv_std,
+                            hipStream_t s);
+hipError_t launch_grp_bwd(int dt, const void* z, const void* dy, void* dz, int N, int64_t S, int C, int G, int act,
+                          const float* gamma, const float* beta, const float* mean, const float* inv_std,
+                          float* dgamma, float* dbeta, int accumulate, void* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- MFMA implicit GEMM
 // Returns false (and launches nothing) when the shape is outside what the tiled

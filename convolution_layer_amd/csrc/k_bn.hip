@@ -69,23 +69,33 @@ __device__ __forceinline__ void merge_rows(float* red, int rpi, int width, int r
 
 // Per-slab sums of two quantities per channel over a slab of rows, merged across the
 // workgroup's row groups in a fixed order and written to part[c][q][slab] (q = 0, 1).
-// Each lane streams UNROLL 16-byte vectors per iteration.  An accumulator with kOut
-// also produces one output element per input element (written to `out`, same layout).
+// The rows form segments of `seg` rows (one segment of all M rows for batch norm, one
+// per sample for layer and group norm), each cut into `bps` slabs of rows_per_block
+// rows: slab b covers rows of segment b / bps only.  Each lane streams UNROLL 16-byte
+// vectors per iteration.  An accumulator with kOut also produces one output element
+// per input element (written to `out`, same layout).
 template <typename T, int VEC, class Acc>
 __device__ __forceinline__ void slab_partials(const T* __restrict__ a, const T* __restrict__ b, int64_t M, int C,
                                               int tpr, int rpi, int64_t rows_per_block, Acc accf,
-                                              float* __restrict__ part, float* red, T* out = nullptr) {
+                                              float* __restrict__ part, float* red, T* out = nullptr,
+                                              int64_t seg = 0, int bps = 0) {
     constexpr int UNROLL = 4;
     const int t = threadIdx.x, cv = t % tpr, r = t / tpr;
     const int c0 = (blockIdx.y * tpr + cv) * VEC;
     const bool active = r < rpi && c0 < C;
-    const int64_t m0 = (int64_t)blockIdx.x * rows_per_block;
-    const int64_t m1 = m0 + rows_per_block < M ? m0 + rows_per_block : M;
+    if (seg == 0) {
+        seg = M;
+        bps = gridDim.x;
+    }
+    const int sid = (int)(blockIdx.x / bps);
+    const int64_t s0 = (int64_t)sid * seg, s1end = s0 + seg < M ? s0 + seg : M;
+    const int64_t m0 = s0 + (int64_t)(blockIdx.x - sid * bps) * rows_per_block;
+    const int64_t m1 = m0 + rows_per_block < s1end ? m0 + rows_per_block : s1end;
     float s1[VEC], s2[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) s1[j] = s2[j] = 0.0f;
     if (active) {
-        accf.init(c0);
+        accf.init(c0, sid, s0);
         int64_t m = m0 + r;
         for (; m + (UNROLL - 1) * rpi < m1; m += UNROLL * rpi) {
             float va[UNROLL][VEC], vb[UNROLL][VEC];
@@ -139,8 +149,10 @@ __device__ __forceinline__ void slab_partials(const T* __restrict__ a, const T* 
 template <typename T, int VEC> struct StatsAcc {
     static constexpr bool kOut = false;
     const T* z;
+    int C;
     float sh[VEC];
-    __device__ __forceinline__ void init(int c0) { Vec<T, VEC>::load(z + c0, sh); }
+    // shift: the segment's first row
+    __device__ __forceinline__ void init(int c0, int, int64_t row0) { Vec<T, VEC>::load(z + row0 * C + c0, sh); }
     __device__ __forceinline__ void add(const float* v, const float*, float* s1, float* s2) const {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
@@ -156,7 +168,7 @@ template <typename T, int VEC, int ACT> struct BwdAcc {
     static constexpr bool kOut = false;
     const float *gamma, *beta, *mean, *inv_std;
     float g[VEC], bt[VEC], mu[VEC], is[VEC];
-    __device__ __forceinline__ void init(int c0) {
+    __device__ __forceinline__ void init(int c0, int, int64_t) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
             g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j]; mu[j] = mean[c0 + j]; is[j] = inv_std[c0 + j];
@@ -180,7 +192,7 @@ template <typename T, int VEC, int ACT> struct EvalBwdAcc {
     static constexpr bool kOut = true;
     const float *gamma, *beta, *mean, *inv_std;
     float g[VEC], bt[VEC], mu[VEC], is[VEC];
-    __device__ __forceinline__ void init(int c0) {
+    __device__ __forceinline__ void init(int c0, int, int64_t) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
             g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j]; mu[j] = mean[c0 + j]; is[j] = inv_std[c0 + j];
@@ -242,10 +254,10 @@ __device__ __forceinline__ void merge_slabs(const float* __restrict__ part, int 
 template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void bn_stats_partials(const T* __restrict__ z, int64_t M, int C, int tpr,
                                                               int rpi, int64_t rows_per_block,
-                                                              float* __restrict__ part) {
+                                                              float* __restrict__ part, int64_t seg, int bps) {
     extern __shared__ float red[];
-    StatsAcc<T, VEC> acc{z, {}};
-    slab_partials<T, VEC>(z, (const T*)nullptr, M, C, tpr, rpi, rows_per_block, acc, part, red);
+    StatsAcc<T, VEC> acc{z, C, {}};
+    slab_partials<T, VEC>(z, (const T*)nullptr, M, C, tpr, rpi, rows_per_block, acc, part, red, nullptr, seg, bps);
 }
 
 // Statistics from the slab partials (one workgroup per kThreads/P2 channels):
@@ -369,6 +381,282 @@ __global__ __launch_bounds__(kThreads) void bn_bwd_finalize(const float* __restr
         coef[3 * c + 1] = evaluation ? 0.0f : (float)(A / (double)M);
         coef[3 * c + 2] = evaluation ? 0.0f : (float)(B / (double)M);
     });
+}
+
+// ------------------------------------------------------------ layer norm / group norm
+// Statistics per sample n and group g of Cg = C/G consecutive channels (layer norm:
+// G = 1), over the S = OH*OW rows of the sample: the rows of a sample form one segment
+// of the slab partials, and the merges below combine channels as well as slabs.
+
+// Fixed-order sum over the workgroup; every thread gets the result.
+__device__ __forceinline__ double block_sum(double v, double* dred) {
+    const int t = threadIdx.x;
+    dred[t] = v;
+    __syncthreads();
+    for (int h = kThreads / 2; h > 0; h >>= 1) {
+        if (t < h) dred[t] += dred[t + h];
+        __syncthreads();
+    }
+    const double r = dred[0];
+    __syncthreads();
+    return r;
+}
+
+// Group statistics from the per-sample slab partials (bps slabs per sample; shifts =
+// each sample's first row): one workgroup per (n, g).  Channel c of the group:
+// mean_c = s_c + S1_c/S, M2_c = S2_c - S1_c^2/S (fp64, slabs in order); then
+// mean = sum mean_c / Cg and var = sum [M2_c + S (mean_c - mean)^2] / (S Cg).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void grp_stats_finalize(const float* __restrict__ part, int bps, int C, int G,
+                                                               const T* __restrict__ z, int64_t S, float eps,
+                                                               float* __restrict__ mean, float* __restrict__ inv_std) {
+    __shared__ double dred[kThreads];
+    const int ng = blockIdx.x, n = ng / G, g = ng - n * G, cg = C / G, t = threadIdx.x;
+    const int nslab = bps;
+    const int64_t total_slabs = (int64_t)nslab * (gridDim.x / G);  // N * bps
+    double msum = 0.0;
+    for (int k = t; k < cg; k += kThreads) {
+        const int c = g * cg + k;
+        const float* p1 = part + (int64_t)c * 2 * total_slabs + (int64_t)n * nslab;
+        double a = 0.0;
+        for (int j = 0; j < nslab; ++j) a += (double)p1[j];
+        msum += (double)to_f32(z[(int64_t)n * S * C + c]) + a / (double)S;
+    }
+    const double mu = block_sum(msum, dred) / (double)cg;
+    double m2 = 0.0;
+    for (int k = t; k < cg; k += kThreads) {
+        const int c = g * cg + k;
+        const float* p1 = part + (int64_t)c * 2 * total_slabs + (int64_t)n * nslab;
+        double a = 0.0, b = 0.0;
+        for (int j = 0; j < nslab; ++j) {
+            a += (double)p1[j];
+            b += (double)p1[total_slabs + j];
+        }
+        const double mc = (double)to_f32(z[(int64_t)n * S * C + c]) + a / (double)S;
+        m2 += (b - a * a / (double)S) + (double)S * (mc - mu) * (mc - mu);
+    }
+    double var = block_sum(m2, dred) / ((double)S * cg);
+    if (var < 0.0) var = 0.0;
+    if (t == 0) {
+        mean[ng] = (float)mu;
+        inv_std[ng] = (float)(1.0 / sqrt(var + (double)eps));
+    }
+}
+
+// Group statistics from the per-tile partials of the convolution epilogue (tiles of
+// image n are tiles n*tpi .. (n+1)*tpi - 1; see bn_tiles_finalize for the quantities):
+// one workgroup per (n, g); thread t takes (tile, channel) pairs t, t + kThreads, ...
+__global__ __launch_bounds__(kThreads) void grp_tiles_finalize(const float* __restrict__ part, int ntiles, int tpi,
+                                                               int C, int G, int64_t S, float eps,
+                                                               float* __restrict__ mean,
+                                                               float* __restrict__ inv_std) {
+    __shared__ double dred[kThreads];
+    const int ng = blockIdx.x, n = ng / G, g = ng - n * G, cg = C / G, t = threadIdx.x;
+    const int pairs = tpi * cg;
+    const double cnt_all = (double)S * cg;
+    double a = 0.0;
+    for (int q = t; q < pairs; q += kThreads) {
+        const int k = q / tpi, tile = n * tpi + (q - k * tpi), c = g * cg + k;
+        const float* p = part + (int64_t)c * 4 * ntiles + tile;
+        a += (double)p[3 * (int64_t)ntiles] * (double)p[2 * (int64_t)ntiles] + (double)p[0];
+    }
+    const double mu = block_sum(a, dred) / cnt_all;
+    double b = 0.0;
+    for (int q = t; q < pairs; q += kThreads) {
+        const int k = q / tpi, tile = n * tpi + (q - k * tpi), c = g * cg + k;
+        const float* p = part + (int64_t)c * 4 * ntiles + tile;
+        const double cn = (double)p[3 * (int64_t)ntiles], s1 = (double)p[0];
+        if (cn > 0.0) {
+            const double dm = (double)p[2 * (int64_t)ntiles] + s1 / cn - mu;
+            b += ((double)p[ntiles] - s1 * s1 / cn) + cn * dm * dm;
+        }
+    }
+    double var = block_sum(b, dred) / cnt_all;
+    if (var < 0.0) var = 0.0;
+    if (t == 0) {
+        mean[ng] = (float)mu;
+        inv_std[ng] = (float)(1.0 / sqrt(var + (double)eps));
+    }
+}
+
+// Per-element statistics of sample n for channels c0 .. c0 + VEC - 1.
+template <int VEC>
+__device__ __forceinline__ void grp_params(const float* mean, const float* inv_std, int n, int G, int cg, int c0,
+                                           float* mu, float* is) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const int st = n * G + (c0 + j) / cg;
+        mu[j] = mean[st];
+        is[j] = inv_std[st];
+    }
+}
+
+// y = act(gamma_c (z - mean_ng) inv_std_ng + beta_c); grid (blocks per sample, N).
+template <typename T, int VEC, int ACT>
+__global__ __launch_bounds__(kThreads) void grp_apply(const T* __restrict__ z, T* __restrict__ y, int64_t per_sample,
+                                                      int C, int G, const float* __restrict__ gamma,
+                                                      const float* __restrict__ beta, const float* __restrict__ mean,
+                                                      const float* __restrict__ inv_std) {
+    const int n = blockIdx.y, cg = C / G;
+    const int64_t nvec = per_sample / VEC, base = (int64_t)n * per_sample;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    int c0 = (int)((v * VEC) % C), cached = -1;
+    const int step = (int)((stride * VEC) % C);
+    float mu[VEC], is[VEC], g[VEC], bt[VEC];
+    for (; v < nvec; v += stride) {
+        float a[VEC];
+        Vec<T, VEC>::load(z + base + v * VEC, a);
+        if (c0 != cached) {
+            grp_params<VEC>(mean, inv_std, n, G, cg, c0, mu, is);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) { g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j]; }
+            cached = c0;
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            float zh;
+            a[j] = act_fwd<ACT>(bn_affine(a[j], mu[j], is[j], g[j], bt[j], &zh));
+        }
+        Vec<T, VEC>::store(y + base + v * VEC, a);
+        c0 += step;
+        if (c0 >= C) c0 -= C;
+    }
+}
+
+// Sums of dno and dno*zhat per channel over a slab of one sample's rows, with the
+// sample's group statistics.
+template <typename T, int VEC, int ACT> struct GrpBwdAcc {
+    static constexpr bool kOut = false;
+    const float *gamma, *beta, *mean, *inv_std;
+    int G, cg;
+    float g[VEC], bt[VEC], mu[VEC], is[VEC];
+    __device__ __forceinline__ void init(int c0, int n, int64_t) {
+        grp_params<VEC>(mean, inv_std, n, G, cg, c0, mu, is);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) { g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j]; }
+    }
+    __device__ __forceinline__ void add(const float* zv, const float* gv, float* s1, float* s2) const {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            float zh;
+            const float a = bn_affine(zv[j], mu[j], is[j], g[j], bt[j], &zh);
+            const float dno = act_slope<ACT>(a) * gv[j];
+            s1[j] += dno;
+            s2[j] = __builtin_fmaf(dno, zh, s2[j]);
+        }
+    }
+};
+
+template <typename T, int VEC, int ACT>
+__global__ __launch_bounds__(kThreads) void grp_bwd_partials(const T* __restrict__ z, const T* __restrict__ dy,
+                                                             int64_t M, int C, int tpr, int rpi, int64_t rows_per_block,
+                                                             int64_t seg, int bps, int G,
+                                                             const float* __restrict__ gamma,
+                                                             const float* __restrict__ beta,
+                                                             const float* __restrict__ mean,
+                                                             const float* __restrict__ inv_std,
+                                                             float* __restrict__ part) {
+    extern __shared__ float red[];
+    GrpBwdAcc<T, VEC, ACT> acc{gamma, beta, mean, inv_std, G, C / G, {}, {}, {}, {}};
+    slab_partials<T, VEC>(z, dy, M, C, tpr, rpi, rows_per_block, acc, part, red, nullptr, seg, bps);
+}
+
+// Per (n, c): A = sum dno, B = sum dno*zhat over the sample's slabs, in order, as fp64
+// into ab[(n*C + c)*2 + {0,1}].
+__global__ __launch_bounds__(kThreads) void grp_bwd_merge(const float* __restrict__ part, int bps, int N, int C,
+                                                          double* __restrict__ ab) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)N * C) return;
+    const int n = (int)(i / C), c = (int)(i - (int64_t)n * C);
+    const int64_t slabs = (int64_t)N * bps;
+    const float* p1 = part + (int64_t)c * 2 * slabs + (int64_t)n * bps;
+    double a = 0.0, b = 0.0;
+    for (int j = 0; j < bps; ++j) {
+        a += (double)p1[j];
+        b += (double)p1[slabs + j];
+    }
+    ab[2 * i] = a;
+    ab[2 * i + 1] = b;
+}
+
+// Workgroups 0 .. N*G-1: per (n, g) S1 = sum_c gamma_c A_nc, S2 = sum_c gamma_c B_nc
+// (channels of the group, fixed order) -> coef[(n*G + g)*2] = S1/cnt, [+1] = S2/cnt.
+// Workgroups N*G ..: per channel dgamma (+)= sum_n B_nc, dbeta (+)= sum_n A_nc.
+__global__ __launch_bounds__(kThreads) void grp_bwd_coef(const double* __restrict__ ab, int N, int C, int G,
+                                                         double cnt, const float* __restrict__ gamma,
+                                                         float* __restrict__ dgamma, float* __restrict__ dbeta,
+                                                         int accumulate, float* __restrict__ coef) {
+    __shared__ double dred[kThreads];
+    const int t = threadIdx.x, cg = C / G;
+    if ((int)blockIdx.x < N * G) {
+        const int ng = blockIdx.x, n = ng / G, g = ng - n * G;
+        double a = 0.0, b = 0.0;
+        for (int k = t; k < cg; k += kThreads) {
+            const int c = g * cg + k;
+            const double* p = ab + ((int64_t)n * C + c) * 2;
+            a += (double)gamma[c] * p[0];
+            b += (double)gamma[c] * p[1];
+        }
+        a = block_sum(a, dred);
+        b = block_sum(b, dred);
+        if (t == 0) {
+            coef[2 * ng] = (float)(a / cnt);
+            coef[2 * ng + 1] = (float)(b / cnt);
+        }
+        return;
+    }
+    const int c = (blockIdx.x - N * G) * kThreads + t;
+    if (c >= C || (!dgamma && !dbeta)) return;
+    double a = 0.0, b = 0.0;
+    for (int n = 0; n < N; ++n) {
+        a += ab[((int64_t)n * C + c) * 2];
+        b += ab[((int64_t)n * C + c) * 2 + 1];
+    }
+    if (dgamma) dgamma[c] = accumulate ? (float)((double)dgamma[c] + b) : (float)b;
+    if (dbeta) dbeta[c] = accumulate ? (float)((double)dbeta[c] + a) : (float)a;
+}
+
+// dz = inv_std_ng (gamma_c dno - k1_ng - zhat k2_ng); grid (blocks per sample, N).
+template <typename T, int VEC, int ACT>
+__global__ __launch_bounds__(kThreads) void grp_bwd_apply(const T* __restrict__ z, const T* dy, T* dz,
+                                                          int64_t per_sample, int C, int G,
+                                                          const float* __restrict__ gamma,
+                                                          const float* __restrict__ beta,
+                                                          const float* __restrict__ mean,
+                                                          const float* __restrict__ inv_std,
+                                                          const float* __restrict__ coef) {
+    const int n = blockIdx.y, cg = C / G;
+    const int64_t nvec = per_sample / VEC, base = (int64_t)n * per_sample;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    int c0 = (int)((v * VEC) % C), cached = -1;
+    const int step = (int)((stride * VEC) % C);
+    float mu[VEC], is[VEC], g[VEC], bt[VEC], k1[VEC], k2[VEC];
+    for (; v < nvec; v += stride) {
+        float zv[VEC], gv[VEC];
+        Vec<T, VEC>::load(z + base + v * VEC, zv);
+        Vec<T, VEC>::load(dy + base + v * VEC, gv);
+        if (c0 != cached) {
+            grp_params<VEC>(mean, inv_std, n, G, cg, c0, mu, is);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const int st = n * G + (c0 + j) / cg;
+                g[j] = gamma[c0 + j]; bt[j] = beta[c0 + j];
+                k1[j] = coef[2 * st]; k2[j] = coef[2 * st + 1];
+            }
+            cached = c0;
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            float zh, a = bn_affine(zv[j], mu[j], is[j], g[j], bt[j], &zh);
+            const float dno = act_slope<ACT>(a) * gv[j];
+            gv[j] = is[j] * (__builtin_fmaf(g[j], dno, -k1[j]) - zh * k2[j]);
+        }
+        Vec<T, VEC>::store(dz + base + v * VEC, gv);
+        c0 += step;
+        if (c0 >= C) c0 -= C;
+    }
 }
 
 // Evaluation-mode statistics: mean = running_mean, inv_std = 1/sqrt(running_var + eps)
@@ -495,6 +783,7 @@ int merge_grid(int C) {
 
 RowPlan row_plan(int64_t M, int C, int dt) {
     RowPlan p;
+    p.seg = 0;
     const int full = dt == DT_BF16 ? 8 : 4;
     p.vec = (C % full == 0) ? full : 1;
     const int cv = C / p.vec;
@@ -506,6 +795,20 @@ RowPlan row_plan(int64_t M, int C, int dt) {
     if (rpb < p.rpi) rpb = p.rpi;
     p.rows_per_block = rpb;
     p.blocks = (int)ceil_div(M, rpb);
+    p.bps = p.blocks;
+    return p;
+}
+
+RowPlan seg_plan(int N, int64_t S, int C, int dt) {
+    RowPlan p = row_plan(S, C, dt);
+    int bps = (int)ceil_div(kTargetBlocks, N);
+    int64_t rpb = ceil_div(S, bps);
+    rpb = ceil_div(rpb, p.rpi) * p.rpi;
+    if (rpb < p.rpi) rpb = p.rpi;
+    p.rows_per_block = rpb;
+    p.bps = (int)ceil_div(S, rpb);
+    p.blocks = N * p.bps;
+    p.seg = S;
     return p;
 }
 
@@ -513,6 +816,13 @@ size_t bn_stats_ws_bytes(int64_t M, int C, int dt) { return partial_bytes(row_pl
 
 size_t bn_bwd_ws_bytes(int64_t M, int C, int dt) {
     return partial_bytes(row_plan(M, C, dt), C) + align_up((size_t)C * 3 * sizeof(float), 256);
+}
+
+size_t grp_stats_ws_bytes(int N, int64_t S, int C, int dt) { return partial_bytes(seg_plan(N, S, C, dt), C); }
+
+size_t grp_bwd_ws_bytes(int N, int64_t S, int C, int G, int dt) {
+    return partial_bytes(seg_plan(N, S, C, dt), C) + align_up((size_t)N * C * 2 * sizeof(double), 256) +
+           align_up((size_t)N * G * 2 * sizeof(float), 256);
 }
 
 #define CONVMI_VEC_SWITCH(dt, vec, T, VEC, ...)                                  \
@@ -534,7 +844,7 @@ hipError_t launch_bn_stats(int dt, const void* z, int64_t M, int C, float moment
     size_t lds = (size_t)p.rpi * p.tpr * p.vec * 2 * sizeof(float);
     CONVMI_VEC_SWITCH(dt, p.vec, T, VEC,
                       (bn_stats_partials<T, VEC><<<grid, block, lds, s>>>((const T*)z, M, C, p.tpr, p.rpi,
-                                                                          p.rows_per_block, part)));
+                                                                          p.rows_per_block, part, 0, 0)));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dt == DT_BF16)
@@ -619,6 +929,80 @@ hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_
     CONVMI_VEC_SWITCH(dt, p.vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (bn_bwd_apply<T, VEC, A><<<g2, block, 0, s>>>(
                                                                       (const T*)z, (const T*)dy, (T*)dz, nvec, C,
                                                                       gamma, beta, mean, inv_std, coef))));
+    return hipGetLastError();
+}
+
+hipError_t launch_grp_stats(int dt, const void* z, int N, int64_t S, int C, int G, float eps, float* mean,
+                            float* inv_std, void* ws, hipStream_t s) {
+    RowPlan p = seg_plan(N, S, C, dt);
+    float* part = (float*)ws;
+    dim3 grid(p.blocks, p.chunks), block(kThreads);
+    size_t lds = (size_t)p.rpi * p.tpr * p.vec * 2 * sizeof(float);
+    const int64_t M = (int64_t)N * S;
+    CONVMI_VEC_SWITCH(dt, p.vec, T, VEC,
+                      (bn_stats_partials<T, VEC><<<grid, block, lds, s>>>((const T*)z, M, C, p.tpr, p.rpi,
+                                                                          p.rows_per_block, part, p.seg, p.bps)));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (dt == DT_BF16)
+        grp_stats_finalize<bf16><<<N * G, block, 0, s>>>(part, p.bps, C, G, (const bf16*)z, S, eps, mean, inv_std);
+    else
+        grp_stats_finalize<float><<<N * G, block, 0, s>>>(part, p.bps, C, G, (const float*)z, S, eps, mean, inv_std);
+    return hipGetLastError();
+}
+
+hipError_t launch_grp_tiles_finalize(const float* part, int ntiles, int N, int C, int G, int64_t S, float eps,
+                                     float* mean, float* inv_std, hipStream_t s) {
+    grp_tiles_finalize<<<N * G, kThreads, 0, s>>>(part, ntiles, ntiles / N, C, G, S, eps, mean, inv_std);
+    return hipGetLastError();
+}
+
+static int per_sample_grid(int N, int64_t nvec_per_sample) {
+    int64_t g = ceil_div(nvec_per_sample, kThreads * 4);
+    const int64_t cap = ceil_div(8192, N);
+    if (g > cap) g = cap;
+    return g < 1 ? 1 : (int)g;
+}
+
+hipError_t launch_grp_apply(int dt, const void* z, void* y, int N, int64_t S, int C, int G, int act,
+                            const float* gamma, const float* beta, const float* mean, const float* inv_std,
+                            hipStream_t s) {
+    const int full = dt == DT_BF16 ? 8 : 4;
+    const int vec = (C % full == 0) ? full : 1;
+    const int64_t per_sample = S * C;
+    dim3 grid(per_sample_grid(N, per_sample / vec), N), block(kThreads);
+    CONVMI_VEC_SWITCH(dt, vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (grp_apply<T, VEC, A><<<grid, block, 0, s>>>(
+                                                                   (const T*)z, (T*)y, per_sample, C, G, gamma, beta,
+                                                                   mean, inv_std))));
+    return hipGetLastError();
+}
+
+hipError_t launch_grp_bwd(int dt, const void* z, const void* dy, void* dz, int N, int64_t S, int C, int G, int act,
+                          const float* gamma, const float* beta, const float* mean, const float* inv_std,
+                          float* dgamma, float* dbeta, int accumulate, void* ws, hipStream_t s) {
+    RowPlan p = seg_plan(N, S, C, dt);
+    float* part = (float*)ws;
+    double* ab = (double*)((char*)ws + partial_bytes(p, C));
+    float* coef = (float*)((char*)ab + align_up((size_t)N * C * 2 * sizeof(double), 256));
+    dim3 grid(p.blocks, p.chunks), block(kThreads);
+    size_t lds = (size_t)p.rpi * p.tpr * p.vec * 2 * sizeof(float);
+    const int64_t M = (int64_t)N * S;
+    CONVMI_VEC_SWITCH(dt, p.vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (grp_bwd_partials<T, VEC, A><<<grid, block, lds, s>>>(
+                                                                      (const T*)z, (const T*)dy, M, C, p.tpr, p.rpi,
+                                                                      p.rows_per_block, p.seg, p.bps, G, gamma, beta,
+                                                                      mean, inv_std, part))));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    grp_bwd_merge<<<(int)ceil_div((int64_t)N * C, kThreads), block, 0, s>>>(part, p.bps, N, C, ab);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    grp_bwd_coef<<<N * G + (int)ceil_div(C, kThreads), block, 0, s>>>(ab, N, C, G, (double)S * (C / G), gamma, dgamma,
+                                                                      dbeta, accumulate, coef);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t per_sample = S * C;
+    dim3 g2(per_sample_grid(N, per_sample / p.vec), N);
+    CONVMI_VEC_SWITCH(dt, p.vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (grp_bwd_apply<T, VEC, A><<<g2, block, 0, s>>>(
+                                                                      (const T*)z, (const T*)dy, (T*)dz, per_sample, C,
+                                                                      G, gamma, beta, mean, inv_std, coef))));
     return hipGetLastError();
 }
 

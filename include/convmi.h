@@ -13,6 +13,8 @@
  *   [cuda]    "rl_tools/nn/layers/conv2d/operations_cuda.h"    (hyperray 0.0.1 wheel)
  *   [mkl]     "rl_tools/nn/layers/conv2d/operations_cpu_mkl.h" (hyperray 0.0.1 wheel)
  *   [wgsl]    "conv2d_backward_weight.wgsl" (@simulatte/doppler 0.1.0)
+ *   [doppler] the same package's backward kernels "groupnorm_backward.wgsl" and
+ *             "gelu_backward.wgsl"
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller (for example the
@@ -65,15 +67,30 @@ typedef enum {
 typedef enum { CONVMI_F32 = 0, CONVMI_BF16 = 1 } convmi_dtype;
 
 /* The activation set of the [mkl] listing's post-op table: identity, relu, tanh,
- * sigmoid.  relu'(0) is taken as 0. */
+ * sigmoid; relu'(0) is taken as 0.  Plus GELU in its tanh form, as the [doppler]
+ * gelu_backward kernel differentiates it: gelu(a) = a/2 (1 + tanh(u)),
+ * u = sqrt(2/pi) (a + 0.044715 a^3). */
 typedef enum {
     CONVMI_ACT_IDENTITY = 0,
     CONVMI_ACT_RELU = 1,
     CONVMI_ACT_TANH = 2,
-    CONVMI_ACT_SIGMOID = 3
+    CONVMI_ACT_SIGMOID = 3,
+    CONVMI_ACT_GELU = 4
 } convmi_act;
 
-typedef enum { CONVMI_NORM_NONE = 0, CONVMI_NORM_BATCH = 1 } convmi_norm;
+/* Normalisation of z before the activation, a = gamma[c]*(z - mean)*inv_std + beta[c]:
+ *   BATCH  per channel over the N*OH*OW rows (training or running statistics, see mode);
+ *   LAYER  per sample over its OH*OW*OC values ([generic] layer-norm branches);
+ *   GROUP  per sample and group of OC/groups consecutive channels over OH*OW*OC/groups
+ *          values ([doppler] groupnorm_backward); LAYER is GROUP with one group.
+ * LAYER and GROUP have no running statistics and use the sample's own statistics in
+ * both modes; their save_mean / save_inv_std hold [N][groups] values. */
+typedef enum {
+    CONVMI_NORM_NONE = 0,
+    CONVMI_NORM_BATCH = 1,
+    CONVMI_NORM_LAYER = 2,
+    CONVMI_NORM_GROUP = 3
+} convmi_norm;
 
 /* Batch-norm mode.  TRAIN: batch statistics, running statistics updated.  EVAL: the
  * running statistics normalise (mean = running_mean, inv_std = 1/sqrt(running_var +
@@ -96,8 +113,8 @@ typedef enum {
  * runtime descriptor.  Padding is symmetric and zero-filled; the operation is a
  * cross-correlation (the [cuda] descriptor uses CUDNN_CROSS_CORRELATION).
  * Limits: all sizes >= 1, strides >= 1, pads >= 0, OH and OW >= 1, each tensor of one
- * image below 2^31 elements, N*OH*OW below 2^31.  momentum in [0,1]; eps > 0 when
- * normalization is BATCH. */
+ * image below 2^31 elements, N*OH*OW below 2^31.  momentum in [0,1] (BATCH); eps > 0
+ * with any normalisation; groups >= 1 dividing OC (GROUP; ignored otherwise). */
 typedef struct convmi_desc {
     int64_t N, H, W, IC, OC, KH, KW;
     int32_t stride_h, stride_w, pad_h, pad_w;
@@ -107,6 +124,7 @@ typedef struct convmi_desc {
     int32_t dtype;         /* convmi_dtype */
     float momentum;        /* running <- (1-momentum)*running + momentum*batch */
     float eps;             /* inv_std = 1/sqrt(var + eps) */
+    int32_t groups;        /* channel groups of CONVMI_NORM_GROUP */
 } convmi_desc;
 
 /* OH, OW for a descriptor (floor formula above).  Checks the descriptor. */
@@ -117,8 +135,10 @@ convmi_status convmi_workspace_size(const convmi_desc* desc, int32_t op, size_t*
 
 /* a1 + a2 + a3: convolution + bias, then (batch norm) training statistics and the
  * normalise/affine step, then the activation.  [generic] forward (conv + bias into
- * pre_activations; batch-norm training statistics; normalise + activate); [cuda]
+ * pre_activations; batch-norm or layer-norm statistics; normalise + activate); [cuda]
  * forward (conv, add bias, bn_stats_training, bn_forward_affine, activation).
+ * LAYER / GROUP: gamma, beta, save_mean, save_inv_std ([N][groups]) and z required;
+ * running_mean / running_var must be NULL.
  *   x, w: inputs.  bias: fp32 [OC] or NULL (no bias).
  *   gamma, beta, running_mean, running_var, save_mean, save_inv_std: batch norm only
  *     (NULL otherwise).  TRAIN: running_* (optional, both or neither) are updated in
@@ -171,7 +191,9 @@ convmi_status conv2d_backward_weight(const convmi_desc* desc, const void* x, con
  * save_inv_std = 1/sqrt(var+eps); running_mean/var (nullable, both or neither)
  * updated with momentum.  [generic] forward, batch-norm training statistics; [cuda]
  * bn_stats_training.  TRAIN mode only (INVALID_ARG in EVAL mode, where
- * conv2d_forward takes the running statistics). */
+ * conv2d_forward takes the running statistics).  With LAYER / GROUP normalisation the
+ * same call gives the per-sample (per-group) statistics, [N][groups] values, in either
+ * mode; running_mean / running_var must then be NULL. */
 convmi_status bn_stats_training(const convmi_desc* desc, const void* z, float* save_mean, float* save_inv_std,
                                 float* running_mean, float* running_var,
                                 void* workspace, size_t workspace_bytes, void* stream);
@@ -186,6 +208,9 @@ convmi_status bn_stats_training(const convmi_desc* desc, const void* z, float* s
  *     dgamma, dbeta optional (NULL skips them); `accumulate` as for dw.
  *   Batch norm, EVAL mode (constant statistics): dz = dno * gamma * inv_std, with
  *     dgamma, dbeta as above.
+ *   LAYER / GROUP (either mode): the training formula above per sample and group, with
+ *     cnt = OH*OW*OC/groups values in place of M, save_* [N][groups]; dgamma and dbeta
+ *     per channel over all samples and pixels.
  * dz may equal dy (in place).  [generic] backward_input / backward (training-mode
  * two-phase normalisation backward, evaluation-mode branch); [cuda]
  * activation_backward, bn_training_backward. */

@@ -73,6 +73,12 @@ def relu_kink_ties(z, gamma, beta, mean, inv_std):
     return np.abs(a) <= 2.0 ** -21 * (np.abs(gamma * zh) + np.abs(beta))
 
 
+def expand_group_stats(v, N, C):
+    """Per (sample, group) statistics [N*G] -> [N, 1, 1, C], broadcastable over z."""
+    v = np.asarray(v, np.float64).reshape(N, -1)
+    return np.repeat(v, C // v.shape[1], axis=1).reshape(N, 1, 1, C)
+
+
 def untie_relu(dy, z, act, gamma, beta, mean, inv_std):
     """dy with the ReLU-kink ties (relu_kink_ties) zeroed; other activations are smooth
     and pass through unchanged."""
@@ -104,11 +110,11 @@ def desc_for(wl: WL.Workload):
                         cm.MODE_TRAIN, cdtype(wl.dtype), wl.momentum, wl.eps)
 
 
-def shape_desc(shape: WL.ConvShape, dt: str, act=0, norm=0, momentum=0.1, eps=1e-5, evaluation=False):
+def shape_desc(shape: WL.ConvShape, dt: str, act=0, norm=0, momentum=0.1, eps=1e-5, evaluation=False, groups=1):
     import convolution_layer_amd as cm
     s = shape
     return cm.make_desc(s.N, s.H, s.W, s.IC, s.OC, s.KH, s.KW, (s.sh, s.sw), (s.ph, s.pw), act, norm,
-                        cm.MODE_EVAL if evaluation else cm.MODE_TRAIN, cdtype(dt), momentum, eps)
+                        cm.MODE_EVAL if evaluation else cm.MODE_TRAIN, cdtype(dt), momentum, eps, groups)
 
 
 def sample_indices(shape4, count: int, seed: int) -> np.ndarray:
@@ -129,9 +135,9 @@ def run_forward(desc, dt, x, w, b=None, gamma=None, beta=None, rmean=None, rvar=
     y = torch.empty(shape, dtype=tdtype(dt), device="cuda")
     out = {"z": z, "y": y}
     sm = si = None
-    if desc.normalization == cm.NORM_BATCH:
-        sm = torch.empty(desc.OC, dtype=torch.float32, device="cuda")
-        si = torch.empty(desc.OC, dtype=torch.float32, device="cuda")
+    if desc.normalization != cm.NORM_NONE:
+        sm = torch.empty(cm.stat_count(desc), dtype=torch.float32, device="cuda")
+        si = torch.empty(cm.stat_count(desc), dtype=torch.float32, device="cuda")
         out.update(save_mean=sm, save_inv_std=si, running_mean=rmean, running_var=rvar)
     ws = cm.workspace(desc, cm.OP_FORWARD)
     cm.conv2d_forward(desc, x, w, b, gamma, beta, rmean, rvar, sm, si, z, y, ws)
@@ -158,8 +164,8 @@ def run_backward_weight(desc, x, dz, with_bias=True, accumulate=0, dw=None, db=N
 
 def run_bn_stats(desc, z, rmean=None, rvar=None):
     import convolution_layer_amd as cm
-    sm = torch.empty(desc.OC, dtype=torch.float32, device="cuda")
-    si = torch.empty(desc.OC, dtype=torch.float32, device="cuda")
+    sm = torch.empty(cm.stat_count(desc), dtype=torch.float32, device="cuda")
+    si = torch.empty(cm.stat_count(desc), dtype=torch.float32, device="cuda")
     cm.bn_stats_training(desc, z, sm, si, rmean, rvar, cm.workspace(desc, cm.OP_BN_STATS))
     return sm, si
 
@@ -169,7 +175,7 @@ def run_act_bwd(desc, dt, z, dy, gamma=None, beta=None, mean=None, inv=None, dz=
     import convolution_layer_amd as cm
     if dz is None:
         dz = torch.empty_like(dy)
-    if desc.normalization == cm.NORM_BATCH:
+    if desc.normalization != cm.NORM_NONE:
         if dgamma is None:
             dgamma = torch.empty(desc.OC, dtype=torch.float32, device="cuda")
         if dbeta is None:

@@ -70,13 +70,15 @@ def _good(cm, **kw):
     base.update(kw)
     return cm.make_desc(base["N"], base["H"], base["W"], base["IC"], base["OC"], base["KH"], base["KW"],
                         base["stride"], base["pad"], base.get("activation", 0), base.get("normalization", 0),
-                        base.get("mode", 0), base.get("dtype", 0), base.get("momentum", 0.1), base.get("eps", 1e-5))
+                        base.get("mode", 0), base.get("dtype", 0), base.get("momentum", 0.1), base.get("eps", 1e-5),
+                        base.get("groups", 1))
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(N=0), 1), (dict(IC=-1), 1), (dict(KH=0), 1), (dict(stride=(0, 1)), 1), (dict(pad=(-1, 0)), 1),
-    (dict(KH=11, pad=(0, 0)), 1), (dict(dtype=7), 1), (dict(activation=9), 1), (dict(normalization=3), 1),
-    (dict(mode=5), 1), (dict(normalization=1, eps=0.0), 1),
+    (dict(KH=11, pad=(0, 0)), 1), (dict(dtype=7), 1), (dict(activation=9), 1), (dict(activation=5), 1),
+    (dict(normalization=4), 1), (dict(mode=5), 1), (dict(normalization=1, eps=0.0), 1),
+    (dict(normalization=2, eps=0.0), 1), (dict(normalization=3, groups=0), 1), (dict(normalization=3, groups=5), 1),
     (dict(normalization=1, momentum=1.5), 1), (dict(N=1 << 40), 2),
 ])
 def test_bad_descriptor(cm, kw, status):
@@ -85,6 +87,27 @@ def test_bad_descriptor(cm, kw, status):
     st = cm.lib.convmi_output_dims(C.byref(d), C.byref(oh), C.byref(ow))
     assert st == status, cm.lib.convmi_last_error()
     assert cm.lib.convmi_last_error().decode()
+
+
+def test_norm_variant_descriptors(cm):
+    """GELU, layer norm and group norm (groups dividing OC) are valid descriptors; their
+    statistics take N*groups entries and the calls refuse running statistics."""
+    oh, ow = C.c_int64(), C.c_int64()
+    for kw in (dict(activation=cm.ACT_GELU), dict(normalization=cm.NORM_LAYER), dict(normalization=cm.NORM_GROUP, groups=4),
+               dict(normalization=cm.NORM_GROUP, groups=16, mode=1)):
+        d = _good(cm, **kw)
+        assert cm.lib.convmi_output_dims(C.byref(d), C.byref(oh), C.byref(ow)) == cm.OK
+    d = _good(cm, normalization=cm.NORM_GROUP, groups=4)
+    assert cm.stat_count(d) == 2 * 4
+    for op in (cm.OP_FORWARD, cm.OP_BN_STATS, cm.OP_ACTIVATION_BACKWARD):
+        assert cm.workspace_size(d, op) > 0
+    vec = [A + 0x300000 + 0x1000 * i for i in range(6)]
+    args = [C.byref(d), A, A + 0x100000, None, vec[0], vec[1], vec[2], vec[3], vec[4], vec[5], A + 0x400000,
+            A + 0x200000, None, 0, None]
+    assert cm.lib.conv2d_forward(*args) == cm.ERR_INVALID_ARG
+    assert "running" in cm.lib.convmi_last_error().decode()
+    st = cm.lib.bn_stats_training(C.byref(d), A, vec[4], vec[5], vec[2], vec[3], None, 0, None)
+    assert st == cm.ERR_INVALID_ARG
 
 
 def test_evaluation_mode_checks(cm):

@@ -27,8 +27,8 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 
-ACT_IDENTITY, ACT_RELU, ACT_TANH, ACT_SIGMOID = 0, 1, 2, 3
-NORM_NONE, NORM_BATCH = 0, 1
+ACT_IDENTITY, ACT_RELU, ACT_TANH, ACT_SIGMOID, ACT_GELU = 0, 1, 2, 3, 4
+NORM_NONE, NORM_BATCH, NORM_LAYER, NORM_GROUP = 0, 1, 2, 3
 
 
 @dataclass(frozen=True)
