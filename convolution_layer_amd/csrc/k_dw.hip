@@ -810,6 +810,7 @@ __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_
     // two-wave 64-channel workgroups issue theirs at once before the first MFMAs (measured
     // ~2 us faster on c5, ~1 us slower for the eight-wave 128-channel kernel)
     const int spread = CH == 64 ? 0 : (nk > 2 ? 2 : 1);
+    const int sdiv = spread > 0 ? spread : 1;  // divisor of the slices (unused when spread is 0)
     if (KT > 0) issue(segs_of(0), 0, nmine);
     for (int k = 0; k < KT; ++k) {
         wait_dma(0);
@@ -827,21 +828,21 @@ __global__ __launch_bounds__(dw3_threads<CH>()) __attribute__((amdgpu_waves_per_
             for (int kk = 0; kk < NK; ++kk) {
                 if (kk + 1 < NK) read_frags(As, Xs, (kk + 1) * 16, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
                 mfmas(fa[kk & 1], fb[kk & 1]);
-                if (next && kk < spread) issue(sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+                if (next && kk < spread) issue(sg, kk * nmine / sdiv, (kk + 1) * nmine / sdiv);
             }
         } else {
             int kk = 0;
             for (; kk + 1 < nk; kk += 2) {
                 read_frags(As, Xs, (kk + 1) * 16, fa[1], fb[1]);
                 mfmas(fa[0], fb[0]);
-                if (next && kk < spread) issue(sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+                if (next && kk < spread) issue(sg, kk * nmine / sdiv, (kk + 1) * nmine / sdiv);
                 if (kk + 2 < nk) read_frags(As, Xs, (kk + 2) * 16, fa[0], fb[0]);
                 mfmas(fa[1], fb[1]);
-                if (next && kk + 1 < spread) issue(sg, (kk + 1) * nmine / spread, (kk + 2) * nmine / spread);
+                if (next && kk + 1 < spread) issue(sg, (kk + 1) * nmine / sdiv, (kk + 2) * nmine / sdiv);
             }
             if (kk < nk) {
                 mfmas(fa[0], fb[0]);
-                if (next && kk < spread) issue(sg, kk * nmine / spread, nmine);
+                if (next && kk < spread) issue(sg, kk * nmine / sdiv, nmine);
             }
         }
     }
@@ -964,6 +965,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // before the MFMAs of kk.
     const int nk = NK > 0 ? NK : g.SPp / 4;
     const int spread = nk > 2 ? 2 : nk;
+    const int sdiv = spread > 0 ? spread : 1;  // divisor of the slices (unused when spread is 0)
     if (KT > 0) cp.issue(g, cp.segs_of(g, 0), 0, nmine);
     for (int k = 0; k < KT; ++k) {
         wait_dma(0);
@@ -980,21 +982,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int kk = 0; kk < NK; ++kk) {
                 if (kk + 1 < NK) read_frags(As, Xs, (kk + 1) * 4, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
                 mfmas(fa[kk & 1], fb[kk & 1]);
-                if (next && kk < spread) cp.issue(g, sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+                if (next && kk < spread) cp.issue(g, sg, kk * nmine / sdiv, (kk + 1) * nmine / sdiv);
             }
         } else {
             int kk = 0;
             for (; kk + 1 < nk; kk += 2) {
                 read_frags(As, Xs, (kk + 1) * 4, fa[1], fb[1]);
                 mfmas(fa[0], fb[0]);
-                if (next && kk < spread) cp.issue(g, sg, kk * nmine / spread, (kk + 1) * nmine / spread);
+                if (next && kk < spread) cp.issue(g, sg, kk * nmine / sdiv, (kk + 1) * nmine / sdiv);
                 if (kk + 2 < nk) read_frags(As, Xs, (kk + 2) * 4, fa[0], fb[0]);
                 mfmas(fa[1], fb[1]);
-                if (next && kk + 1 < spread) cp.issue(g, sg, (kk + 1) * nmine / spread, (kk + 2) * nmine / spread);
+                if (next && kk + 1 < spread) cp.issue(g, sg, (kk + 1) * nmine / sdiv, (kk + 2) * nmine / sdiv);
             }
             if (kk < nk) {
                 mfmas(fa[0], fb[0]);
-                if (next && kk < spread) cp.issue(g, sg, kk * nmine / spread, nmine);
+                if (next && kk < spread) cp.issue(g, sg, kk * nmine / sdiv, nmine);
             }
         }
     }

@@ -7,6 +7,14 @@
 // after such a copy is preceded by a full vmcnt(0) wait, which would serialise the
 // pipeline.  Lanes whose source lies outside the tensor (padding, ragged tiles) copy a
 // 16-byte zero page instead.
+//
+// M0: each copy sets M0 to its LDS base in the same asm block, right before the
+// instruction that reads it, and lists M0 as clobbered.  The compiler warns that it may
+// not preserve a reserved register across such a block; that would only matter if it
+// kept a value of its own in M0 across one.  In these kernels it never uses M0 at all
+// (no indirect register indexing, messages, GWS or LDS-DMA builtins), so every M0 write
+// in the built code is one of these blocks, immediately followed by its copy;
+// tests/test_isa_cpu.py checks exactly that on the built library.
 #pragma once
 
 #include "common.hpp"
@@ -19,6 +27,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)(p); }
+
+// The M0 clobber warning is silenced for these two blocks only (see above for why it
+// is safe and which test guards it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 
 // 16 bytes per lane, global -> LDS; lds_base must be wave-uniform.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
@@ -47,6 +60,8 @@ __device__ __forceinline__ void dma16_buf(uint32_t voff, dma_rsrc rsrc, uint32_t
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_base)
                  : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // Wait until at most n of this wave's copies are outstanding (n wave-uniform; values
 // above 31 wait for 31, which is only more conservative).
