@@ -53,6 +53,40 @@ template <typename T> struct Vec<T, 1> {
     static __device__ __forceinline__ void store(T* p, const float* v) { *p = from_f32<T>(v[0]); }
 };
 
+// ---------------------------------------------------------------- cross-lane sums
+// Lanes l and l + k of a wave64 exchange values without LDS memory: rotations within
+// 16-lane rows through DPP (row_ror), the two halves of each 32-lane group through
+// ds_swizzle (bit mode, xor 16), the two 32-lane halves through ds_bpermute (xor 32).
+__device__ __forceinline__ float dpp_ror(float v, int k) {  // k in {1, 2, 4, 8}; lane i gets lane (i + k) % 16 of its row
+    const int x = __builtin_bit_cast(int, v);
+    int r;
+    switch (k) {
+    case 8: r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false); break;
+    }
+    return __builtin_bit_cast(float, r);
+}
+__device__ __forceinline__ float lane_xor16(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), (0x10 << 10) | 0x1f));
+}
+__device__ __forceinline__ float lane_xor32(float v) {
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, v)));
+}
+
+// Sum over the lanes of a wave congruent modulo `stride` (a power of two <= 64): every
+// lane ends with the sum of its class.  Each lane adds the same terms in the same
+// pairing (IEEE addition is commutative), so all lanes of a class agree bit for bit and
+// the result depends only on the data.
+__device__ __forceinline__ float wave_class_sum(float v, int stride) {
+    for (int k = 8; k >= stride && k >= 1; k >>= 1) v += dpp_ror(v, k);
+    if (stride <= 16) v += lane_xor16(v);
+    if (stride <= 32) v += lane_xor32(v);
+    return v;
+}
+
 // Fixed-order merge of `rpi` row groups held in red[r][lane_slot] (any rpi >= 1):
 // halve the count each step, adding the upper part onto the lower.  Result in red[0][*].
 __device__ __forceinline__ void merge_rows(float* red, int rpi, int width, int r, int slot, int nvals,
@@ -79,7 +113,7 @@ __device__ __forceinline__ void slab_partials(const T* __restrict__ a, const T* 
                                               int tpr, int rpi, int64_t rows_per_block, Acc accf,
                                               float* __restrict__ part, float* red, T* out = nullptr,
                                               int64_t seg = 0, int bps = 0) {
-    constexpr int UNROLL = 4;
+    constexpr int UNROLL = 8;
     const int t = threadIdx.x, cv = t % tpr, r = t / tpr;
     const int c0 = (blockIdx.y * tpr + cv) * VEC;
     const bool active = r < rpi && c0 < C;
@@ -127,6 +161,34 @@ __device__ __forceinline__ void slab_partials(const T* __restrict__ a, const T* 
                 accf.add(va, vb, s1, s2);
             }
         }
+    }
+    if ((tpr & (tpr - 1)) == 0 && tpr <= 64) {
+        // The row groups of a wave hold the same channels in lanes tpr apart: sum them
+        // across lanes, then the kThreads/64 waves' sums in wave order (one barrier).
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            s1[j] = wave_class_sum(s1[j], tpr);
+            s2[j] = wave_class_sum(s2[j], tpr);
+        }
+        const int lane = t & 63, wv = t >> 6, slot = cv * VEC * 2, width = tpr * VEC * 2;
+        if (lane < tpr)
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                red[wv * width + slot + 2 * j] = s1[j];
+                red[wv * width + slot + 2 * j + 1] = s2[j];
+            }
+        __syncthreads();
+        if (t < tpr && c0 < C)
+            for (int j = 0; j < VEC; ++j) {
+                float a = 0.0f, b = 0.0f;
+                for (int w = 0; w < kThreads / 64; ++w) {
+                    a += red[w * width + slot + 2 * j];
+                    b += red[w * width + slot + 2 * j + 1];
+                }
+                part[((int64_t)(c0 + j) * 2 + 0) * gridDim.x + blockIdx.x] = a;
+                part[((int64_t)(c0 + j) * 2 + 1) * gridDim.x + blockIdx.x] = b;
+            }
+        return;
     }
     const int width = tpr * VEC * 2, slot = cv * VEC * 2;
     if (active)
