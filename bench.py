@@ -1,9 +1,11 @@
 """Benchmark of the conv2d training layer on one MI355X.
 
-A step is one pass of the layer's hot path over one batch of seeded synthetic input:
-conv2d_forward (conv + bias + activation, z and y written), activation_backward, dX
-(conv2d_backward_data) and dW + db (conv2d_backward_weight), on the wide bf16 layer
-N=64, 56x56x128 -> 128, 3x3 s1 p1, bias + tanh (fp32 accumulate).  The headline value
+A step is one pass of the layer's hot path over one batch of seeded synthetic input, on
+the wide bf16 layer N=64, 56x56x128 -> 128, 3x3 s1 p1, bias + tanh (fp32 accumulate):
+conv2d_forward (conv + bias + activation; only the output y is stored, since the tanh
+derivative is a function of y) and conv2d_backward_full (activation derivative from y,
+dX, dW + db).  Layers with a normalisation run forward, activation_backward, dX and dW
+as four calls.  The headline value
 is (forward + dX + dW flops) / step time in TFLOP/s.  Batch-norm statistics GB/s are
 measured on the conv + batch-norm layer (fp32, N=128, 32x32x64 -> 64) in the same run.
 
@@ -51,6 +53,7 @@ METRIC = "conv2d fwd+dX+dW TFLOP/s and % MFMA peak; BN-stats GB/s (1 MI355X)"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 CONV_CALLS = ("forward", "backward_data", "backward_weight")
+PRODUCTS = {"forward": 1, "backward_data": 1, "backward_weight": 1, "backward_full": 2}  # conv products per call
 
 
 def log(msg):
@@ -98,12 +101,21 @@ class Layer:
         self.db = torch.empty(s.OC, dtype=torch.float32, device="cuda")
         f32 = lambda: torch.empty(s.OC, dtype=torch.float32, device="cuda")
         self.sm, self.si, self.dg, self.dbt = (f32(), f32(), f32(), f32()) if self.bn else (None,) * 4
-        n = max(cm.workspace_size(self.desc, op) for op in range(5))
+        n = max(cm.workspace_size(self.desc, op) for op in (range(6) if wl.norm == WL.NORM_NONE else range(5)))
         self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
 
     def forward(self):
         self.cm.conv2d_forward(self.desc, self.x, self.w, self.b, self.gamma, self.beta, self.rm, self.rv,
                                self.sm, self.si, self.z, self.y, self.ws)
+
+    def forward_y(self):
+        """Forward storing only y (no normalisation: the backward reads y)."""
+        self.cm.conv2d_forward(self.desc, self.x, self.w, self.b, None, None, None, None, None, None, None, self.y,
+                               self.ws)
+
+    def bwd_full(self):
+        self.cm.conv2d_backward_full(self.desc, self.x, self.w, self.y, 1, self.dy, self.dx, self.dw, self.db, 0,
+                                     self.ws)
 
     def act_bwd(self):
         self.cm.activation_backward(self.desc, self.z, self.dy, self.gamma, self.beta, self.sm, self.si, self.dz,
@@ -119,6 +131,18 @@ class Layer:
         self.cm.bn_stats_training(self.desc, self.z, self.sm, self.si, None, None, self.ws)
 
     def calls(self):
+        """The calls of one training step."""
+        if not self.bn and self.wl.norm == WL.NORM_NONE and self.wl.act != WL.ACT_GELU:
+            return [("forward", self.forward_y), ("backward_full", self.bwd_full)]
+        return self.unit_calls()
+
+    @staticmethod
+    def calls_of(wl):
+        fused = wl.norm == WL.NORM_NONE and wl.act != WL.ACT_GELU
+        return [("forward", None), ("backward_full", None)] if fused else \
+            [("forward", None), ("activation_backward", None), ("backward_data", None), ("backward_weight", None)]
+
+    def unit_calls(self):
         return [("forward", self.forward), ("activation_backward", self.act_bwd),
                 ("backward_data", self.bwd_data), ("backward_weight", self.bwd_weight)]
 
@@ -225,6 +249,10 @@ def call_bytes(wl: WL.Workload, call: str, evaluation: bool = False) -> int:
     x, w, y = s.N * s.H * s.W * s.IC, s.OC * s.KH * s.KW * s.IC, s.P * s.OC
     if call == "forward":  # x, w, bias, z and y (training batch norm: + the statistics pass over z)
         return (x + w + 2 * y) * e + 4 * s.OC + (y * e if wl.norm == WL.NORM_BATCH and not evaluation else 0)
+    if call == "forward_y":  # x, w, bias -> y
+        return (x + w + y) * e + 4 * s.OC
+    if call == "backward_full":  # x, w, y, dy -> dx, dw (fp32), db
+        return (2 * x + w + 2 * y) * e + 4 * w + 4 * s.OC
     if call == "bn_stats":
         return y * e
     if call == "activation_backward":  # z, dy -> dz
@@ -302,6 +330,8 @@ def report(replays=10):
             calls.append(("bn_stats", layer.bn_stats))
         calls += [("activation_backward", layer.act_bwd), ("backward_data", layer.bwd_data),
                   ("backward_weight", layer.bwd_weight)]
+        if wl.norm == WL.NORM_NONE:  # the fused step: forward storing y only, then backward_full from y
+            calls += [("forward_y", layer.forward_y), ("backward_full", layer.bwd_full)]
         if layer.bn:  # evaluation-mode batch norm: running statistics, constant in the backward
             ev = Layer(wl, x=layer.x, evaluation=True)
             ev.forward()
@@ -317,8 +347,8 @@ def report(replays=10):
             row["hbm_frac"] = round(row["GB/s"] / PEAK_HBM_GBS, 4)
             row["cold_GB/s"] = round(by / (row["cold_ms"]["median"] * 1e-3) / 1e9, 1)
             row["cold_hbm_frac"] = round(row["cold_GB/s"] / PEAK_HBM_GBS, 4)
-            if cname in ("forward", "forward[eval]", "backward_data", "backward_weight"):
-                tf = wl.shape.flops() / (med * 1e-3) / 1e12
+            if cname in ("forward", "forward[eval]", "forward_y", "backward_data", "backward_weight", "backward_full"):
+                tf = (2 if cname == "backward_full" else 1) * wl.shape.flops() / (med * 1e-3) / 1e12
                 row["TFLOP/s"] = round(tf, 3)
                 row["mfma_frac"] = round(tf / PEAK_TFLOPS[wl.dtype], 4)
             out.append(row)
@@ -374,6 +404,9 @@ KERNEL_OF_CALL = {  # kernel-name fragments each library call launches
     "backward_data": ("halo_rb_kernel<", "halo_kernel<", "frag_weights", "dx_weights", "igemm2_kernel<",
                       "igemm_kernel<", "conv_dx_direct"),
     "backward_weight": ("dw3_kernel", "dw2_kernel", "dw_kernel", "dw_reduce4", "conv_dw_direct"),
+    "backward_full": ("act_bwd<", "halo_rb_kernel<", "halo_kernel<", "frag_weights", "dx_weights", "igemm2_kernel<",
+                      "igemm_kernel<", "conv_dx_direct", "dw3_kernel", "dw2_kernel", "dw_kernel", "dw_reduce4",
+                      "conv_dw_direct"),
 }
 
 
@@ -522,7 +555,8 @@ def main():
     ap.add_argument("--cpu-images", type=int, default=64, help="images of the batch the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bn", action="store_true", help="skip the batch-norm statistics measurement")
-    ap.add_argument("--only", choices=("forward", "activation_backward", "backward_data", "backward_weight"))
+    ap.add_argument("--only", choices=("forward", "activation_backward", "backward_data", "backward_weight",
+                                       "backward_full"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--report", action="store_true",
@@ -558,9 +592,11 @@ def main():
     value = flops / (total / args.steps) / 1e12
     log(f"bench: step {step_ms:.3f} ms (graph), {eager_total / args.steps * 1e3:.3f} ms (eager); per call ms {ms}")
 
-    # dominant call: the convolution call with the longest mean duration
-    conv_calls = {k: v for k, v in ms.items() if k in CONV_CALLS}
-    dom = max(conv_calls, key=conv_calls.get)
+    # dominant kernel: the single-product convolution call with the longest mean duration
+    # (in the fused step, the forward; backward_full holds two products and three launches)
+    conv_calls = {k: v for k, v in ms.items() if k in PRODUCTS}
+    single = {k: v for k, v in conv_calls.items() if PRODUCTS[k] == 1}
+    dom = max(single, key=single.get)
     achieved = s.flops() / (conv_calls[dom] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     tr = call_traffic(dom, wl.name)
@@ -569,10 +605,11 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None if tr is None else round(tr),
                 "mfma_busy": None if mf is None else mf["busy"], "mfma_counters": mf,
                 "per_call_ms": {k: round(v, 4) for k, v in ms.items()},
-                "per_call_tflops": {k: round(s.flops() / (v * 1e-3) / 1e12, 2) for k, v in conv_calls.items()},
-                "per_call_hbm_bytes": {k: call_traffic(k, wl.name) for k in CONV_CALLS},
+                "per_call_tflops": {k: round(PRODUCTS[k] * s.flops() / (v * 1e-3) / 1e12, 2)
+                                    for k, v in conv_calls.items()},
+                "per_call_hbm_bytes": {k: call_traffic(k, wl.name) for k in conv_calls},
                 "per_call_mfma_busy": {k: (lambda m: None if m is None else m["busy"])(call_mfma(k, wl.name))
-                                       for k in CONV_CALLS}}
+                                       for k in conv_calls}}
 
     bn = None
     if not args.no_bn:
@@ -617,7 +654,7 @@ def main():
             "data": "synthetic",
             "config": {"workload": f"{wl.name}: {wl.note}", "N": s.N, "H": s.H, "W": s.W, "IC": s.IC,
                        "OC": s.OC, "kernel": f"{s.KH}x{s.KW}", "stride": s.sh, "pad": s.ph,
-                       "step": "forward + activation_backward + backward_data + backward_weight",
+                       "step": " + ".join(n for n, _ in Layer.calls_of(wl)),
                        "launch": "the step's calls captured once in a HIP graph and replayed",
                        "eager_ms_per_step": round(eager_total / args.steps * 1e3, 4),
                        "flops_per_step": flops},

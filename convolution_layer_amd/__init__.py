@@ -24,14 +24,15 @@ F32, BF16 = 0, 1
 ACT_IDENTITY, ACT_RELU, ACT_TANH, ACT_SIGMOID, ACT_GELU = 0, 1, 2, 3, 4
 NORM_NONE, NORM_BATCH, NORM_LAYER, NORM_GROUP = 0, 1, 2, 3
 MODE_TRAIN, MODE_EVAL = 0, 1
-OP_FORWARD, OP_BACKWARD_DATA, OP_BACKWARD_WEIGHT, OP_BN_STATS, OP_ACTIVATION_BACKWARD = range(5)
+OP_FORWARD, OP_BACKWARD_DATA, OP_BACKWARD_WEIGHT, OP_BN_STATS, OP_ACTIVATION_BACKWARD, OP_BACKWARD_FULL = range(6)
 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "MISALIGNED", 5: "HIP"}
 
 # Every symbol include/convmi.h declares.
 EXPORTS = ("convmi_output_dims", "convmi_workspace_size", "conv2d_forward", "conv2d_forward_noalloc",
            "conv2d_backward_data",
-           "conv2d_backward_weight", "bn_stats_training", "activation_backward", "convmi_last_error",
+           "conv2d_backward_weight", "bn_stats_training", "activation_backward", "conv2d_backward_full",
+           "convmi_last_error",
            "convmi_version")
 
 
@@ -67,6 +68,7 @@ def _load():
     L.conv2d_backward_weight.argtypes = [dp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.bn_stats_training.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.activation_backward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.conv2d_backward_full.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, sz, vp]
     for name in EXPORTS:
         if name not in ("convmi_last_error", "convmi_version"):
             getattr(L, name).restype = C.c_int
@@ -183,3 +185,10 @@ def activation_backward(desc, z, dy, gamma, beta, save_mean, save_inv_std, dz, d
     _check(lib.activation_backward(C.byref(desc), _ptr(z), _ptr(dy), _ptr(gamma), _ptr(beta), _ptr(save_mean),
                                    _ptr(save_inv_std), _ptr(dz), _ptr(dgamma), _ptr(dbeta), int(accumulate),
                                    wp, wn, _stream(stream)))
+
+
+def conv2d_backward_full(desc, x, w, saved, saved_is_output, dy, dx, dw, db, accumulate=0, workspace=None,
+                         stream=None):
+    wp, wn = _ws(workspace)
+    _check(lib.conv2d_backward_full(C.byref(desc), _ptr(x), _ptr(w), _ptr(saved), int(saved_is_output), _ptr(dy),
+                                    _ptr(dx), _ptr(dw), _ptr(db), int(accumulate), wp, wn, _stream(stream)))

@@ -152,6 +152,17 @@ size_t ws_act_bwd(const convmi_desc* desc, const ConvDims& d) {
     return desc->normalization == CONVMI_NORM_BATCH ? bn_bwd_ws_bytes(rows_of(d), d.OC, desc->dtype) : 0;
 }
 
+// backward_full: dz (unless the activation is the identity), then the larger of the
+// two products' workspaces (they run one after the other on the stream).
+size_t dz_bytes_full(const convmi_desc* desc, const ConvDims& d) {
+    return desc->activation == CONVMI_ACT_IDENTITY ? 0
+                                                   : align_up((size_t)rows_of(d) * d.OC * dtype_size(desc->dtype), 256);
+}
+size_t ws_backward_full(const convmi_desc* desc, const ConvDims& d) {
+    const size_t a = ws_backward_data(desc, d), b = ws_backward_weight(desc, d);
+    return dz_bytes_full(desc, d) + (a > b ? a : b);
+}
+
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
     if (!a || !b) return false;
     uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -187,6 +198,7 @@ CONVMI_API convmi_status convmi_workspace_size(const convmi_desc* desc, int32_t 
     case CONVMI_OP_BACKWARD_WEIGHT: *bytes = ws_backward_weight(desc, d); break;
     case CONVMI_OP_BN_STATS: *bytes = ws_bn_stats(desc, d); break;
     case CONVMI_OP_ACTIVATION_BACKWARD: *bytes = ws_act_bwd(desc, d); break;
+    case CONVMI_OP_BACKWARD_FULL: *bytes = ws_backward_full(desc, d); break;
     default: return fail(CONVMI_ERR_INVALID_ARG, "unknown op %d", op);
     }
     return CONVMI_OK;
@@ -490,6 +502,57 @@ CONVMI_API convmi_status activation_backward(const convmi_desc* desc, const void
         e = launch_act_bwd(desc->dtype, z, dy, dz, rows_of(d), d.OC, desc->activation, s);
     }
     if (e != hipSuccess) return hip_fail(e, "activation_backward launch");
+    return CONVMI_OK;
+}
+
+CONVMI_API convmi_status conv2d_backward_full(const convmi_desc* desc, const void* x, const void* w, const void* saved,
+                                              int32_t saved_is_output, const void* dy, void* dx, float* dw, float* db,
+                                              int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    if (desc->normalization != CONVMI_NORM_NONE)
+        return fail(CONVMI_ERR_UNSUPPORTED,
+                    "conv2d_backward_full takes unnormalised layers; with a normalisation call activation_backward, "
+                    "then conv2d_backward_data and conv2d_backward_weight");
+    if (saved_is_output != 0 && saved_is_output != 1)
+        return fail(CONVMI_ERR_INVALID_ARG, "saved_is_output must be 0 or 1");
+    if (saved_is_output && desc->activation == CONVMI_ACT_GELU)
+        return fail(CONVMI_ERR_INVALID_ARG, "the GELU derivative is not a function of its output: pass z");
+    CHECK(need(x, "x"));
+    CHECK(need(w, "w"));
+    CHECK(need(saved, saved_is_output ? "y" : "z"));
+    CHECK(need(dy, "dy"));
+    CHECK(need(dw, "dw"));
+    if (dx) CHECK(need(dx, "dx"));
+    if (db) CHECK(need_vec(db, "db"));
+    if (accumulate != 0 && accumulate != 1) return fail(CONVMI_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    const size_t es = dtype_size(desc->dtype);
+    const size_t xb = (size_t)d.N * d.H * d.W * d.IC * es, yb = (size_t)rows_of(d) * d.OC * es;
+    if (dx && (overlaps(dx, xb, x, xb) || overlaps(dx, xb, dy, yb) || overlaps(dx, xb, saved, yb) ||
+               overlaps(dx, xb, w, (size_t)d.OC * d.KH * d.KW * d.IC * es)))
+        return fail(CONVMI_ERR_INVALID_ARG, "dx overlaps an input");
+    CHECK(check_ws(workspace, workspace_bytes, ws_backward_full(desc, d), "conv2d_backward_full"));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    const void* dz = dy;  // identity: act' = 1
+    const size_t zb = dz_bytes_full(desc, d);
+    if (zb) {
+        dz = workspace;
+        e = saved_is_output
+                ? launch_act_bwd_from_output(desc->dtype, saved, dy, workspace, rows_of(d), d.OC, desc->activation, s)
+                : launch_act_bwd(desc->dtype, saved, dy, workspace, rows_of(d), d.OC, desc->activation, s);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_backward_full: activation backward launch");
+    }
+    void* ws = (char*)workspace + zb;
+    e = igemm_dw_supported(desc->dtype, d) ? launch_igemm_dw(desc->dtype, x, dz, dw, db, accumulate, d, ws, s)
+                                           : launch_conv_dw_direct(desc->dtype, x, dz, dw, db, accumulate, d, s);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_backward_full: weight-gradient launch");
+    if (dx) {
+        e = igemm_dx_supported(desc->dtype, d) ? launch_igemm_dx(desc->dtype, dz, w, dx, d, ws, s)
+                                               : launch_conv_dx_direct(desc->dtype, dz, w, dx, d, s);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_backward_full: input-gradient launch");
+    }
     return CONVMI_OK;
 }
 

@@ -99,6 +99,15 @@ template <int ACT> __device__ __forceinline__ float act_slope(float a) {
     else return 1.0f;
 }
 
+// d act / d a written in terms of the output y = act(a) (identity, relu, tanh, sigmoid):
+// 1, [y > 0], 1 - y^2, y (1 - y).  GELU has no such form; callers never pass it.
+template <int ACT> __device__ __forceinline__ float act_slope_out(float y) {
+    if constexpr (ACT == ACT_RELU) return y > 0.0f ? 1.0f : 0.0f;
+    else if constexpr (ACT == ACT_TANH) return __builtin_fmaf(-y, y, 1.0f);
+    else if constexpr (ACT == ACT_SIGMOID) return y * (1.0f - y);
+    else return 1.0f;
+}
+
 // Batch-norm activation input, in a fixed fp32 operation order (subtract, multiply,
 // fused multiply-add) so the ReLU mask can be reproduced exactly off the GPU.
 __device__ __forceinline__ float bn_affine(float z, float mean, float inv_std, float gamma, float beta,

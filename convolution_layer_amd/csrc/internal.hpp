@@ -56,6 +56,10 @@ hipError_t launch_apply_act(int dt, const void* z, void* y, int64_t M, int C, in
 // dz = act'(z) * dy (no norm).
 hipError_t launch_act_bwd(int dt, const void* z, const void* dy, void* dz, int64_t M, int C, int act,
                           hipStream_t s);
+// dz = act'(a) * dy with the derivative taken from the output y = act(a) (no norm;
+// identity, relu, tanh, sigmoid).
+hipError_t launch_act_bwd_from_output(int dt, const void* y, const void* dy, void* dz, int64_t M, int C, int act,
+                                      hipStream_t s);
 // Batch-norm training backward (+ activation derivative), dgamma/dbeta optional.
 hipError_t launch_bn_bwd(int dt, const void* z, const void* dy, void* dz, int64_t M, int C, int act,
                          const float* gamma, const float* beta, const float* mean, const float* inv_std,

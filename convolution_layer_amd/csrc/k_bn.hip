@@ -773,15 +773,15 @@ __global__ __launch_bounds__(kThreads) void apply_act(const T* __restrict__ z, T
     }
 }
 
-// dz = act'(z) * dy, no norm.
-template <typename T, int VEC, int ACT>
+// dz = act'(z) * dy, no norm; FROM_OUT: the derivative from the stored output y instead.
+template <typename T, int VEC, int ACT, bool FROM_OUT = false>
 __global__ __launch_bounds__(kThreads) void act_bwd(const T* __restrict__ z, const T* dy, T* dz, int64_t nvec) {
     for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads) {
         float a[VEC], g[VEC];
         Vec<T, VEC>::load(z + v * VEC, a);
         Vec<T, VEC>::load(dy + v * VEC, g);
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) g[j] *= act_slope<ACT>(a[j]);
+        for (int j = 0; j < VEC; ++j) g[j] *= FROM_OUT ? act_slope_out<ACT>(a[j]) : act_slope<ACT>(a[j]);
         Vec<T, VEC>::store(dz + v * VEC, g);
     }
 }
@@ -942,6 +942,18 @@ hipError_t launch_act_bwd(int dt, const void* z, const void* dy, void* dz, int64
     dim3 grid(elementwise_grid(nvec)), block(kThreads);
     CONVMI_VEC_SWITCH(dt, vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (act_bwd<T, VEC, A><<<grid, block, 0, s>>>(
                                                                    (const T*)z, (const T*)dy, (T*)dz, nvec))));
+    return hipGetLastError();
+}
+
+hipError_t launch_act_bwd_from_output(int dt, const void* y, const void* dy, void* dz, int64_t M, int C, int act,
+                                      hipStream_t s) {
+    const int full = dt == DT_BF16 ? 8 : 4;
+    const int vec = (C % full == 0) ? full : 1;
+    const int64_t nvec = M * C / vec;
+    dim3 grid(elementwise_grid(nvec)), block(kThreads);
+    if (act == ACT_GELU) return hipErrorInvalidValue;
+    CONVMI_VEC_SWITCH(dt, vec, T, VEC, CONVMI_ACT_SWITCH(act, A, (act_bwd<T, VEC, A, true><<<grid, block, 0, s>>>(
+                                                                   (const T*)y, (const T*)dy, (T*)dz, nvec))));
     return hipGetLastError();
 }
 

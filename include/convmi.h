@@ -104,7 +104,8 @@ typedef enum {
     CONVMI_OP_BACKWARD_DATA = 1,
     CONVMI_OP_BACKWARD_WEIGHT = 2,
     CONVMI_OP_BN_STATS = 3,
-    CONVMI_OP_ACTIVATION_BACKWARD = 4
+    CONVMI_OP_ACTIVATION_BACKWARD = 4,
+    CONVMI_OP_BACKWARD_FULL = 5
 } convmi_op;
 
 /* The layer's problem statement: the [generic] listing's compile-time layer spec
@@ -219,6 +220,25 @@ convmi_status activation_backward(const convmi_desc* desc, const void* z, const 
                                   const float* save_mean, const float* save_inv_std,
                                   void* dz, float* dgamma, float* dbeta, int32_t accumulate,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* a4 + a5 + a6 of an unnormalised layer in one call, as the [generic] listing's
+ * backward_full (input gradient and parameter gradients from the output gradient):
+ *   dz = act'(.) * dy;  dx = conv^T(dz, w) (overwritten);  dw (+)= sum dz * x;
+ *   db (+)= sum dz  -- the results of activation_backward followed by
+ * conv2d_backward_data and conv2d_backward_weight, without dz in the caller's memory.
+ *   saved: what the forward kept of the activation input: z (saved_is_output = 0), or
+ *     the output y (saved_is_output = 1) for identity, relu, tanh and sigmoid, whose
+ *     derivative is a function of y -- 1, [y > 0], 1 - y^2, y (1 - y) -- as the [cuda]
+ *     listing's activation backward reads y.  GELU needs z.
+ *   dx may be NULL (no input gradient, as for a network's first layer); dw is
+ *   required, db may be NULL; accumulate as for conv2d_backward_weight.
+ * normalization must be NONE (CONVMI_ERR_UNSUPPORTED otherwise: normalised layers call
+ * activation_backward and then the two products).  Workspace: the size
+ * convmi_workspace_size reports for CONVMI_OP_BACKWARD_FULL (it holds dz unless the
+ * activation is the identity, when dz = dy). */
+convmi_status conv2d_backward_full(const convmi_desc* desc, const void* x, const void* w, const void* saved,
+                                   int32_t saved_is_output, const void* dy, void* dx, float* dw, float* db,
+                                   int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message describing the last non-OK status returned on the calling thread. */
 const char* convmi_last_error(void);

@@ -53,6 +53,8 @@ def _load(path: str, rebuild: bool = False):
     L.oracle_conv2d_backward_weight.argtypes = [_D, _D, _D, _D] + dims
     L.oracle_conv2d_backward_weight_at.argtypes = [_D, _D, _L, _i, _D] + dims
     L.oracle_bias_grad.argtypes = [_D, _i, _i, _D]
+    L.oracle_activation_backward_from_output.restype = C.c_int
+    L.oracle_activation_backward_from_output.argtypes = [_D, _D, _i, C.c_int, _D]
     L.oracle_group_stats.argtypes = [_D, _i, _i, _i, _i, C.c_double, _D, _D, _D]
     L.oracle_apply_group_norm.argtypes = [_D, _i, _i, _i, _i, C.c_int, _D, _D, _D, _D, _D]
     L.oracle_group_norm_backward.argtypes = [_D, _D, _i, _i, _i, _i, C.c_int, _D, _D, _D, _D, _D, _D, _D]
@@ -177,6 +179,17 @@ def activation_backward(z, dy, act, norm=NORM_NONE, gamma=None, beta=None, mean=
                                      _p(_f64(beta)), _p(_f64(mean)), _p(_f64(inv_std)), _p(dz),
                                      _p(dg), _p(dbt))
     return dz, dg, dbt
+
+
+def activation_backward_from_output(y, dy, act):
+    """dz = act'(z) * dy of an unnormalised layer, with the derivative written in terms of
+    the stored output y = act(z) (identity, relu, tanh, sigmoid)."""
+    y, dy = _f64(y), _f64(dy)
+    assert y.shape == dy.shape
+    dz = np.zeros_like(y)
+    if lib().oracle_activation_backward_from_output(_p(y), _p(dy), y.size, act, _p(dz)) != 0:
+        raise ValueError("this activation's derivative is not a function of its output")
+    return dz
 
 
 def conv2d_backward_data(dz, w, x_shape, stride=(1, 1), pad=(0, 0)):

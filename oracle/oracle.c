@@ -247,6 +247,23 @@ void oracle_activation_backward(const double* z, const double* dy, i64 M, i64 C,
     }
 }
 
+/* The same derivative for the unnormalised layer, taken from the layer output y = act(z)
+ * instead of z (the [cuda] listing's cuDNN activation backward reads the output y):
+ *   identity 1,  relu [y > 0] (= [z > 0]),  tanh 1 - y^2,  sigmoid y (1 - y);
+ *   dz = act'(y) * dy.  GELU has no such form (it is not invertible) and is rejected (-1). */
+int oracle_activation_backward_from_output(const double* y, const double* dy, i64 n, int act, double* dz) {
+    if (act == ACT_GELU) return -1;
+#pragma omp parallel for schedule(static)
+    for (i64 i = 0; i < n; ++i) {
+        double s = 1.0, v = y[i];
+        if (act == ACT_RELU) s = v > 0.0 ? 1.0 : 0.0;
+        else if (act == ACT_TANH) s = 1.0 - v * v;
+        else if (act == ACT_SIGMOID) s = v * (1.0 - v);
+        dz[i] = s * dy[i];
+    }
+    return 0;
+}
+
 /* Evaluation-mode batch-norm backward: the statistics are constants, so each element
  * stands alone:
  *   zhat = (z - mean) * inv_std,  a = gamma*zhat + beta,  dno = act'(a) * dy,

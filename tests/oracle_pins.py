@@ -466,6 +466,26 @@ def pin_bn_eval_backward_fd_and_closed_form():
     _close(dg1, (dy * (z - rm)).reshape(-1, 3).sum(0), 1e-13, "eval dgamma closed form")
 
 
+def pin_act_backward_from_output():
+    """The output form of the derivative equals the pre-activation form on y = act(z)
+    (relu mask, 1 - tanh^2, sigmoid (1 - sigmoid)), and torch fp64 autograd; GELU, whose
+    derivative is not a function of its output, is refused."""
+    r = _rng(19)
+    z = r.standard_normal((2, 5, 4, 3)) * 2
+    dy = r.standard_normal(z.shape)
+    for act in (O.ACT_IDENTITY, O.ACT_RELU, O.ACT_TANH, O.ACT_SIGMOID):
+        y = O.apply_activation(z, act)
+        _close(O.activation_backward_from_output(y, dy, act), O.activation_backward(z, dy, act)[0], 1e-14,
+               f"output-form derivative act {act}")
+    y = np.tanh(z)
+    _close(O.activation_backward_from_output(y, dy, O.ACT_TANH), (1 - y * y) * dy, 0, "tanh closed form")
+    try:
+        O.activation_backward_from_output(z, dy, O.ACT_GELU)
+        raise AssertionError("GELU output form accepted")
+    except ValueError:
+        pass
+
+
 # ---------------------------------------------------------------- GELU (tanh form)
 def pin_gelu_values_and_slope():
     """gelu against torch's tanh-form GELU in fp64 (values, autograd slope); closed forms

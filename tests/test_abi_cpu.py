@@ -57,7 +57,7 @@ def test_output_dims_match_workloads(cm, name):
     s = wl.shape
     d = cm.make_desc(s.N, s.H, s.W, s.IC, s.OC, s.KH, s.KW, (s.sh, s.sw), (s.ph, s.pw), wl.act, wl.norm)
     assert cm.output_dims(d) == (s.OH, s.OW)
-    for op in range(5):
+    for op in range(6):
         n = cm.workspace_size(d, op)
         assert n >= 0 and n % 256 == 0
     if wl.norm == WL.NORM_BATCH:

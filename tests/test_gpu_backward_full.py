@@ -1,0 +1,102 @@
+"""GPU parity of conv2d_backward_full (the [generic] listing's backward_full: the
+activation derivative, dX and dW/db of an unnormalised layer in one call) against the
+oracle's composition activation_backward -> conv2d_backward_data / _weight, with the
+derivative taken from the stored z or from the stored output y (identity, relu, tanh,
+sigmoid: 1, [y > 0], 1 - y^2, y(1 - y)).  Both sides get the same rounded z or y and dy;
+the library keeps dz in the data type between the steps, as the pages store it."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import convolution_layer_amd  # noqa: F401
+
+
+CASES = [
+    ((2, 15, 15, 128, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH),
+    ((1, 40, 37, 64, 64, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_IDENTITY),
+    ((2, 13, 11, 64, 64, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_RELU),
+    ((2, 23, 23, 4, 32, 8, 8, 4, 4, 0, 0), WL.F32, WL.ACT_SIGMOID),
+    ((2, 10, 12, 3, 8, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_GELU),
+    ((2, 9, 70, 128, 256, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+]
+
+
+def _ids(c):
+    s = c[0]
+    return f"{'x'.join(map(str, s[:7]))}_s{s[7]}_{c[1]}_a{c[2]}"
+
+
+def _run(desc, dt, shape, x, w, saved, from_out, dy, with_dx=True):
+    import convolution_layer_amd as cm
+    dx = torch.empty(shape.x_shape, dtype=G.tdtype(dt), device="cuda") if with_dx else None
+    dw = torch.empty(shape.w_shape, dtype=torch.float32, device="cuda")
+    db = torch.empty(shape.OC, dtype=torch.float32, device="cuda")
+    cm.conv2d_backward_full(desc, G.dev(x, dt), G.dev(w, dt), G.dev(saved, dt), int(from_out), G.dev(dy, dt), dx, dw,
+                            db, 0, cm.workspace(desc, cm.OP_BACKWARD_FULL))
+    return dx, dw, db
+
+
+def _check(shape, dt, act, x, w, z, dy, from_out, name, with_dx=True):
+    st, pd = (shape.sh, shape.sw), (shape.ph, shape.pw)
+    desc = G.shape_desc(shape, dt, act)
+    if from_out:
+        saved = WL.round_to(dt, O.apply_activation(z, act))
+        dz_r = O.activation_backward_from_output(saved, dy, act)
+    else:
+        saved = z
+        dz_r = O.activation_backward(z, dy, act)[0]
+    dx, dw, db = _run(desc, dt, shape, x, w, saved, from_out, dy, with_dx)
+    if with_dx:
+        G.assert_close(G.host(dx), O.conv2d_backward_data(dz_r, w, shape.x_shape, st, pd), dt, f"{name} dx")
+    dw_r, db_r = O.conv2d_backward_weight(x, dz_r, shape.w_shape, st, pd)
+    G.assert_close(G.host(dw), dw_r, dt, f"{name} dw")
+    G.assert_close(G.host(db), db_r, dt, f"{name} db")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_backward_full_matches_composition(case):
+    s, dt, act = case
+    shape = WL.ConvShape(*s)
+    r = np.random.default_rng(400)
+    x = WL.round_to(dt, r.standard_normal(shape.x_shape))
+    w = WL.round_to(dt, r.standard_normal(shape.w_shape) * (2.0 / shape.Kdim) ** 0.5)
+    z = WL.round_to(dt, r.standard_normal(shape.y_shape) * 1.5)
+    dy = WL.round_to(dt, r.standard_normal(shape.y_shape))
+    _check(shape, dt, act, x, w, z, dy, False, "from z")
+    if act != WL.ACT_GELU:
+        _check(shape, dt, act, x, w, z, dy, True, "from y")
+    _check(shape, dt, act, x, w, z, dy, act != WL.ACT_GELU, "no dx", with_dx=False)
+
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_backward_full_workloads(name):
+    """The bench's backward at full size, from the stored output y, every element."""
+    wl = WL.WORKLOADS[name]
+    s, dt = wl.shape, wl.dtype
+    d = WL.make_inputs(wl)
+    z = WL.round_to(dt, O.conv2d_forward(d["x"], d["w"], d.get("b"), (s.sh, s.sw), (s.ph, s.pw)))
+    _check(s, dt, wl.act, d["x"], d["w"], z, d["dy"], True, f"{name} full")
+
+
+def test_backward_full_refuses_normalised_layers_and_gelu_output():
+    import convolution_layer_amd as cm
+    shape = WL.ConvShape(1, 8, 8, 8, 8, 3, 3, 1, 1, 1, 1)
+    t = torch.zeros(64, dtype=torch.float32, device="cuda")
+    desc = G.shape_desc(shape, WL.F32, WL.ACT_RELU, WL.NORM_BATCH)
+    with pytest.raises(cm.ConvmiError) as e:
+        cm.conv2d_backward_full(desc, t, t, t, 0, t, t, t, None)
+    assert e.value.status == cm.ERR_UNSUPPORTED
+    desc = G.shape_desc(shape, WL.F32, WL.ACT_GELU)
+    with pytest.raises(cm.ConvmiError) as e:
+        cm.conv2d_backward_full(desc, t, t, t, 1, t, t, t, None)
+    assert e.value.status == cm.ERR_INVALID_ARG

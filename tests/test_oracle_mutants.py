@@ -57,6 +57,9 @@ MUTANTS = [
      "inv_std[c] = 1.0 / sqrt(running_var[c]);", 0),
     ("bneval_inv_std_missing", "dz[i] = dno * g * is;", "dz[i] = dno * g;", 0),
     ("bneval_dgamma_no_zhat", "sg += dno * zh;", "sg += dno;", 1),
+    ("outform_tanh", "else if (act == ACT_TANH) s = 1.0 - v * v;", "else if (act == ACT_TANH) s = 1.0 - v;", 0),
+    ("outform_sigmoid", "else if (act == ACT_SIGMOID) s = v * (1.0 - v);", "else if (act == ACT_SIGMOID) s = v * (1.0 + v);", 0),
+    ("outform_relu_mask", "if (act == ACT_RELU) s = v > 0.0 ? 1.0 : 0.0;", "if (act == ACT_RELU) s = v >= 0.0 ? 1.0 : 0.0;", 0),
     ("gelu_value_cubic_dropped", "(a + GELU_K1 * a * a * a)", "(a)", 0),
     ("gelu_slope_cubic_factor", "(1.0 + 3.0 * GELU_K1 * a * a)", "(1.0 + GELU_K1 * a * a)", 0),
     ("gelu_slope_half_dropped", "return 0.5 * (1.0 + t) + 0.5 * a", "return (1.0 + t) + 0.5 * a", 0),
