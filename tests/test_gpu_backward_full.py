@@ -28,6 +28,11 @@ CASES = [
     ((2, 23, 23, 4, 32, 8, 8, 4, 4, 0, 0), WL.F32, WL.ACT_SIGMOID),
     ((2, 10, 12, 3, 8, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_GELU),
     ((2, 9, 70, 128, 256, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+    # the stride-1 weight-gradient kernel with a run-time k-step count, 64-channel tiles
+    # (one and several segments per row)
+    ((2, 12, 48, 128, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_SIGMOID),
+    ((2, 10, 32, 64, 64, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH),
+    ((1, 9, 224, 64, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
 ]
 
 
@@ -86,6 +91,29 @@ def test_backward_full_workloads(name):
     d = WL.make_inputs(wl)
     z = WL.round_to(dt, O.conv2d_forward(d["x"], d["w"], d.get("b"), (s.sh, s.sw), (s.ph, s.pw)))
     _check(s, dt, wl.act, d["x"], d["w"], z, d["dy"], True, f"{name} full")
+
+
+@pytest.mark.parametrize("s", [(2, 15, 15, 128, 128, 3, 3, 1, 1, 1, 1), (2, 10, 32, 64, 64, 3, 3, 1, 1, 1, 1)])
+def test_backward_full_relu_bitwise_equals_separate_calls(s):
+    """ReLU: the output-form mask [y > 0] equals [z > 0], so backward_full must reproduce
+    activation_backward -> conv2d_backward_weight / conv2d_backward_data bit for bit."""
+    import convolution_layer_amd as cm
+    shape, dt, act = WL.ConvShape(*s), WL.BF16, WL.ACT_RELU
+    r = np.random.default_rng(410)
+    x = G.dev(WL.round_to(dt, r.standard_normal(shape.x_shape)), dt)
+    w = G.dev(WL.round_to(dt, r.standard_normal(shape.w_shape) * 0.05), dt)
+    z = WL.round_to(dt, r.standard_normal(shape.y_shape))
+    y = G.dev(np.maximum(z, 0.0), dt)
+    dy = G.dev(WL.round_to(dt, r.standard_normal(shape.y_shape)), dt)
+    desc = G.shape_desc(shape, dt, act)
+    dx = torch.empty(shape.x_shape, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty(shape.w_shape, dtype=torch.float32, device="cuda")
+    db = torch.empty(shape.OC, dtype=torch.float32, device="cuda")
+    cm.conv2d_backward_full(desc, x, w, y, 1, dy, dx, dw, db, 0, cm.workspace(desc, cm.OP_BACKWARD_FULL))
+    dz, _, _ = G.run_act_bwd(desc, dt, G.dev(z, dt), dy)
+    dw2, db2 = G.run_backward_weight(desc, x, dz)
+    dx2 = G.run_backward_data(desc, dt, dz, w)
+    assert torch.equal(dw, dw2) and torch.equal(db, db2) and torch.equal(dx, dx2)
 
 
 def test_backward_full_refuses_normalised_layers_and_gelu_output():
