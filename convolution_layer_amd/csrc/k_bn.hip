@@ -293,9 +293,19 @@ __device__ __forceinline__ void merge_slabs(const float* __restrict__ part, int 
         double a = 0.0, b = 0.0;
         if (own) {
             const float* p1 = part + (int64_t)c * 2 * slabs;
-            for (int k = j; k < slabs; k += p2) {
-                a += (double)p1[k];
-                b += (double)p1[slabs + k];
+            for (int k0 = j; k0 < slabs; k0 += 8 * p2) {  // eight slabs' loads in flight, then their sums in order
+                float va[8], vb[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int k = k0 + u * p2;
+                    va[u] = k < slabs ? p1[k] : 0.0f;
+                    vb[u] = k < slabs ? p1[slabs + k] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    a += (double)va[u];
+                    b += (double)vb[u];
+                }
             }
         }
         dred[2 * t] = a;
