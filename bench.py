@@ -73,7 +73,9 @@ def source_hash() -> str:
 class Layer:
     """Device buffers and the four library calls of one training step."""
 
-    def __init__(self, wl: WL.Workload, x=None, evaluation=False):
+    def __init__(self, wl: WL.Workload, x=None, evaluation=False, norm=None):
+        """norm: None, or (normalization, groups, activation) replacing the workload's
+        (layer / group norm variants on the workload's shape)."""
         import torch
 
         import convolution_layer_amd as cm
@@ -84,6 +86,11 @@ class Layer:
         self.desc = G.desc_for(wl)
         if evaluation:
             self.desc.mode = cm.MODE_EVAL
+        if norm is not None:
+            self.desc.normalization, self.desc.groups, self.desc.activation = norm
+            r = np.random.default_rng(97)
+            d.setdefault("gamma", WL.round_to(WL.F32, r.uniform(0.5, 1.5, s.OC)))
+            d.setdefault("beta", WL.round_to(WL.F32, r.normal(0.0, 0.1, s.OC)))
         dev = lambda a, t=None: G.dev(a, t)
         self.x = x if x is not None else dev(d["x"], dt)  # a chained layer takes the previous y
         self.w = dev(d["w"], dt)
@@ -92,6 +99,8 @@ class Layer:
         self.bn = wl.norm == WL.NORM_BATCH
         self.gamma, self.beta = dev(d.get("gamma")), dev(d.get("beta"))
         self.rm, self.rv = dev(d.get("running_mean")), dev(d.get("running_var"))
+        if norm is not None:  # layer / group norm keep no running statistics
+            self.rm = self.rv = None
         tdt = G.tdtype(dt)
         self.z = torch.empty(s.y_shape, dtype=tdt, device="cuda")
         self.y = torch.empty(s.y_shape, dtype=tdt, device="cuda")
@@ -99,9 +108,11 @@ class Layer:
         self.dx = torch.empty(s.x_shape, dtype=tdt, device="cuda")
         self.dw = torch.empty(s.w_shape, dtype=torch.float32, device="cuda")
         self.db = torch.empty(s.OC, dtype=torch.float32, device="cuda")
-        f32 = lambda: torch.empty(s.OC, dtype=torch.float32, device="cuda")
-        self.sm, self.si, self.dg, self.dbt = (f32(), f32(), f32(), f32()) if self.bn else (None,) * 4
-        n = max(cm.workspace_size(self.desc, op) for op in (range(6) if wl.norm == WL.NORM_NONE else range(5)))
+        f32 = lambda n=s.OC: torch.empty(n, dtype=torch.float32, device="cuda")
+        normed = self.desc.normalization != cm.NORM_NONE
+        self.sm, self.si = (f32(cm.stat_count(self.desc)), f32(cm.stat_count(self.desc))) if normed else (None, None)
+        self.dg, self.dbt = (f32(), f32()) if normed else (None, None)
+        n = max(cm.workspace_size(self.desc, op) for op in range(6))
         self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
 
     def forward(self):
@@ -242,13 +253,17 @@ def time_graph(f, calls=20, replays=10):
 REPORT_ORDER = ("c1", "c2a", "c2b", "c2c", "c3", "c4", "c5")
 
 
-def call_bytes(wl: WL.Workload, call: str, evaluation: bool = False) -> int:
-    """Algorithmic HBM bytes of one call: what the operation itself must read and write."""
+def call_bytes(wl: WL.Workload, call: str, evaluation: bool = False, norm: bool = False) -> int:
+    """Algorithmic HBM bytes of one call: what the operation itself must read and write.
+    norm: a layer / group norm variant of the workload (statistics pass over z)."""
     s = wl.shape
     e = 2 if wl.dtype == WL.BF16 else 4
     x, w, y = s.N * s.H * s.W * s.IC, s.OC * s.KH * s.KW * s.IC, s.P * s.OC
+    if call == "norm_stats":
+        return y * e
     if call == "forward":  # x, w, bias, z and y (training batch norm: + the statistics pass over z)
-        return (x + w + 2 * y) * e + 4 * s.OC + (y * e if wl.norm == WL.NORM_BATCH and not evaluation else 0)
+        stats = (wl.norm == WL.NORM_BATCH and not evaluation) or norm
+        return (x + w + 2 * y) * e + 4 * s.OC + (y * e if stats else 0)
     if call == "forward_y":  # x, w, bias -> y
         return (x + w + y) * e + 4 * s.OC
     if call == "backward_full":  # x, w, y, dy -> dx, dw (fp32), db
@@ -336,18 +351,26 @@ def report(replays=10):
             ev = Layer(wl, x=layer.x, evaluation=True)
             ev.forward()
             calls += [("forward[eval]", ev.forward), ("activation_backward[eval]", ev.act_bwd)]
+        if name in ("c3", "c4"):  # layer norm and group norm (8 groups) with GELU on the same shape
+            import convolution_layer_amd as cm
+            for tag, norm in (("layer", (cm.NORM_LAYER, 1, cm.ACT_GELU)), ("group8", (cm.NORM_GROUP, 8, cm.ACT_GELU))):
+                v = Layer(wl, x=layer.x, norm=norm)
+                v.forward()
+                calls += [(f"forward[{tag}]", v.forward), (f"norm_stats[{tag}]", v.bn_stats),
+                          (f"activation_backward[{tag}]", v.act_bwd)]
         for cname, f in calls:
             warm, cold, k = cold_warm_ms(f, replays)
             row = {"config": name, "call": cname, "dtype": wl.dtype, "graph_calls": k,
                    "warm_ms": {q: round(float(np.percentile(warm, p)), 5) for q, p in (("p10", 10), ("median", 50), ("p90", 90))},
                    "cold_ms": {q: round(float(np.percentile(cold, p)), 5) for q, p in (("p10", 10), ("median", 50), ("p90", 90))}}
             med = row["warm_ms"]["median"]
-            by = call_bytes(wl, cname.split("[")[0], evaluation=cname.endswith("[eval]"))
+            by = call_bytes(wl, cname.split("[")[0], evaluation=cname.endswith("[eval]"),
+                            norm=cname.endswith("[layer]") or cname.endswith("[group8]"))
             row["GB/s"] = round(by / (med * 1e-3) / 1e9, 1)
             row["hbm_frac"] = round(row["GB/s"] / PEAK_HBM_GBS, 4)
             row["cold_GB/s"] = round(by / (row["cold_ms"]["median"] * 1e-3) / 1e9, 1)
             row["cold_hbm_frac"] = round(row["cold_GB/s"] / PEAK_HBM_GBS, 4)
-            if cname in ("forward", "forward[eval]", "forward_y", "backward_data", "backward_weight", "backward_full"):
+            if cname.startswith("forward") or cname in ("backward_data", "backward_weight", "backward_full"):
                 tf = (2 if cname == "backward_full" else 1) * wl.shape.flops() / (med * 1e-3) / 1e12
                 row["TFLOP/s"] = round(tf, 3)
                 row["mfma_frac"] = round(tf / PEAK_TFLOPS[wl.dtype], 4)

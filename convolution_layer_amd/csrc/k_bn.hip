@@ -654,7 +654,9 @@ __global__ __launch_bounds__(kThreads) void grp_bwd_merge(const float* __restric
 
 // Workgroups 0 .. N*G-1: per (n, g) S1 = sum_c gamma_c A_nc, S2 = sum_c gamma_c B_nc
 // (channels of the group, fixed order) -> coef[(n*G + g)*2] = S1/cnt, [+1] = S2/cnt.
-// Workgroups N*G ..: per channel dgamma (+)= sum_n B_nc, dbeta (+)= sum_n A_nc.
+// Workgroups N*G .. N*G+C-1: channel c = blockIdx - N*G, dgamma (+)= sum_n B_nc,
+// dbeta (+)= sum_n A_nc (thread t takes samples t, t + kThreads, ..., then a fixed-order
+// tree over the threads).
 __global__ __launch_bounds__(kThreads) void grp_bwd_coef(const double* __restrict__ ab, int N, int C, int G,
                                                          double cnt, const float* __restrict__ gamma,
                                                          float* __restrict__ dgamma, float* __restrict__ dbeta,
@@ -678,15 +680,19 @@ __global__ __launch_bounds__(kThreads) void grp_bwd_coef(const double* __restric
         }
         return;
     }
-    const int c = (blockIdx.x - N * G) * kThreads + t;
-    if (c >= C || (!dgamma && !dbeta)) return;
+    const int c = blockIdx.x - N * G;
+    if (!dgamma && !dbeta) return;  // uniform per workgroup
     double a = 0.0, b = 0.0;
-    for (int n = 0; n < N; ++n) {
+    for (int n = t; n < N; n += kThreads) {
         a += ab[((int64_t)n * C + c) * 2];
         b += ab[((int64_t)n * C + c) * 2 + 1];
     }
-    if (dgamma) dgamma[c] = accumulate ? (float)((double)dgamma[c] + b) : (float)b;
-    if (dbeta) dbeta[c] = accumulate ? (float)((double)dbeta[c] + a) : (float)a;
+    a = block_sum(a, dred);
+    b = block_sum(b, dred);
+    if (t == 0) {
+        if (dgamma) dgamma[c] = accumulate ? (float)((double)dgamma[c] + b) : (float)b;
+        if (dbeta) dbeta[c] = accumulate ? (float)((double)dbeta[c] + a) : (float)a;
+    }
 }
 
 // dz = inv_std_ng (gamma_c dno - k1_ng - zhat k2_ng); grid (blocks per sample, N).
@@ -1079,8 +1085,8 @@ hipError_t launch_grp_bwd(int dt, const void* z, const void* dy, void* dz, int N
     if (e != hipSuccess) return e;
     grp_bwd_merge<<<(int)ceil_div((int64_t)N * C, kThreads), block, 0, s>>>(part, p.bps, N, C, ab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    grp_bwd_coef<<<N * G + (int)ceil_div(C, kThreads), block, 0, s>>>(ab, N, C, G, (double)S * (C / G), gamma, dgamma,
-                                                                      dbeta, accumulate, coef);
+    grp_bwd_coef<<<N * G + C, block, 0, s>>>(ab, N, C, G, (double)S * (C / G), gamma, dgamma, dbeta, accumulate,
+                                             coef);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t per_sample = S * C;
     dim3 g2(per_sample_grid(N, per_sample / p.vec), N);
