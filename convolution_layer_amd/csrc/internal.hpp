@@ -94,6 +94,8 @@ bool igemm_dw_supported(int dt, const ConvDims& d);
 size_t igemm_fwd_ws_bytes(int dt, const ConvDims& d);
 size_t igemm_dx_ws_bytes(int dt, const ConvDims& d);
 size_t igemm_dw_ws_bytes(int dt, const ConvDims& d);
+// True when the weight-gradient kernel's workgroups leave room on a CU for others.
+bool dw_leaves_room(int dt, const ConvDims& d);
 hipError_t launch_igemm_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
                             const ConvDims& d, int act, void* ws, hipStream_t s);
 hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, const ConvDims& d, void* ws,

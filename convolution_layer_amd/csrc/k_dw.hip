@@ -1175,6 +1175,13 @@ int dw3_ch(int dt, const ConvDims& d) {
     return 0;
 }
 bool dw3_ok(int dt, const ConvDims& d) { return dw3_ch(dt, d) != 0; }
+}  // namespace
+
+// The 64-channel stride-1 kernel runs two-wave workgroups with a small LDS ring, so a CU
+// that holds some of them still has room for input-gradient workgroups.
+bool dw_leaves_room(int dt, const ConvDims& d) { return dw3_ch(dt, d) == 64; }
+
+namespace {
 // fp32 stride-1 layers with 64-channel multiples and kernels at most 3 wide, on output
 // rows of at least 16 positions (shorter rows leave most of a 16-position stage padding;
 // the per-tap kernel is faster there: c2c's 7-wide rows).

@@ -18,9 +18,11 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller (for example the
- *     data_ptr() of torch tensors on the same GPU).  The library never allocates,
- *     frees or synchronises: every kernel is enqueued on `stream` (a hipStream_t;
- *     NULL means the default stream) and the call returns before the work is done.
+ *     data_ptr() of torch tensors on the same GPU).  The library never allocates or
+ *     frees device memory and never waits on the host: every kernel is enqueued on
+ *     `stream` (a hipStream_t; NULL means the default stream) and the call returns
+ *     before the work is done.  (conv2d_backward_full may also run part of its work on
+ *     one library stream per device, ordered with `stream` by events; see there.)
  *   - Layouts are dense and row-major, as the [cuda] listing requires of its inputs:
  *       x, dx          [N][H][W][IC]
  *       w              [OC][KH][KW][IC]
@@ -235,7 +237,16 @@ convmi_status activation_backward(const convmi_desc* desc, const void* z, const 
  * normalization must be NONE (CONVMI_ERR_UNSUPPORTED otherwise: normalised layers call
  * activation_backward and then the two products).  Workspace: the size
  * convmi_workspace_size reports for CONVMI_OP_BACKWARD_FULL (it holds dz unless the
- * activation is the identity, when dz = dy). */
+ * activation is the identity, when dz = dy, and the two products' own workspaces side
+ * by side).
+ * Streams: with dx requested on a bf16 stride-1 layer whose weight gradient takes
+ * 64-channel tiles (small workgroups that leave room on a CU), the weight gradient runs
+ * on a second stream that the library creates once per device (default priority),
+ * forked from `stream` after dz and joined back into it with events, while the input
+ * gradient runs on `stream`; every other layer runs both on `stream`.  For the
+ * caller the call stays ordered on `stream` like any other, and it can be captured into
+ * a HIP graph (the fork and join become graph dependencies).  Calls on one device share
+ * that second stream, so their weight gradients run in issue order. */
 convmi_status conv2d_backward_full(const convmi_desc* desc, const void* x, const void* w, const void* saved,
                                    int32_t saved_is_output, const void* dy, void* dx, float* dw, float* db,
                                    int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream);

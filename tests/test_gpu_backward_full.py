@@ -128,3 +128,66 @@ def test_backward_full_refuses_normalised_layers_and_gelu_output():
     with pytest.raises(cm.ConvmiError) as e:
         cm.conv2d_backward_full(desc, t, t, t, 1, t, t, t, None)
     assert e.value.status == cm.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("s", [(2, 15, 15, 128, 128, 3, 3, 1, 1, 1, 1), (2, 10, 32, 64, 64, 3, 3, 1, 1, 1, 1),
+                               (2, 13, 11, 64, 64, 3, 3, 1, 1, 1, 1)])
+def test_backward_full_side_stream_in_graph_and_on_a_caller_stream(s):
+    """The weight gradient runs on the library's second stream, forked from and joined into
+    the caller's: eager on a non-default stream, then captured into a HIP graph and replayed
+    three times (with eager calls and synchronisations between the replays), every result
+    equals the call on the default stream bit for bit, and the work that follows on the
+    caller's stream sees finished gradients."""
+    import convolution_layer_amd as cm
+    shape = WL.ConvShape(*s)
+    dt = WL.BF16 if s[3] == 128 or s[1] == 10 else WL.F32
+    act = WL.ACT_TANH
+    r = np.random.default_rng(420)
+    x = G.dev(WL.round_to(dt, r.standard_normal(shape.x_shape)), dt)
+    w = G.dev(WL.round_to(dt, r.standard_normal(shape.w_shape) * 0.05), dt)
+    y = G.dev(WL.round_to(dt, np.tanh(r.standard_normal(shape.y_shape))), dt)
+    dy = G.dev(WL.round_to(dt, r.standard_normal(shape.y_shape)), dt)
+    desc = G.shape_desc(shape, dt, act)
+    ws = cm.workspace(desc, cm.OP_BACKWARD_FULL)
+    tdt = G.tdtype(dt)
+
+    def outs():
+        return (torch.empty(shape.x_shape, dtype=tdt, device="cuda"),
+                torch.empty(shape.w_shape, dtype=torch.float32, device="cuda"),
+                torch.empty(shape.OC, dtype=torch.float32, device="cuda"))
+
+    ref = outs()
+    cm.conv2d_backward_full(desc, x, w, y, 1, dy, *ref, 0, ws)
+    torch.cuda.synchronize()
+    ref = tuple(t.clone() for t in ref)
+
+    side = torch.cuda.Stream()
+    got = outs()
+    with torch.cuda.stream(side):
+        cm.conv2d_backward_full(desc, x, w, y, 1, dy, *got, 0, ws, stream=side)
+        sums = [t.double().sum() for t in got]  # ordered after the join on the same stream
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(ref, got))
+    assert all(float(a) == float(t.double().sum()) for a, t in zip(sums, ref))
+
+    g_out = outs()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        cm.conv2d_backward_full(desc, x, w, y, 1, dy, *g_out, 0, ws, stream=cap)  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cm.conv2d_backward_full(desc, x, w, y, 1, dy, *g_out, 0, ws)
+    for rep in range(3):
+        for t in g_out:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(ref, g_out)), f"replay {rep}"
+        other = outs()
+        cm.conv2d_backward_full(desc, x, w, y, 1, dy, *other, 0, ws)  # eager work between replays
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(ref, other))
+    del g
