@@ -569,6 +569,71 @@ def call_mfma(call: str, workload: str):
             "kernel_us": None if t is None else round(t, 2)}
 
 
+def vendor(names=("c3", "c4", "c5"), reps=20):
+    """Context, not part of the bench line: the vendor libraries on the same GPU and the same
+    shapes -- torch's conv2d and its convolution_backward (MIOpen on ROCm; channels-last, so
+    NHWC like ours) and torch.matmul (hipBLASLt) on the implicit-GEMM shape [P, KH*KW*IC] x
+    [KH*KW*IC, OC] -- beside this library's forward (convolution + bias, no normalisation or
+    activation), input-gradient and weight-gradient calls, all timed the same way: eager
+    calls between HIP events, median of `reps` after warm-up, inputs resident."""
+    import torch
+    import torch.nn.functional as F
+    import convolution_layer_amd as cm
+    torch.backends.cudnn.benchmark = True
+
+    def med_us(f):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(ts))
+
+    for name in names:
+        wl = WL.WORKLOADS[name]
+        s = wl.shape
+        tdt = torch.bfloat16 if wl.dtype == WL.BF16 else torch.float32
+        cl = torch.channels_last
+        g = torch.Generator(device="cuda").manual_seed(1)
+        x = torch.randn(s.N, s.IC, s.H, s.W, device="cuda", generator=g).to(tdt).contiguous(memory_format=cl)
+        w = (0.05 * torch.randn(s.OC, s.IC, s.KH, s.KW, device="cuda", generator=g)).to(tdt).contiguous(memory_format=cl)
+        b = torch.randn(s.OC, device="cuda", generator=g).to(tdt) if wl.b_dist is not None else None
+        dy = torch.randn(s.N, s.OC, s.OH, s.OW, device="cuda", generator=g).to(tdt).contiguous(memory_format=cl)
+        st, pd = [s.sh, s.sw], [s.ph, s.pw]
+        bwd = lambda mask: torch.ops.aten.convolution_backward(dy, x, w, [s.OC], st, pd, [1, 1], False, [0, 0], 1, mask)
+        K = s.KH * s.KW * s.IC
+        A = torch.randn(s.P, K, device="cuda", generator=g).to(tdt)
+        B = torch.randn(K, s.OC, device="cuda", generator=g).to(tdt)
+        ven = {"forward": med_us(lambda: F.conv2d(x, w, b, stride=st, padding=pd)),
+               "backward_data": med_us(lambda: bwd([True, False, False])),
+               "backward_weight": med_us(lambda: bwd([False, True, True])),
+               "gemm": med_us(lambda: A @ B)}
+        del x, w, b, dy, A, B
+        torch.cuda.empty_cache()
+        layer = Layer(wl, norm=(cm.NORM_NONE, 1, cm.ACT_IDENTITY))
+        layer.forward_y()
+        layer.dz.copy_(layer.dy)  # identity activation: dz = dy
+        torch.cuda.synchronize()
+        ours = {"forward": med_us(layer.forward_y), "backward_data": med_us(layer.bwd_data),
+                "backward_weight": med_us(layer.bwd_weight)}
+        del layer
+        torch.cuda.empty_cache()
+        tf = lambda us: round(s.flops() / (us * 1e-6) / 1e12, 1)
+        print(json.dumps({"workload": name, "dtype": wl.dtype, "timing": f"eager, HIP events, median of {reps}",
+                          "vendor_us": {k: round(v, 2) for k, v in ven.items()},
+                          "vendor_TFLOP/s": {k: tf(v) for k, v in ven.items()},
+                          "convmi_us": {k: round(v, 2) for k, v in ours.items()},
+                          "convmi_TFLOP/s": {k: tf(v) for k, v in ours.items()},
+                          "speedup": {k: round(ven[k] / ours[k], 2) for k in ours}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -584,12 +649,17 @@ def main():
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--report", action="store_true",
                     help="time every call of every configuration (warm and cold) instead of the bench step")
+    ap.add_argument("--vendor", action="store_true",
+                    help="time MIOpen (torch conv2d) and hipBLASLt (torch.matmul) beside this library on c3-c5")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.workload)
         return
     if args.report:
         report()
+        return
+    if args.vendor:
+        vendor()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is not built.",

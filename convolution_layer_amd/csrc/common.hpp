@@ -108,8 +108,10 @@ template <int ACT> __device__ __forceinline__ float act_slope_out(float y) {
     else return 1.0f;
 }
 
-// Batch-norm activation input, in a fixed fp32 operation order (subtract, multiply,
-// fused multiply-add) so the ReLU mask can be reproduced exactly off the GPU.
+// Normalised activation input a = gamma (z - mean) inv_std + beta, in one fixed fp32
+// operation order (subtract, multiply, fused multiply-add) shared by every kernel that
+// forms it, so the fused epilogues, the separate normalise pass and the backward passes
+// agree bit for bit on a (and hence on the activation's derivative at a).
 __device__ __forceinline__ float bn_affine(float z, float mean, float inv_std, float gamma, float beta,
                                            float* zhat_out) {
     float zh = (z - mean) * inv_std;
