@@ -48,6 +48,12 @@ MEDIUM = [
     ((2, 11, 11, 16, 16, 3, 3, 2, 2, 1, 1), WL.BF16, WL.ACT_SIGMOID),
     ((3, 12, 10, 32, 96, 5, 5, 1, 1, 2, 2), WL.F32, WL.ACT_TANH),
     ((2, 30, 30, 64, 32, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+    # degenerate geometry: a one-pixel image under a 3x3 kernel; padding wider than the
+    # kernel's reach (border outputs see only zeros: bias alone); stride larger than the
+    # kernel (input pixels no tap touches get a zero gradient)
+    ((1, 1, 1, 16, 16, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+    ((2, 3, 4, 8, 16, 3, 3, 1, 1, 2, 2), WL.F32, WL.ACT_TANH),
+    ((2, 10, 10, 8, 8, 2, 2, 3, 3, 0, 0), WL.F32, WL.ACT_SIGMOID),
     # stride-1 shapes for the input-tile-reuse kernels: rows split into segments,
     # KH != KW, asymmetric padding, ragged output channels (vector and scalar stores),
     # one and two halo buffers
