@@ -72,7 +72,7 @@ convmi_status check_desc(const convmi_desc* d, ConvDims* out) {
         d->N * d->H * d->W > kI32Max || d->OC * d->KH * d->KW * d->IC > kI32Max ||
         d->stride_h > 65535 || d->stride_w > 65535 || d->pad_h > 65535 || d->pad_w > 65535 ||
         d->H > kI32Max / 4 || d->W > kI32Max / 4)
-        return fail(CONVMI_ERR_UNSUPPORTED, "problem exceeds the int32 index limits of this build");
+        return fail(CONVMI_ERR_UNSUPPORTED, "problem exceeds the int32 index limits of the kernels");
     if (out) {
         *out = ConvDims{(int)d->N, (int)d->H, (int)d->W, (int)d->IC, (int)d->OC, (int)d->KH, (int)d->KW,
                         d->stride_h, d->stride_w, d->pad_h, d->pad_w, (int)OH, (int)OW};

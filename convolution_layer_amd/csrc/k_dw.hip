@@ -1,4 +1,4 @@
-// k_dw.hip -- weight and bias gradients (a6) as a split-K GEMM on gfx950 MFMA.
+// k_dw.hip -- weight and bias gradients as a split-K GEMM on gfx950 MFMA.
 //
 //   dw[oc][k] = sum_p dz[p][oc] * x_col[p][k],   db[oc] = sum_p dz[p][oc]
 //   p = (n, oh, ow) over the N*OH*OW output positions (the reduction),

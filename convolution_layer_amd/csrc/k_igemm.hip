@@ -1,14 +1,14 @@
 // k_igemm.hip -- convolution forward and input gradient as implicit GEMM on gfx950 MFMA.
 //
-// Forward (a1, with the bias + activation epilogue of a3 fused when there is no batch
-// norm):  C[m][n] = sum_k A[m][k] * B[n][k]
+// Forward (convolution + bias, with the activation epilogue fused when there is no
+// normalisation):  C[m][n] = sum_k A[m][k] * B[n][k]
 //   m = (n_img, oh, ow)  rows of z, y         (M = N*OH*OW)
 //   n = oc                                     (N = OC)
 //   k = (kh, kw, ic)     ic fastest            (K = KH*KW*IC)
 //   A[m][k] = x[n_img, oh*sh - ph + kh, ow*sw - pw + kw, ic] (0 outside)   -- gathered
 //   B[n][k] = w[oc, kh, kw, ic]                                            -- w as stored
 //
-// Input gradient (a5), any stride, as one GEMM over "phase blocks":  write
+// Input gradient, any stride, as one GEMM over "phase blocks":  write
 // ih + ph = sh*qh + rh (0 <= rh < sh), likewise for w.  A tap kh reaches input row ih
 // only from oh = qh - a where kh = rh + sh*a, so with KHs = ceil(KH/sh):
 //   m = (n_img, qh, qw)                       rows   (qh over the blocks that touch the image)

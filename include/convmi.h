@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
     CONVMI_OK = 0,
     CONVMI_ERR_INVALID_ARG = 1, /* bad size, stride, pad, enum value, NULL pointer, aliasing */
-    CONVMI_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    CONVMI_ERR_UNSUPPORTED = 2, /* valid request the library does not implement */
     CONVMI_ERR_WORKSPACE = 3,   /* workspace smaller than convmi_workspace_size() */
     CONVMI_ERR_MISALIGNED = 4,  /* a pointer violates the alignment rule above */
     CONVMI_ERR_HIP = 5          /* a HIP launch or runtime call failed */
@@ -136,7 +136,7 @@ convmi_status convmi_output_dims(const convmi_desc* desc, int64_t* OH, int64_t* 
 /* Bytes of workspace `op` needs for `desc` (0 is possible). */
 convmi_status convmi_workspace_size(const convmi_desc* desc, int32_t op, size_t* bytes);
 
-/* a1 + a2 + a3: convolution + bias, then (batch norm) training statistics and the
+/* Forward: convolution + bias, then (batch norm) training statistics and the
  * normalise/affine step, then the activation.  [generic] forward (conv + bias into
  * pre_activations; batch-norm or layer-norm statistics; normalise + activate); [cuda]
  * forward (conv, add bias, bn_stats_training, bn_forward_affine, activation).
@@ -173,7 +173,7 @@ convmi_status conv2d_forward_noalloc(const convmi_desc* desc, const void* x, con
                                      float* running_var, float* save_mean, float* save_inv_std, void* z, void* y,
                                      void* stream);
 
-/* a5: dx[n,ih,iw,ic] = sum over (oc,kh,kw) with oh*stride_h - pad_h + kh == ih and
+/* Input gradient: dx[n,ih,iw,ic] = sum over (oc,kh,kw) with oh*stride_h - pad_h + kh == ih and
  * ow*stride_w - pad_w + kw == iw of w[oc,kh,kw,ic] * dz[n,oh,ow,oc].  Linear in dz:
  * the activation / batch-norm derivative is applied beforehand by
  * activation_backward.  dx is overwritten.  [generic] backward_input (the scatter
@@ -181,7 +181,7 @@ convmi_status conv2d_forward_noalloc(const convmi_desc* desc, const void* x, con
 convmi_status conv2d_backward_data(const convmi_desc* desc, const void* dz, const void* w, void* dx,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* a6: dw[oc,kh,kw,ic] = sum_{n,oh,ow} dz[n,oh,ow,oc] * x[n, oh*sh-ph+kh, ow*sw-pw+kw, ic]
+/* Weight and bias gradients: dw[oc,kh,kw,ic] = sum_{n,oh,ow} dz[n,oh,ow,oc] * x[n, oh*sh-ph+kh, ow*sw-pw+kw, ic]
  * (zero outside the image); db[oc] = sum_{n,oh,ow} dz[n,oh,ow,oc].  accumulate = 0
  * overwrites dw/db, 1 adds into them (the pages accumulate parameter gradients).
  * db may be NULL.  [generic] backward; [wgsl] conv2d_backward_weight; [cuda]
@@ -190,7 +190,7 @@ convmi_status conv2d_backward_weight(const convmi_desc* desc, const void* x, con
                                      float* db, int32_t accumulate, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
-/* a2: per-channel training statistics of z over the N*OH*OW rows: mean, biased var,
+/* Training statistics: per-channel statistics of z over the N*OH*OW rows: mean, biased var,
  * save_inv_std = 1/sqrt(var+eps); running_mean/var (nullable, both or neither)
  * updated with momentum.  [generic] forward, batch-norm training statistics; [cuda]
  * bn_stats_training.  TRAIN mode only (INVALID_ARG in EVAL mode, where
@@ -201,7 +201,7 @@ convmi_status bn_stats_training(const convmi_desc* desc, const void* z, float* s
                                 float* running_mean, float* running_var,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* a4: activation backward, plus the batch-norm training backward when
+/* Activation backward, plus the batch-norm training backward when
  * desc->normalization is BATCH.
  *   No norm:   dz = act'(z) * dy.
  *   Batch norm: zhat = (z-mean)*inv_std, a = gamma*zhat + beta, dno = act'(a)*dy,
@@ -223,8 +223,9 @@ convmi_status activation_backward(const convmi_desc* desc, const void* z, const 
                                   void* dz, float* dgamma, float* dbeta, int32_t accumulate,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* a4 + a5 + a6 of an unnormalised layer in one call, as the [generic] listing's
- * backward_full (input gradient and parameter gradients from the output gradient):
+/* Activation backward, input gradient and weight/bias gradients of an unnormalised
+ * layer in one call, as the [generic] listing's backward_full (input gradient and
+ * parameter gradients from the output gradient):
  *   dz = act'(.) * dy;  dx = conv^T(dz, w) (overwritten);  dw (+)= sum dz * x;
  *   db (+)= sum dz  -- the results of activation_backward followed by
  * conv2d_backward_data and conv2d_backward_weight, without dz in the caller's memory.

@@ -99,7 +99,7 @@ static double act_slope(int act, double a) {
     }
 }
 
-/* ---------------------------------------------------------------- a1 forward ---- */
+/* ------------------------------------------------------------------- forward ---- */
 /* z[n,oh,ow,oc] = b[oc] + sum_{kh,kw,ic} w[oc,kh,kw,ic] * x[n, oh*sh-ph+kh, ow*sw-pw+kw, ic]
  * with out-of-range taps contributing zero.  [generic] forward, phase 1 (conv + bias
  * into pre_activations). */
@@ -147,7 +147,7 @@ void oracle_conv2d_forward_at(const double* x, const double* w, const double* b,
                             idx[4 * i], idx[4 * i + 1], idx[4 * i + 2], idx[4 * i + 3]);
 }
 
-/* ---------------------------------------------------------------- a2 BN stats ---- */
+/* --------------------------------------------------- batch-norm statistics ---- */
 /* Per channel c over the M = N*OH*OW rows of z [M][C]:
  *   mean = sum z / M;  var = sum (z - mean)^2 / M  (biased);  inv_std = 1/sqrt(var+eps)
  *   running_mean <- (1-momentum)*running_mean + momentum*mean
@@ -187,7 +187,7 @@ void oracle_bn_eval_stats(const double* running_mean, const double* running_var,
     }
 }
 
-/* ------------------------------------------------------- a3 normalise + activate ---- */
+/* ---------------------------------------------------- normalise + activate ---- */
 /* a = z (no norm) or gamma*(z-mean)*inv_std + beta (batch norm); y = act(a).
  * [generic] forward phase 3 and the no-norm branch; [cuda] bn_forward_affine. */
 void oracle_apply_activation(const double* z, i64 M, i64 C, int act, int norm,
@@ -202,7 +202,7 @@ void oracle_apply_activation(const double* z, i64 M, i64 C, int act, int norm,
         }
 }
 
-/* ------------------------------------------------------ a4 activation backward ---- */
+/* ----------------------------------------------------- activation backward ---- */
 /* No norm:  dz = act'(z) * dy.
  * Batch norm, training mode, per channel c over M rows:
  *   zhat = (z - mean) * inv_std,  a = gamma*zhat + beta,  dno = act'(a) * dy,
@@ -394,8 +394,8 @@ void oracle_group_norm_backward(const double* z, const double* dy, i64 N, i64 S,
     }
 }
 
-/* ---------------------------------------------------------------- a5 dX ---- */
-/* Scatter form of the adjoint of a1: for every output (n,oh,ow,oc) and every in-range
+/* ------------------------------------------------------ input gradient dX ---- */
+/* Scatter form of the adjoint of the forward: for every output (n,oh,ow,oc) and every in-range
  * tap (kh,kw), dx[n, oh*sh-ph+kh, ow*sw-pw+kw, ic] += w[oc,kh,kw,ic] * dz[n,oh,ow,oc].
  * dx is overwritten (zeroed first).  [generic] backward_input (the scatter loop after
  * the activation derivative); [cuda] backward_input = BackwardData with beta 0. */
@@ -451,7 +451,7 @@ void oracle_conv2d_backward_data_at(const double* dz, const double* w, const i64
     }
 }
 
-/* ---------------------------------------------------------------- a6 dW, db ---- */
+/* ---------------------------------------------- weight and bias gradients ---- */
 /* dw[oc,kh,kw,ic] = sum_{n,oh,ow} dz[n,oh,ow,oc] * x[n, oh*sh-ph+kh, ow*sw-pw+kw, ic]
  * (out-of-range taps contribute zero);  db[oc] = sum_{n,oh,ow} dz[n,oh,ow,oc].
  * Written, not accumulated.  [generic] backward (weight and bias accumulators);

@@ -58,7 +58,7 @@ def _close(a, b, rtol=1e-12, what=""):
     assert err <= rtol * scale, f"{what}: max abs err {err:.3e} > {rtol:.1e} * {scale:.3e}"
 
 
-# ---------------------------------------------------------------- forward (a1)
+# ---------------------------------------------------------------- forward
 def pin_forward_vs_scipy():
     """Multi-channel cross-correlation = sum over ic of scipy correlate2d on the
     zero-padded plane, subsampled by the stride, plus the bias."""
@@ -148,7 +148,7 @@ def pin_forward_at_matches_full():
         np.testing.assert_array_equal(O.conv2d_forward_at(x, w, b, idx, st, pd), z.reshape(-1))
 
 
-# ---------------------------------------------------------------- dX, dW, db (a5, a6)
+# ---------------------------------------------------------------- dX, dW, db
 def pin_adjoint_identities():
     """<conv(x,w), dy> = <x, dX(dy)> = <w, dW(x,dy)> (bias 0); <1, dy> summed per oc = db."""
     for i, sh_ in enumerate(SMALL_SHAPES):
@@ -239,7 +239,7 @@ def pin_backward_at_matches_full():
         _close(O.bias_grad(dy), db, 1e-12, "bias_grad")
 
 
-# ---------------------------------------------------------------- batch norm (a2, a3)
+# ---------------------------------------------------------------- batch norm
 def pin_bn_stats_vs_numpy():
     r = _rng(10)
     z = r.standard_normal((3, 5, 4, 6)) * r.uniform(0.1, 3, 6) + r.uniform(-2, 2, 6)
@@ -297,7 +297,7 @@ def pin_activation_values():
     _close(O.apply_activation(a, O.ACT_SIGMOID), 0.5 * (1 + np.tanh(a / 2)), 1e-15, "sigmoid")
 
 
-# ---------------------------------------------------------------- activation backward (a4)
+# ---------------------------------------------------------------- activation backward
 def pin_act_backward_no_norm():
     """dz = act'(z)*dy against torch fp64 autograd; tanh' = 1 - tanh^2 identity."""
     r = _rng(12)
