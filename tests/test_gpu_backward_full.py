@@ -191,3 +191,56 @@ def test_backward_full_side_stream_in_graph_and_on_a_caller_stream(s):
         torch.cuda.synchronize()
         assert all(torch.equal(a, b) for a, b in zip(ref, other))
     del g
+
+
+def test_backward_full_two_host_threads_share_the_side_stream():
+    """Two host threads, each on its own stream with its own buffers, call
+    conv2d_backward_full on a layer whose weight gradient runs on the library's second
+    stream (64-channel bf16 stride 1); the shared fork/join events are taken under the
+    library's lock, so every result equals the single-threaded one bit for bit."""
+    import threading
+    import convolution_layer_amd as cm
+    shape, dt, act = WL.ConvShape(2, 10, 32, 64, 64, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH
+    desc = G.shape_desc(shape, dt, act)
+    r = np.random.default_rng(430)
+    x = G.dev(WL.round_to(dt, r.standard_normal(shape.x_shape)), dt)
+    w = G.dev(WL.round_to(dt, r.standard_normal(shape.w_shape) * 0.05), dt)
+    y = G.dev(WL.round_to(dt, np.tanh(r.standard_normal(shape.y_shape))), dt)
+    dy = G.dev(WL.round_to(dt, r.standard_normal(shape.y_shape)), dt)
+
+    def outs():
+        return (torch.empty(shape.x_shape, dtype=torch.bfloat16, device="cuda"),
+                torch.empty(shape.w_shape, dtype=torch.float32, device="cuda"),
+                torch.empty(shape.OC, dtype=torch.float32, device="cuda"))
+
+    ref = outs()
+    cm.conv2d_backward_full(desc, x, w, y, 1, dy, *ref, 0, cm.workspace(desc, cm.OP_BACKWARD_FULL))
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(k):
+        try:
+            torch.cuda.set_device(0)
+            st = torch.cuda.Stream()
+            ws = cm.workspace(desc, cm.OP_BACKWARD_FULL)
+            got = []
+            with torch.cuda.stream(st):
+                for _ in range(12):
+                    o = outs()
+                    cm.conv2d_backward_full(desc, x, w, y, 1, dy, *o, 0, ws, stream=st)
+                    got.append(o)
+            st.synchronize()
+            results[k] = got
+        except Exception as e:  # reported below, on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert sorted(results) == [0, 1]
+    for got in results.values():
+        for o in got:
+            assert all(torch.equal(a, b) for a, b in zip(ref, o))
