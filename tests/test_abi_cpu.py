@@ -213,3 +213,72 @@ def test_noalloc_forward_rejects_layers_beyond_its_scratch(cm):
 def test_noalloc_scratch_limit_matches_header(cm):
     m = re.search(r"#define CONVMI_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
     assert m and int(m.group(1)) << int(m.group(2)) == cm.NOALLOC_SCRATCH_BYTES
+
+
+# Property tests over random descriptors (host logic only: sizes and argument checks).
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+
+@st.composite
+def descriptors(draw):
+    KH, KW = draw(st.integers(1, 9)), draw(st.integers(1, 9))
+    sh, sw = draw(st.integers(1, 5)), draw(st.integers(1, 5))
+    ph, pw = draw(st.integers(0, 4)), draw(st.integers(0, 4))
+    H, W = draw(st.integers(1, 80)), draw(st.integers(1, 80))
+    N = draw(st.integers(1, 16))
+    IC = draw(st.sampled_from([1, 3, 4, 8, 16, 24, 32, 64, 96, 128, 256]))
+    OC = draw(st.sampled_from([1, 8, 16, 30, 32, 64, 72, 128, 256]))
+    norm = draw(st.integers(0, 3))
+    groups = draw(st.sampled_from([g for g in (1, 2, 4, 8) if OC % g == 0])) if norm == 3 else 1
+    return dict(N=N, H=H, W=W, IC=IC, OC=OC, KH=KH, KW=KW, stride=(sh, sw), pad=(ph, pw),
+                activation=draw(st.integers(0, 4)), normalization=norm, dtype=draw(st.integers(0, 1)), groups=groups)
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(descriptors())
+def test_random_descriptors_sizes_and_checks(cm, kw):
+    """Output sizes follow the floor formula and every operation's workspace query
+    succeeds on a valid descriptor; the fused backward's workspace holds dz and the two
+    products' workspaces side by side; an empty output is rejected as INVALID_ARG."""
+    d = _good(cm, **kw)
+    oh_ref = (kw["H"] + 2 * kw["pad"][0] - kw["KH"]) // kw["stride"][0] + 1
+    ow_ref = (kw["W"] + 2 * kw["pad"][1] - kw["KW"]) // kw["stride"][1] + 1
+    oh, ow = C.c_int64(), C.c_int64()
+    status = cm.lib.convmi_output_dims(C.byref(d), C.byref(oh), C.byref(ow))
+    if oh_ref < 1 or ow_ref < 1:
+        assert status == cm.ERR_INVALID_ARG
+        return
+    assert status == cm.OK, cm.lib.convmi_last_error()
+    assert (oh.value, ow.value) == (oh_ref, ow_ref)
+    sizes = [cm.workspace_size(d, op) for op in range(6)]
+    assert all(n >= 0 for n in sizes)
+    full = sizes[cm.OP_BACKWARD_FULL]
+    if kw["normalization"] == 0:
+        assert full >= sizes[cm.OP_BACKWARD_DATA] + sizes[cm.OP_BACKWARD_WEIGHT]
+    if kw["normalization"] != 0:
+        assert sizes[cm.OP_BN_STATS] > 0 and sizes[cm.OP_ACTIVATION_BACKWARD] > 0
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(descriptors(), st.sampled_from(["stride0", "pad_neg", "groups", "eps", "kernel_big"]))
+def test_random_invalid_descriptors_are_rejected(cm, kw, fault):
+    """One planted fault in an otherwise valid descriptor gives INVALID_ARG from every
+    host check, before any device work."""
+    if fault == "stride0":
+        kw["stride"] = (0, kw["stride"][1])
+    elif fault == "pad_neg":
+        kw["pad"] = (kw["pad"][0], -1)
+    elif fault == "groups":
+        kw["normalization"], kw["groups"] = 3, kw["OC"] + 1
+    elif fault == "eps":
+        kw["normalization"] = max(kw["normalization"], 1)
+    else:
+        kw["KH"], kw["pad"] = kw["H"] + 1, (0, kw["pad"][1])
+    d = _good(cm, **kw)
+    if fault == "eps":
+        d.eps = 0.0
+    oh, ow = C.c_int64(), C.c_int64()
+    assert cm.lib.convmi_output_dims(C.byref(d), C.byref(oh), C.byref(ow)) == cm.ERR_INVALID_ARG
+    n = C.c_size_t()
+    for op in range(6):
+        assert cm.lib.convmi_workspace_size(C.byref(d), op, C.byref(n)) == cm.ERR_INVALID_ARG
