@@ -19,14 +19,14 @@
 // Definitions: rl_tools conv2d listings "operations_generic.h" (forward, backward_input)
 // and "operations_cuda.h" (forward with bias and activation; backward_input).
 //
-// Pipeline: steps (chunk c, tap t), c outer.  Weight tiles (BN rows x 128 bytes) go
-// through a two-slot LDS ring, one step ahead.  With two halo buffers the halo of chunk
-// c + 1 is copied during chunk c; with one it is copied after the last tap of chunk c and
-// a second workgroup on the CU covers the gap.  All copies are 16-byte LDS-DMA with
-// XOR-swizzled 16-byte chunks; each wave counts the copies it has issued and waits for
-// exactly the ones the next step reads.  The epilogue stages the tile in LDS in the
-// storage type (the activation reads the stored pre-activation, so staging the rounded
-// value loses nothing) and writes 16-byte vectors.
+// Pipeline: steps (chunk c, tap t), c outer.  The weights are laid out in MFMA fragment
+// order beforehand and each wave streams its own fragments into registers one step ahead;
+// LDS holds only the input halo.  With two halo buffers the halo of chunk c + 1 is copied
+// during chunk c; with one it is copied after the last tap of chunk c and a second
+// workgroup on the CU covers the gap.  Halo copies are 16-byte LDS-DMA with XOR-swizzled
+// 16-byte chunks.  The epilogue stages the tile in LDS in the storage type (the
+// activation reads the stored pre-activation, so staging the rounded value loses nothing)
+// and writes 16-byte vectors.
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
@@ -371,22 +371,30 @@ __device__ __forceinline__ void epilogue_store(const T* Cs, const Out& out, cons
     }
 }
 
-// Two workgroups per CU must fit the register file: at most 256 registers per lane.
-template <typename T, int MF, int BM, int BN, int WM, int WN, int ACT, class Out>
-__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_kernel(
-    const T* __restrict__ A, HaloGeom g, const T* __restrict__ B, Out out, int tiles_n) {
+// The tile kernel, bf16 or fp32, without a per-step barrier.  The weights are first laid
+// out in MFMA fragment order (frag_weights below): the B fragment that a wave needs for
+// one MFMA k-step (32 or 16 rows x 32 bytes of k) is 1 KB contiguous, so every weight
+// load instruction reads whole cache lines.  Each wave loads its own B fragments straight into registers one step
+// ahead; LDS holds only the input halo, whose next chunk is copied during the current one
+// (two buffers) or after it (one buffer).  Waves therefore only meet at chunk
+// boundaries, where each waits for all of its outstanding vector-memory operations:
+// LDS-DMA copies and register loads need not complete in issue order with respect to
+// each other, so a count that mixes the two kinds proves nothing.
+template <typename T, int BM, int BN, int WM, int WN, int ACT, class Out, int MF>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_rb_kernel(
+    const T* __restrict__ A, HaloGeom g, const uint4* __restrict__ Bf, Out out, int tiles_n) {
     using MM = HMma<T, MF>;
     using Acc = typename MM::Acc;
-    constexpr int NWAVE = WM * WN, NTH = kThreadsH;
-    static_assert(NWAVE * 64 == NTH, "four waves");
-    constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-    constexpr int CK = 8 * VEC;               // channels per 128-byte chunk
-    constexpr int LG = 64 / MF;               // lane groups (16-byte k chunks per MFMA)
-    constexpr int KST = 8 / LG;               // MFMA k-steps per 128-byte chunk
+    constexpr int NWAVE = 4, NTH = kThreadsH;
+    static_assert(WM * WN == NWAVE, "four waves");
     constexpr int TM = BM / (WM * MF), TN = BN / (WN * MF);
     static_assert(TM * WM * MF == BM && TN * WN * MF == BN, "tile shape");
-    static_assert(BN % 8 == 0, "8-row copy groups");
-    constexpr int GB = BN / 8;  // 1-KB weight copies per step
+    // 16-byte chunk = 8 bf16 or 4 fp32; a 128-byte chunk (64 bf16 or 32 fp32 channels) is 4
+    // k-steps of 32 bytes (32x32x16: lane groups of 32 take 2 chunks per k-step) or 2 of 64
+    // bytes (16x16x32 bf16, 4 x 16x16x4 fp32: lane groups of 16 take 4 chunks)
+    static_assert(sizeof(T) == 2 || MF == 16, "fp32 tiles use 16-row fragments");
+    constexpr int VEC = 16 / (int)sizeof(T), CK = 128 / (int)sizeof(T), KST = MF == 32 ? 4 : 2,
+                  LGS = MF == 32 ? 5 : 4;
     extern __shared__ __align__(1024) unsigned char smem[];
 
     const int t = threadIdx.x, lane = t & 63;
@@ -394,9 +402,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     const int halo_bytes = g.GH * 1024;
     const bool two = g.hb == 2;
     const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-    const uint32_t w_base = smem_base + g.hb * halo_bytes;
 
-    // tile -> (image, tile row, tile column, column tile); consecutive tiles share an XCD
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     const int tn = tile % tiles_n;
     const int sp = tile / tiles_n;
@@ -407,237 +413,6 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
     const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
     const T* Aimg = A + (int64_t)n * g.img_stride;
-    ParStage<Out, BN, NTH> pst;  // stored to LDS after the main loop
-    pst.load(out, n0, t);
-    const int nsteps = g.nchunks * g.KH * g.KW;
-
-    // Copy group grp covers 8 LDS rows (halo positions or weight rows) 8*grp .. 8*grp+7;
-    // lane l copies 16-byte chunk l%8 of row 8*grp + l/8.  Each returns this wave's copies.
-    const int rg = lane >> 3, pc = lane & 7;
-    auto issue_halo = [&](int c) -> int {
-        const uint32_t dstb = smem_base + (uint32_t)((two ? (c & 1) : 0) * halo_bytes);
-        int cnt = 0;
-        for (int grp = wid; grp < g.GH; grp += NWAVE, ++cnt) {
-            const int p = grp * 8 + rg;
-            const void* src = &kZero16;
-            if (p < g.HP) {
-                const int hr = fdiv(p, g.fHQ);
-                const int ih = hr0 + hr, iw = hc0 + (p - hr * g.HQ);
-                if ((unsigned)ih < (unsigned)g.Hin && (unsigned)iw < (unsigned)g.Win)
-                    src = Aimg + ((int64_t)ih * g.Win + iw) * g.Cin + c * CK + (pc ^ swz(p)) * VEC;
-            }
-            dma16(src, __builtin_amdgcn_readfirstlane(dstb + grp * 1024));
-        }
-        return cnt;
-    };
-    // weight tiles are issued strictly in step order; (wc, wkh, wkw) is the next one
-    int wst = 0, wc = 0, wtap = 0;
-    const int taps = g.KH * g.KW;
-    auto issue_w = [&]() -> int {
-        const int kofs = wtap * g.Cin + wc * CK;
-        const uint32_t dstb = w_base + (uint32_t)((wst & 1) * BN * 128);
-        int cnt = 0;
-        for (int grp = wid; grp < GB; grp += NWAVE, ++cnt) {
-            const int r = grp * 8 + rg;
-            const int nr = n0 + r;
-            const void* src = nr < g.Nn ? (const void*)(B + (int64_t)nr * g.Kb + kofs + (pc ^ swz(r)) * VEC)
-                                        : (const void*)&kZero16;
-            dma16(src, __builtin_amdgcn_readfirstlane(dstb + grp * 1024));
-        }
-        ++wst;
-        if (++wtap == taps) {
-            wtap = 0;
-            ++wc;
-        }
-        return cnt;
-    };
-
-    // LDS fragment sources of this lane: A rows are output pixels m = rr*Q + qq of the
-    // tile (halo position rr*HQ + qq before the tap shift), B rows are output channels.
-    const int wm = wid / WN, wn = wid % WN;
-    const int lr = lane % MF, lg = lane / MF;
-    int hpos[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        int m = wm * TM * MF + i * MF + lr;
-        if (m >= g.R * g.Q) m = 0;  // rows past the tile read a valid position; never stored
-        const int rr = fdiv(m, g.fQ);
-        hpos[i] = rr * g.HQ + (m - rr * g.Q);
-    }
-    int boff[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int r = wn * TN * MF + j * MF + lr;
-        boff[j] = r * 128 + (swz(r) << 4);  // xor-able: swz(r) << 4 < 128
-    }
-
-    Acc acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < MM::NE; ++e) acc[i][j][e] = 0.0f;
-
-    // Fragment reads are software-pipelined: the reads of k-step kk + 1 are issued before
-    // the MFMAs of kk, and the reads of the next step's first k-step before the MFMAs of
-    // the current step's last one.  The barrier that hands over a weight slot sits just
-    // before those last MFMAs, so its wait overlaps MFMAs already in flight.
-    uint4 fa[2][TM], fb[2][TN];
-    auto tap_off = [&](int kh_, int kw_) {
-        return g.sign > 0 ? kh_ * g.HQ + kw_ : (g.KH - 1 - kh_) * g.HQ + (g.KW - 1 - kw_);
-    };
-    auto read_frags = [&](const unsigned char* Hs, const unsigned char* Ws, int toff, int lc, uint4 (&a)[TM],
-                          uint4 (&b)[TN]) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int p = hpos[i] + toff;
-            a[i] = *(const uint4*)(Hs + p * 128 + ((lc ^ swz(p)) << 4));
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = *(const uint4*)(Ws + (boff[j] ^ (lc << 4)));
-    };
-    auto mfmas = [&](const uint4 (&a)[TM], const uint4 (&b)[TN]) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) MM::run(acc[i][j], a[i], b[j]);
-    };
-    auto halo_at = [&](int c_) { return smem + (two ? (c_ & 1) : 0) * halo_bytes; };
-    auto slot_at = [&](int st_) { return smem + g.hb * halo_bytes + (st_ & 1) * BN * 128; };
-
-    // Wave-local copy accounting: `issued` copies so far; e1 the count right after the
-    // next step's weight tile, eh_next right after the next chunk's halo.
-    int issued = issue_halo(0);
-    int eh_next = issued;
-    issued += issue_w();
-    const int e0 = issued;
-    int e1 = issued;
-    if (nsteps > 1) {
-        issued += issue_w();
-        e1 = issued;
-    }
-    if (two && g.nchunks > 1) {
-        issued += issue_halo(1);
-        eh_next = issued;
-    }
-    wait_dma(issued - e0);
-    __syncthreads();
-    read_frags(halo_at(0), slot_at(0), tap_off(0, 0), lg, fa[0], fb[0]);
-
-    int c = 0, kh = 0, kw = 0;
-    for (int st = 0; st < nsteps; ++st) {
-        const unsigned char* Hs = halo_at(c);
-        const unsigned char* Ws = slot_at(st);
-        const int toff = tap_off(kh, kw);
-#pragma unroll
-        for (int kk = 0; kk + 1 < KST; ++kk) {
-            read_frags(Hs, Ws, toff, (kk + 1) * LG + lg, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(fa[kk & 1], fb[kk & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // next step (c, kh, kw) -> (c2, kh2, kw2)
-        int c2 = c, kh2 = kh, kw2 = kw + 1;
-        if (kw2 == g.KW) {
-            kw2 = 0;
-            if (++kh2 == g.KH) {
-                kh2 = 0;
-                ++c2;
-            }
-        }
-        if (st + 1 < nsteps) {
-            const bool boundary = c2 != c;
-            if (boundary && !two) {
-                // one halo buffer: every wave is done with chunk c's halo, reload it in place
-                wait_dma(issued - e1);
-                __syncthreads();
-                if (st + 2 < nsteps) issued += issue_w();
-                issued += issue_halo(c2);
-                wait_dma(0);
-                __syncthreads();
-                e1 = issued;
-            } else {
-                const int need = boundary && eh_next > e1 ? eh_next : e1;
-                wait_dma(issued - need);
-                __syncthreads();  // weight slot st and, at a boundary, halo c are free again
-                if (st + 2 < nsteps) issued += issue_w();
-                e1 = issued;
-                if (boundary && two && c2 + 1 < g.nchunks) {
-                    issued += issue_halo(c2 + 1);
-                    eh_next = issued;
-                }
-            }
-            read_frags(halo_at(c2), slot_at(st + 1), tap_off(kh2, kw2), lg, fa[KST & 1], fb[KST & 1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(fa[(KST - 1) & 1], fb[(KST - 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        c = c2;
-        kh = kh2;
-        kw = kw2;
-    }
-    float* par = (float*)(smem + g.par_off);
-    pst.store(par, t);
-    __syncthreads();
-
-    // epilogue: stored values -> LDS (rows of BN + 16 bytes) -> 16-byte vectors
-    constexpr int LDC = BN + VEC;
-    T* Cs = (T*)smem;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int cl = wn * TN * MF + j * MF + lr;
-        const float bj = out.colbias(par, cl);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int e = 0; e < MM::NE; ++e)
-                Cs[(wm * TM * MF + i * MF + MM::row(lg, e)) * LDC + cl] = from_f32<T>(acc[i][j][e] + bj);
-    }
-    __syncthreads();
-    epilogue_store<T, ACT, BM, BN, NTH>(Cs, out, par, g, n, r0, c0, n0, sp);
-}
-
-// bf16 variant without a per-step barrier.  The weights are first laid out in MFMA
-// fragment order (frag_weights below): the B fragment of 32 rows x 16 k that a wave needs
-// for one MFMA k-step is 1 KB contiguous, so every weight load instruction reads whole
-// cache lines.  Each wave loads its own B fragments straight into registers one step
-// ahead; LDS holds only the input halo, whose next chunk is copied during the current one
-// (two buffers) or after it (one buffer).  Waves therefore only meet at chunk
-// boundaries, where each waits for all of its outstanding vector-memory operations:
-// LDS-DMA copies and register loads need not complete in issue order with respect to
-// each other, so a count that mixes the two kinds proves nothing.
-template <int BM, int BN, int WM, int WN, int ACT, class Out, int MF>
-__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_rb_kernel(
-    const bf16* __restrict__ A, HaloGeom g, const uint4* __restrict__ Bf, Out out, int tiles_n) {
-    using MM = HMma<bf16, MF>;
-    using Acc = typename MM::Acc;
-    constexpr int NWAVE = 4, NTH = kThreadsH;
-    static_assert(WM * WN == NWAVE, "four waves");
-    constexpr int TM = BM / (WM * MF), TN = BN / (WN * MF);
-    static_assert(TM * WM * MF == BM && TN * WN * MF == BN, "tile shape");
-    // 16-byte chunk = 8 bf16; a 128-byte chunk (64 channels) is 4 k-steps of 16 channels
-    // (32x32x16: lane groups of 32 take 2 chunks per k-step) or 2 k-steps of 32 (16x16x32:
-    // lane groups of 16 take 4 chunks)
-    constexpr int VEC = 8, CK = 64, KST = MF == 32 ? 4 : 2, LGS = MF == 32 ? 5 : 4;
-    extern __shared__ __align__(1024) unsigned char smem[];
-
-    const int t = threadIdx.x, lane = t & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int halo_bytes = g.GH * 1024;
-    const bool two = g.hb == 2;
-    const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int tn = tile % tiles_n;
-    const int sp = tile / tiles_n;
-    const int qsp = fdiv(sp, g.fTC);
-    const int tc = sp - qsp * g.tiles_c;
-    const int n = fdiv(qsp, g.fTR);
-    const int tr = qsp - n * g.tiles_r;
-    const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
-    const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
-    const bf16* Aimg = A + (int64_t)n * g.img_stride;
     ParStage<Out, BN, NTH> pst;  // stored to LDS after the main loop
     pst.load(out, n0, t);
     const int taps = g.KH * g.KW;
@@ -771,7 +546,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     // accumulators hold the transposed tile (MFMA rows are channels, columns pixels), so
     // a lane owns 4 consecutive channels of one pixel per row group: one 8-byte write.
     constexpr int LDC = BN + VEC;
-    bf16* Cs = (bf16*)smem;
+    T* Cs = (T*)smem;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -783,14 +558,17 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int m = wm * TM * MF + i * MF + lr;
-                const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * g4] + bj[0], acc[i][j][4 * g4 + 1] + bj[1]),
-                                           pack_bf16x2(acc[i][j][4 * g4 + 2] + bj[2], acc[i][j][4 * g4 + 3] + bj[3]));
-                *(uint2*)(Cs + m * LDC + cl) = v;
+                const float v0 = acc[i][j][4 * g4] + bj[0], v1 = acc[i][j][4 * g4 + 1] + bj[1];
+                const float v2 = acc[i][j][4 * g4 + 2] + bj[2], v3 = acc[i][j][4 * g4 + 3] + bj[3];
+                if constexpr (sizeof(T) == 2)
+                    *(uint2*)(Cs + m * LDC + cl) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+                else
+                    *(float4*)(Cs + m * LDC + cl) = make_float4(v0, v1, v2, v3);
             }
         }
     }
     __syncthreads();
-    epilogue_store<bf16, ACT, BM, BN, NTH>(Cs, out, par, g, n, r0, c0, n0, sp);
+    epilogue_store<T, ACT, BM, BN, NTH>(Cs, out, par, g, n, r0, c0, n0, sp);
 }
 
 // Weights in B-fragment order for halo_rb_kernel with fragments of mf = 32 or 16 rows.
@@ -800,8 +578,10 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 // (lane/16)*8 (mf 16) at tap.  Forward rows are output channels:
 // w[row, tap, ch]; input-gradient rows are input channels: w[ch, tap, row].  Rows past
 // the matrix are zero.
-__global__ __launch_bounds__(256) void frag_weights(const bf16* __restrict__ w, uint4* __restrict__ dst, int Nn,
+template <typename T>
+__global__ __launch_bounds__(256) void frag_weights(const T* __restrict__ w, uint4* __restrict__ dst, int Nn,
                                                     int taps, int Cin, int nsteps, int groups, int fwd, int mf) {
+    constexpr int EV = 16 / (int)sizeof(T), CK = 128 / (int)sizeof(T);  // per 16 bytes, per 128-byte chunk
     const int kst = mf == 32 ? 4 : 2;
     const int64_t total = (int64_t)groups * nsteps * kst * 64;
     for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
@@ -813,15 +593,15 @@ __global__ __launch_bounds__(256) void frag_weights(const bf16* __restrict__ w, 
         const int grp = (int)(q2 / nsteps);
         const int row = grp * mf + (l % mf);
         const int chunk = st / taps, tap = st - chunk * taps;
-        const int ch0 = chunk * 64 + kk * (64 / kst) + (l / mf) * 8;
+        const int ch0 = chunk * CK + kk * (CK / kst) + (l / mf) * EV;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (row < Nn) {
             if (fwd) {
                 v = *(const uint4*)(w + ((int64_t)row * taps + tap) * Cin + ch0);
             } else {
-                bf16 e[8];
+                T e[EV];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) e[k] = w[((int64_t)(ch0 + k) * taps + tap) * Nn + row];
+                for (int k = 0; k < EV; ++k) e[k] = w[((int64_t)(ch0 + k) * taps + tap) * Nn + row];
                 __builtin_memcpy(&v, e, 16);
             }
         }
@@ -837,16 +617,15 @@ struct HaloPlan {
     int bm, bn, hb;
     int R, Q;
     int lds;     // dynamic LDS bytes per workgroup
-    int mf = 32; // bf16 MFMA fragment height: 32 (32x32x16) or 16 (16x16x32, 224-row blocks)
+    int mf = 32; // MFMA fragment height: bf16 32 (32x32x16) or 16 (16x16x32, 224-row blocks); fp32 16
 };
 
 int halo_groups(int R, int Q, int KH, int KW) { return ((R + KH - 1) * (Q + KW - 1) + 7) / 8; }
 
-// bf16 tiles keep only the halo in LDS (weights go to registers); fp32 tiles also hold a
-// two-slot weight ring.  The epilogue reuses the same bytes.
-// Bytes before the per-column parameters: the halo (and weight) ring, reused by the epilogue.
+// Bytes before the per-column parameters: the halo buffers (the weights stream through
+// registers), reused by the epilogue's staged tile.
 int plan_main(int bm, int bn, int hb, int gh, int esize) {
-    const int ring = hb * gh * 1024 + (esize == 2 ? 0 : 2 * bn * 128);
+    const int ring = hb * gh * 1024;
     const int epi = bm * (bn + 16 / esize) * esize;
     return (int)align_up((size_t)(ring > epi ? ring : epi), 16);
 }
@@ -922,8 +701,11 @@ bool pick_halo(int dt, const ConvDims& d, const Sides& sd, HaloPlan* best) {
         if (!found) try_bm(128, 32);
         return found;
     }
-    static const int bms_b64[] = {256, 512, 128, 0}, bms_f32[] = {256, 224, 0};
-    for (const int* bms = dt == DT_BF16 ? bms_b64 : bms_f32; *bms && !found; ++bms) try_bm(*bms, 32);
+    // fp32 with 128 output channels: 224-row blocks first (256 rows of 16x16x4 fragments
+    // exceed the register budget of two workgroups per CU)
+    static const int bms_b64[] = {256, 512, 128, 0}, bms_f32[] = {256, 224, 0}, bms_f32w[] = {224, 256, 0};
+    const int* bms0 = dt == DT_BF16 ? bms_b64 : (bn == 128 ? bms_f32w : bms_f32);
+    for (const int* bms = bms0; *bms && !found; ++bms) try_bm(*bms, dt == DT_BF16 ? 32 : 16);
     return found;
 }
 
@@ -966,23 +748,10 @@ template <class K> hipError_t raise_lds(K kern, bool& raised) {
     return e;
 }
 
-template <int MF, int BM, int BN, int WM, int WN, int ACT, class Out>
-hipError_t launch_f32(const float* A, const HaloGeom& g, const float* B, const Out& out, int images, int lds,
-                      hipStream_t s) {
-    auto kern = halo_kernel<float, MF, BM, BN, WM, WN, ACT, Out>;
-    static bool raised = false;
-    const hipError_t e = raise_lds(kern, raised);
-    if (e != hipSuccess) return e;
-    const int tiles_n = (int)ceil_div(g.Nn, BN);
-    const int64_t grid = (int64_t)images * g.tiles_r * g.tiles_c * tiles_n;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreadsH), lds, s, A, g, B, out, tiles_n);
-    return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN, int ACT, class Out, int MF>
-hipError_t launch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, const Out& out, int images, int lds,
-                       hipStream_t s) {
-    auto kern = halo_rb_kernel<BM, BN, WM, WN, ACT, Out, MF>;
+template <typename T, int BM, int BN, int WM, int WN, int ACT, class Out, int MF>
+hipError_t launch_rb(const T* A, const HaloGeom& g, const uint4* Bf, const Out& out, int images, int lds,
+                     hipStream_t s) {
+    auto kern = halo_rb_kernel<T, BM, BN, WM, WN, ACT, Out, MF>;
     static bool raised = false;
     const hipError_t e = raise_lds(kern, raised);
     if (e != hipSuccess) return e;
@@ -993,10 +762,11 @@ hipError_t launch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, const 
 }
 
 template <int ACT, class Out>
-hipError_t dispatch_f32(const float* A, const HaloGeom& g, const float* B, const Out& out, const HaloPlan& p,
+hipError_t dispatch_f32(const float* A, const HaloGeom& g, const uint4* Bf, const Out& out, const HaloPlan& p,
                         int images, hipStream_t s) {
-#define CONVMI_HP(BM_, BN_)                                                                                 \
-    if (p.bm == BM_ && p.bn == BN_) return launch_f32<16, BM_, BN_, 2, 2, ACT, Out>(A, g, B, out, images, p.lds, s);
+#define CONVMI_HP(BM_, BN_)                                                                                      \
+    if (p.bm == BM_ && p.bn == BN_ && p.mf == 16)                                                              \
+        return launch_rb<float, BM_, BN_, 2, 2, ACT, Out, 16>(A, g, Bf, out, images, p.lds, s);
     CONVMI_HP(224, 128) CONVMI_HP(224, 64) CONVMI_HP(256, 128) CONVMI_HP(256, 64)
 #undef CONVMI_HP
     return hipErrorInvalidValue;
@@ -1010,7 +780,7 @@ hipError_t dispatch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, cons
                          int images, hipStream_t s) {
 #define CONVMI_RB(BM_, BN_, WM_, WN_, MF_)                                                                  \
     if (p.bm == BM_ && p.bn == BN_ && p.mf == MF_)                                                            \
-        return launch_bf16<BM_, BN_, WM_, WN_, ACT, Out, MF_>(A, g, Bf, out, images, p.lds, s);
+        return launch_rb<bf16, BM_, BN_, WM_, WN_, ACT, Out, MF_>(A, g, Bf, out, images, p.lds, s);
     CONVMI_RB(256, 128, 2, 2, 32) CONVMI_RB(224, 128, 2, 2, 16) CONVMI_RB(128, 128, 2, 2, 32)
     CONVMI_RB(512, 64, 4, 1, 32) CONVMI_RB(256, 64, 4, 1, 32) CONVMI_RB(128, 64, 4, 1, 32)
 #undef CONVMI_RB
@@ -1020,20 +790,24 @@ hipError_t dispatch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, cons
 Sides fwd_sides(const ConvDims& d) { return Sides{d.OH, d.OW, d.IC, d.OC, HFwdBnOut::kPar}; }
 Sides dx_sides(const ConvDims& d) { return Sides{d.H, d.W, d.OC, d.IC, HDxOut::kPar}; }
 
-// Fragment-ordered weights: 32-row groups covering every column tile, KH*KW*Cin k each.
-size_t frag_bytes(const ConvDims& d, const Sides& sd, const HaloPlan& p) {
-    const int64_t groups = ceil_div(sd.Nn, p.bn) * (p.bn / 32);
-    return align_up((size_t)groups * 32 * d.KH * d.KW * sd.Cin * 2, 256);
+// Fragment-ordered weights: every column tile's rows, KH*KW*Cin k each, in the element type.
+size_t frag_bytes(const ConvDims& d, const Sides& sd, const HaloPlan& p, int es) {
+    return align_up((size_t)ceil_div(sd.Nn, p.bn) * p.bn * d.KH * d.KW * sd.Cin * es, 256);
 }
 
-hipError_t launch_frag_weights(const bf16* w, uint4* dst, const ConvDims& d, const Sides& sd, const HaloPlan& p,
-                               bool fwd, hipStream_t s) {
+hipError_t launch_frag_weights(int dt, const void* w, uint4* dst, const ConvDims& d, const Sides& sd,
+                               const HaloPlan& p, bool fwd, hipStream_t s) {
     const int taps = d.KH * d.KW;
-    const int nsteps = (sd.Cin / 64) * taps;
+    const int nsteps = (sd.Cin * (int)dtype_size(dt) / 128) * taps;
     const int groups = (int)(ceil_div(sd.Nn, p.bn) * (p.bn / p.mf));
     const int64_t units = (int64_t)groups * nsteps * (p.mf == 32 ? 4 : 2) * 64;
     const int grid = (int)(ceil_div(units, 256) < 2048 ? ceil_div(units, 256) : 2048);
-    frag_weights<<<grid, 256, 0, s>>>(w, dst, sd.Nn, taps, sd.Cin, nsteps, groups, fwd ? 1 : 0, p.mf);
+    if (dt == DT_BF16)
+        frag_weights<bf16><<<grid, 256, 0, s>>>((const bf16*)w, dst, sd.Nn, taps, sd.Cin, nsteps, groups, fwd ? 1 : 0,
+                                                 p.mf);
+    else
+        frag_weights<float><<<grid, 256, 0, s>>>((const float*)w, dst, sd.Nn, taps, sd.Cin, nsteps, groups,
+                                                  fwd ? 1 : 0, p.mf);
     return hipGetLastError();
 }
 
@@ -1051,14 +825,14 @@ bool halo_dx_supported(int dt, const ConvDims& d) {
 
 size_t halo_fwd_ws_bytes(int dt, const ConvDims& d) {
     HaloPlan p;
-    if (dt != DT_BF16 || !halo_fwd_supported(dt, d) || !pick_halo(dt, d, fwd_sides(d), &p)) return 0;
-    return frag_bytes(d, fwd_sides(d), p);
+    if (!halo_fwd_supported(dt, d) || !pick_halo(dt, d, fwd_sides(d), &p)) return 0;
+    return frag_bytes(d, fwd_sides(d), p, (int)dtype_size(dt));
 }
 
 size_t halo_dx_ws_bytes(int dt, const ConvDims& d) {
     HaloPlan p;
-    if (dt != DT_BF16 || !halo_dx_supported(dt, d) || !pick_halo(dt, d, dx_sides(d), &p)) return 0;
-    return frag_bytes(d, dx_sides(d), p);
+    if (!halo_dx_supported(dt, d) || !pick_halo(dt, d, dx_sides(d), &p)) return 0;
+    return frag_bytes(d, dx_sides(d), p, (int)dtype_size(dt));
 }
 
 int halo_fwd_stat_tiles(int dt, const ConvDims& d) {
@@ -1079,31 +853,27 @@ hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bi
         if (bn_eval || !z) return hipErrorInvalidValue;
         const int ntiles = d.N * g.tiles_r * g.tiles_c;
         const HFwdStatsOut os{z, bias, d.OC, stats_part, ntiles};
-        if (dt == DT_BF16) {
-            const hipError_t e = launch_frag_weights((const bf16*)w, (uint4*)ws, d, sd, p, true, s);
-            if (e != hipSuccess) return e;
+        const hipError_t e = launch_frag_weights(dt, w, (uint4*)ws, d, sd, p, true, s);
+        if (e != hipSuccess) return e;
+        if (dt == DT_BF16)
             return dispatch_bf16<ACT_IDENTITY, HFwdStatsOut>((const bf16*)x, g, (const uint4*)ws, os, p, d.N, s);
-        }
-        return dispatch_f32<ACT_IDENTITY, HFwdStatsOut>((const float*)x, g, (const float*)w, os, p, d.N, s);
+        return dispatch_f32<ACT_IDENTITY, HFwdStatsOut>((const float*)x, g, (const uint4*)ws, os, p, d.N, s);
     }
     const HFwdOut o{z, y, bias, d.OC};
     const HFwdBnOut ob{z, y, bias, d.OC, bn_eval ? bn_eval[0] : nullptr, bn_eval ? bn_eval[1] : nullptr,
                        bn_eval ? bn_eval[2] : nullptr, bn_eval ? bn_eval[3] : nullptr};
     if (bn_eval && (!y || !bn_eval[0] || !bn_eval[1] || !bn_eval[2] || !bn_eval[3])) return hipErrorInvalidValue;
+    const hipError_t e = launch_frag_weights(dt, w, (uint4*)ws, d, sd, p, true, s);
+    if (e != hipSuccess) return e;
+    const uint4* wf = (const uint4*)ws;
     if (dt == DT_BF16) {
-        const hipError_t e = launch_frag_weights((const bf16*)w, (uint4*)ws, d, sd, p, true, s);
-        if (e != hipSuccess) return e;
         if (bn_eval)
-            CONVMI_ACT_SWITCH(act, A_, return (dispatch_bf16<A_, HFwdBnOut>((const bf16*)x, g, (const uint4*)ws, ob,
-                                                                            p, d.N, s)));
-        CONVMI_ACT_SWITCH(act, A_, return (dispatch_bf16<A_, HFwdOut>((const bf16*)x, g, (const uint4*)ws, o, p,
-                                                                      d.N, s)));
+            CONVMI_ACT_SWITCH(act, A_, return (dispatch_bf16<A_, HFwdBnOut>((const bf16*)x, g, wf, ob, p, d.N, s)));
+        CONVMI_ACT_SWITCH(act, A_, return (dispatch_bf16<A_, HFwdOut>((const bf16*)x, g, wf, o, p, d.N, s)));
     } else {
         if (bn_eval)
-            CONVMI_ACT_SWITCH(act, A_, return (dispatch_f32<A_, HFwdBnOut>((const float*)x, g, (const float*)w, ob,
-                                                                           p, d.N, s)));
-        CONVMI_ACT_SWITCH(act, A_, return (dispatch_f32<A_, HFwdOut>((const float*)x, g, (const float*)w, o, p,
-                                                                     d.N, s)));
+            CONVMI_ACT_SWITCH(act, A_, return (dispatch_f32<A_, HFwdBnOut>((const float*)x, g, wf, ob, p, d.N, s)));
+        CONVMI_ACT_SWITCH(act, A_, return (dispatch_f32<A_, HFwdOut>((const float*)x, g, wf, o, p, d.N, s)));
     }
     return hipErrorInvalidValue;
 }
@@ -1115,12 +885,10 @@ hipError_t launch_halo_dx(int dt, const void* dz, const void* w, void* dx, const
     if (d.sh != 1 || d.sw != 1 || !pick_halo(dt, d, sd, &p)) return hipErrorInvalidValue;
     const HaloGeom g = make_geom(d, sd, p, dt, false);
     const HDxOut o{dx, d.IC};
-    if (dt == DT_BF16) {
-        const hipError_t e = launch_frag_weights((const bf16*)w, (uint4*)ws, d, sd, p, false, s);
-        if (e != hipSuccess) return e;
-        return dispatch_bf16<ACT_IDENTITY, HDxOut>((const bf16*)dz, g, (const uint4*)ws, o, p, d.N, s);
-    }
-    return dispatch_f32<ACT_IDENTITY, HDxOut>((const float*)dz, g, (const float*)w, o, p, d.N, s);
+    const hipError_t e = launch_frag_weights(dt, w, (uint4*)ws, d, sd, p, false, s);
+    if (e != hipSuccess) return e;
+    if (dt == DT_BF16) return dispatch_bf16<ACT_IDENTITY, HDxOut>((const bf16*)dz, g, (const uint4*)ws, o, p, d.N, s);
+    return dispatch_f32<ACT_IDENTITY, HDxOut>((const float*)dz, g, (const uint4*)ws, o, p, d.N, s);
 }
 
 }  // namespace convmi

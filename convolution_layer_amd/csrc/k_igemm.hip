@@ -627,8 +627,8 @@ hipError_t launch_igemm_fwd(int dt, const void* x, const void* w, const float* b
 
 hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, const ConvDims& d, void* ws,
                            hipStream_t s) {
-    // bf16 stride-1: the tile-reuse kernel reads the weights in its own fragment order
-    if (dt == DT_BF16 && halo_dx_supported(dt, d)) return launch_halo_dx(dt, dz, w, dx, d, ws, s);
+    // stride 1: the tile-reuse kernel reads the weights in its own fragment order
+    if (halo_dx_supported(dt, d)) return launch_halo_dx(dt, dz, w, dx, d, ws, s);
     const int KHs = dx_khs(d), KWs = dx_kws(d);
     const int Ncol = d.sh * d.sw * d.IC, Kb = KHs * KWs * d.OC;
     // rearranged weights into the workspace
@@ -642,7 +642,6 @@ hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, cons
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (halo_dx_supported(dt, d)) return launch_halo_dx(dt, dz, ws, dx, d, nullptr, s);
     // rows: phase blocks (qh, qw) that touch the image
     const int qh0 = d.ph / d.sh, qh1 = (d.H - 1 + d.ph) / d.sh;
     const int qw0 = d.pw / d.sw, qw1 = (d.W - 1 + d.pw) / d.sw;
