@@ -32,7 +32,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: 
 EXPORTS = ("convmi_output_dims", "convmi_workspace_size", "conv2d_forward", "conv2d_forward_noalloc",
            "conv2d_backward_data",
            "conv2d_backward_weight", "bn_stats_training", "activation_backward", "conv2d_backward_full",
-           "convmi_last_error",
+           "convmi_plan_name", "convmi_last_error",
            "convmi_version")
 
 
@@ -69,6 +69,7 @@ def _load():
     L.bn_stats_training.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.activation_backward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.conv2d_backward_full.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.convmi_plan_name.argtypes = [dp, i32, C.c_char_p, sz]
     for name in EXPORTS:
         if name not in ("convmi_last_error", "convmi_version"):
             getattr(L, name).restype = C.c_int
@@ -110,6 +111,13 @@ def workspace_size(desc: ConvDesc, op: int) -> int:
     n = C.c_size_t()
     _check(lib.convmi_workspace_size(C.byref(desc), op, C.byref(n)))
     return n.value
+
+
+def plan_name(desc: ConvDesc, op: int) -> str:
+    """Kernel plan of the forward or the input gradient for this descriptor (host only)."""
+    buf = C.create_string_buffer(128)
+    _check(lib.convmi_plan_name(C.byref(desc), op, buf, len(buf)))
+    return buf.value.decode()
 
 
 def _ptr(t):

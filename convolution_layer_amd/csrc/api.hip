@@ -204,6 +204,25 @@ CONVMI_API convmi_status convmi_workspace_size(const convmi_desc* desc, int32_t 
     return CONVMI_OK;
 }
 
+CONVMI_API convmi_status convmi_plan_name(const convmi_desc* desc, int32_t op, char* buf, size_t len) {
+    ConvDims d;
+    CHECK(check_desc(desc, &d));
+    if (!buf || len == 0) return fail(CONVMI_ERR_INVALID_ARG, "buf is NULL or len is 0");
+    const int dt = desc->dtype;
+    if (op == CONVMI_OP_FORWARD) {
+        if (!halo_plan_text(dt, d, true, buf, len))
+            snprintf(buf, len, "%s", igemm_fwd_supported(dt, d) ? "implicit gemm" : "direct");
+    } else if (op == CONVMI_OP_BACKWARD_DATA) {
+        if (!igemm_dx_supported(dt, d))
+            snprintf(buf, len, "direct");
+        else if (!halo_plan_text(dt, d, false, buf, len))
+            snprintf(buf, len, "implicit gemm");
+    } else {
+        return fail(CONVMI_ERR_INVALID_ARG, "plan names cover the forward and the input gradient, not op %d", op);
+    }
+    return CONVMI_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -111,6 +111,10 @@ hipError_t launch_igemm_dw(int dt, const void* x, const void* dz, float* dw, flo
 // path (backward, passed as w) directly.
 bool halo_fwd_supported(int dt, const ConvDims& d);
 bool halo_dx_supported(int dt, const ConvDims& d);
+// Text naming the stride-1 tile plan (block, fragments, tile, halo buffers, paired bands),
+// written into buf (at most len bytes, NUL-terminated); false when the layer takes no
+// tile plan.
+bool halo_plan_text(int dt, const ConvDims& d, bool fwd, char* buf, size_t len);
 size_t halo_fwd_ws_bytes(int dt, const ConvDims& d);
 size_t halo_dx_ws_bytes(int dt, const ConvDims& d);
 // bn_eval: null, or {mean, inv_std, gamma, beta} of evaluation-mode batch norm, applied

@@ -27,6 +27,8 @@
 // 16-byte chunks.  The epilogue stages the tile in LDS in the storage type (the
 // activation reads the stored pre-activation, so staging the rounded value loses nothing)
 // and writes 16-byte vectors.
+#include <stdio.h>
+
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
@@ -82,14 +84,17 @@ template <> struct HMma<bf16, 16> {
 // halves, so any 16 consecutive rows read at one logical chunk hit distinct banks.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
+constexpr int kCUs = 256;
+
 struct HaloGeom {
     int Hin, Win, Cin;     // gathered tensor: x (forward) or dz (input gradient)
     int KH, KW;
     int Hout, Wout, Nn;    // output image size and output channels
     int R, Q;              // output tile: R rows x Q columns
+    int R2;                // paired bands: rows of the short bands (0: one tile per workgroup)
     int HQ, HP, GH;        // halo row length (Q + KW - 1), positions, 8-position copy groups
     int org_r, org_c;      // halo origin relative to the tile origin
-    int tiles_r, tiles_c;  // tiles per image
+    int tiles_r, tiles_c;  // tile rows (paired: pairs of bands) and columns per image
     int nchunks;           // Cin / channels per 128-byte chunk
     int Kb;                // weight row length KH*KW*Cin
     int sign;              // +1 forward (tap at (kh, kw)), -1 input gradient (flipped)
@@ -296,7 +301,7 @@ constexpr int kThreadsH = 256;  // four waves, WM x WN
 // barriers below, active or not).
 template <typename T, int ACT, int BM, int BN, int NTH, class Out>
 __device__ __forceinline__ void epilogue_store(const T* Cs, const Out& out, const float* par, const HaloGeom& g,
-                                               int n, int r0, int c0, int n0, int sp) {
+                                               int n, int r0, int c0, int n0, int sp, int R) {
     constexpr int VEC = 16 / (int)sizeof(T);
     constexpr int LDC = BN + VEC;
     constexpr int OVR = BN / VEC;
@@ -308,7 +313,7 @@ __device__ __forceinline__ void epilogue_store(const T* Cs, const Out& out, cons
     const bool active = col < g.Nn;
     if (!Out::kStats && !active) return;
     const int nv = g.Nn - col < VEC ? g.Nn - col : VEC;
-    const int RQ = g.R * g.Q;
+    const int RQ = R * g.Q;
     const typename Out::Cache cache = out.prep(par, BN, cv * VEC, nv);
     float s1[VEC], s2[VEC], sh[VEC];
     int cnt = 0;
@@ -380,9 +385,14 @@ __device__ __forceinline__ void epilogue_store(const T* Cs, const Out& out, cons
 // boundaries, where each waits for all of its outstanding vector-memory operations:
 // LDS-DMA copies and register loads need not complete in issue order with respect to
 // each other, so a count that mixes the two kinds proves nothing.
+//
+// rb_tile computes one tile: R x Q pixels from row r0, column c0 of image n, output
+// channels n0 .. n0 + BN - 1, in BM = TM*WM*MF fragment rows; sp is the tile's index in
+// the per-tile statistics.  Two calls in one workgroup need a barrier between them (the
+// epilogue stages the tile in the halo's LDS).
 template <typename T, int BM, int BN, int WM, int WN, int ACT, class Out, int MF>
-__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_rb_kernel(
-    const T* __restrict__ A, HaloGeom g, const uint4* __restrict__ Bf, Out out, int tiles_n) {
+__device__ __forceinline__ void rb_tile(const T* __restrict__ A, const HaloGeom& g, const uint4* __restrict__ Bf,
+                                        const Out& out, int n, int r0, int c0, int n0, int R, int sp) {
     using MM = HMma<T, MF>;
     using Acc = typename MM::Acc;
     constexpr int NWAVE = 4, NTH = kThreadsH;
@@ -399,18 +409,10 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 
     const int t = threadIdx.x, lane = t & 63;
     const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int halo_bytes = g.GH * 1024;
+    const int halo_bytes = g.GH * 1024;  // buffer stride: the plan's largest halo
+    const int HPt = (R + g.KH - 1) * g.HQ, GHt = (HPt + 7) / 8;  // this tile's halo
     const bool two = g.hb == 2;
     const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int tn = tile % tiles_n;
-    const int sp = tile / tiles_n;
-    const int qsp = fdiv(sp, g.fTC);
-    const int tc = sp - qsp * g.tiles_c;
-    const int n = fdiv(qsp, g.fTR);
-    const int tr = qsp - n * g.tiles_r;
-    const int r0 = tr * g.R, c0 = tc * g.Q, n0 = tn * BN;
     const int hr0 = r0 + g.org_r, hc0 = c0 + g.org_c;
     const T* Aimg = A + (int64_t)n * g.img_stride;
     ParStage<Out, BN, NTH> pst;  // stored to LDS after the main loop
@@ -421,15 +423,15 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
     // Halo copy: a chunk's halo is JH copy instructions per wave; instruction j of this
     // wave covers halo positions 8*(wid + 4j) .. +7, lane l chunk l%8 of position l/8.
     const int rg = lane >> 3, pc = lane & 7;
-    const int JH = (g.GH + NWAVE - 1) / NWAVE;
+    const int JH = (GHt + NWAVE - 1) / NWAVE;
     auto issue_halo = [&](int c, int j0, int j1) {
         const uint32_t dstb = smem_base + (uint32_t)((two ? (c & 1) : 0) * halo_bytes);
         for (int j = j0; j < j1; ++j) {
             const int grp = wid + NWAVE * j;
-            if (grp >= g.GH) break;
+            if (grp >= GHt) break;
             const int p = grp * 8 + rg;
             const void* src = &kZero16;
-            if (p < g.HP) {
+            if (p < HPt) {
                 const int hr = fdiv(p, g.fHQ);
                 const int ih = hr0 + hr, iw = hc0 + (p - hr * g.HQ);
                 if ((unsigned)ih < (unsigned)g.Hin && (unsigned)iw < (unsigned)g.Win)
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         int m = wm * TM * MF + i * MF + lr;
-        if (m >= g.R * g.Q) m = 0;  // rows past the tile read a valid position; never stored
+        if (m >= R * g.Q) m = 0;  // rows past the tile read a valid position; never stored
         const int rr = fdiv(m, g.fQ);
         hpos[i] = rr * g.HQ + (m - rr * g.Q);
     }
@@ -568,7 +570,38 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) 
         }
     }
     __syncthreads();
-    epilogue_store<T, ACT, BM, BN, NTH>(Cs, out, par, g, n, r0, c0, n0, sp);
+    epilogue_store<T, ACT, BM, BN, NTH>(Cs, out, par, g, n, r0, c0, n0, sp, R);
+}
+
+// One tile per workgroup (BM2 = 0), or paired bands (BM2 > 0): the image's rows are cut
+// into tiles_r bands of R rows followed by tiles_r bands of R2 rows, and workgroup
+// (n, band b, column tile, channel tile) computes band b of each kind, the long one
+// first, the short one in BM2 fragment rows.  Every workgroup then carries the same
+// work, where equal tiles would leave the last round of workgroup slots partly empty.
+// (Running the short band first on half of the workgroups, so that co-resident
+// workgroups reach their epilogues at different times, measured slower on c4.)
+template <typename T, int BM, int BN, int WM, int WN, int ACT, class Out, int MF, int BM2>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_rb_kernel(
+    const T* __restrict__ A, HaloGeom g, const uint4* __restrict__ Bf, Out out, int tiles_n) {
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int tn = tile % tiles_n;
+    const int sp = tile / tiles_n;
+    const int qsp = fdiv(sp, g.fTC);
+    const int tc = sp - qsp * g.tiles_c;
+    const int n = fdiv(qsp, g.fTR);
+    const int tr = qsp - n * g.tiles_r;
+    const int c0 = tc * g.Q, n0 = tn * BN;
+    if constexpr (BM2 == 0) {
+        rb_tile<T, BM, BN, WM, WN, ACT, Out, MF>(A, g, Bf, out, n, tr * g.R, c0, n0, g.R, sp);
+    } else {
+        // statistics index: the 2*tiles_r bands of image n are contiguous, long ones first
+        const int bands = 2 * g.tiles_r;
+        rb_tile<T, BM, BN, WM, WN, ACT, Out, MF>(A, g, Bf, out, n, tr * g.R, c0, n0, g.R,
+                                                 (n * bands + tr) * g.tiles_c + tc);
+        __syncthreads();  // the first tile's epilogue is done with the LDS
+        rb_tile<T, BM2, BN, WM, WN, ACT, Out, MF>(A, g, Bf, out, n, g.tiles_r * g.R + tr * g.R2, c0, n0, g.R2,
+                                                  (n * bands + g.tiles_r + tr) * g.tiles_c + tc);
+    }
 }
 
 // Weights in B-fragment order for halo_rb_kernel with fragments of mf = 32 or 16 rows.
@@ -611,13 +644,14 @@ __global__ __launch_bounds__(256) void frag_weights(const T* __restrict__ w, uin
 
 // ------------------------------------------------------------------ host side
 constexpr int kLdsMax = 160 * 1024;
-constexpr int kCUs = 256;
 
 struct HaloPlan {
     int bm, bn, hb;
     int R, Q;
     int lds;     // dynamic LDS bytes per workgroup
     int mf = 32; // MFMA fragment height: bf16 32 (32x32x16) or 16 (16x16x32, 224-row blocks); fp32 16
+    int R2 = 0;  // paired bands: rows of the short bands, computed in bm2 fragment rows
+    int bm2 = 0;
 };
 
 int halo_groups(int R, int Q, int KH, int KW) { return ((R + KH - 1) * (Q + KW - 1) + 7) / 8; }
@@ -655,6 +689,27 @@ double plan_cost(int dt, const ConvDims& d, const Sides& sd, int bm, int bn, int
     if (hb == 1 && chunks > 1) clk += (chunks - 1) * halo / 34.0 * (occ == 1 ? 1.0 : 0.5);
     if (occ == 1) clk *= 1.6;  // a lone workgroup per CU leaves every stall exposed (measured)
     return rounds * occ * clk;
+}
+
+// Paired bands for 224-row tiles (halo_rb_kernel): each workgroup also takes a band of
+// R2 = 192 / Q rows (at most 12 fragments of 16 pixels, 192 rows).  Taken when the plain
+// tiles leave the last round of workgroup slots partly empty and the pairs need fewer
+// fragment-row rounds (7 per 224-row tile, 6 per short one); the bands must tile the
+// image with every band starting inside it.  c4 (64 images of 56 x 56, Q = 28): 896
+// tiles of 8 rows on 512 slots take two rounds of 7; 512 pairs of 8 + 6 rows take 13.
+void pair_bands(const ConvDims& d, const Sides& sd, HaloPlan* p) {
+    const int R = p->R, Q = p->Q, R2 = 192 / Q;
+    if (R2 < 1 || R2 >= R) return;
+    const int occ = p->lds <= kLdsMax / 2 ? 2 : 1;
+    const int64_t slots = (int64_t)kCUs * occ;
+    const int64_t per_band = (int64_t)d.N * ceil_div(sd.Wout, Q) * ceil_div(sd.Nn, p->bn);
+    const int64_t plain = ceil_div(per_band * ceil_div(sd.Hout, R), slots) * 7;
+    const int nb = (int)ceil_div(sd.Hout, R + R2);
+    if (nb * R + (nb - 1) * R2 >= sd.Hout) return;  // the last short band would start below the image
+    const int64_t paired = ceil_div(per_band * nb, slots) * (7 + ceil_div(R2 * Q, 32));
+    if (paired >= plain) return;
+    p->R2 = R2;
+    p->bm2 = 192;
 }
 
 // Output tiles are R x Q rectangles: Q is the whole row or an even split of it, and the
@@ -699,6 +754,7 @@ bool pick_halo(int dt, const ConvDims& d, const Sides& sd, HaloPlan* best) {
         try_bm(256, 32);
         try_bm(224, 16);
         if (!found) try_bm(128, 32);
+        if (found && best->bm == 224) pair_bands(d, sd, best);
         return found;
     }
     // fp32 with 128 output channels: 224-row blocks first (256 rows of 16x16x4 fragments
@@ -720,13 +776,14 @@ HaloGeom make_geom(const ConvDims& d, const Sides& sd, const HaloPlan& p, int dt
     g.Wout = sd.Wout;
     g.Nn = sd.Nn;
     g.R = p.R;
+    g.R2 = p.R2;
     g.Q = p.Q;
     g.HQ = p.Q + d.KW - 1;
     g.HP = (p.R + d.KH - 1) * g.HQ;
     g.GH = (g.HP + 7) / 8;
     g.org_r = fwd ? -d.ph : d.ph - d.KH + 1;
     g.org_c = fwd ? -d.pw : d.pw - d.KW + 1;
-    g.tiles_r = (int)ceil_div(sd.Hout, p.R);
+    g.tiles_r = p.R2 ? (int)ceil_div(sd.Hout, p.R + p.R2) : (int)ceil_div(sd.Hout, p.R);
     g.tiles_c = (int)ceil_div(sd.Wout, p.Q);
     g.nchunks = sd.Cin * (int)dtype_size(dt) / 128;
     g.Kb = d.KH * d.KW * sd.Cin;
@@ -748,10 +805,10 @@ template <class K> hipError_t raise_lds(K kern, bool& raised) {
     return e;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int ACT, class Out, int MF>
+template <typename T, int BM, int BN, int WM, int WN, int ACT, class Out, int MF, int BM2 = 0>
 hipError_t launch_rb(const T* A, const HaloGeom& g, const uint4* Bf, const Out& out, int images, int lds,
                      hipStream_t s) {
-    auto kern = halo_rb_kernel<T, BM, BN, WM, WN, ACT, Out, MF>;
+    auto kern = halo_rb_kernel<T, BM, BN, WM, WN, ACT, Out, MF, BM2>;
     static bool raised = false;
     const hipError_t e = raise_lds(kern, raised);
     if (e != hipSuccess) return e;
@@ -765,7 +822,7 @@ template <int ACT, class Out>
 hipError_t dispatch_f32(const float* A, const HaloGeom& g, const uint4* Bf, const Out& out, const HaloPlan& p,
                         int images, hipStream_t s) {
 #define CONVMI_HP(BM_, BN_)                                                                                      \
-    if (p.bm == BM_ && p.bn == BN_ && p.mf == 16)                                                              \
+    if (p.bm == BM_ && p.bn == BN_ && p.mf == 16 && p.bm2 == 0)                                                \
         return launch_rb<float, BM_, BN_, 2, 2, ACT, Out, 16>(A, g, Bf, out, images, p.lds, s);
     CONVMI_HP(224, 128) CONVMI_HP(224, 64) CONVMI_HP(256, 128) CONVMI_HP(256, 64)
 #undef CONVMI_HP
@@ -779,8 +836,10 @@ template <int ACT, class Out>
 hipError_t dispatch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, const Out& out, const HaloPlan& p,
                          int images, hipStream_t s) {
 #define CONVMI_RB(BM_, BN_, WM_, WN_, MF_)                                                                  \
-    if (p.bm == BM_ && p.bn == BN_ && p.mf == MF_)                                                            \
+    if (p.bm == BM_ && p.bn == BN_ && p.mf == MF_ && p.bm2 == 0)                                              \
         return launch_rb<bf16, BM_, BN_, WM_, WN_, ACT, Out, MF_>(A, g, Bf, out, images, p.lds, s);
+    if (p.bm == 224 && p.bn == 128 && p.mf == 16 && p.bm2 == 192)
+        return launch_rb<bf16, 224, 128, 2, 2, ACT, Out, 16, 192>(A, g, Bf, out, images, p.lds, s);
     CONVMI_RB(256, 128, 2, 2, 32) CONVMI_RB(224, 128, 2, 2, 16) CONVMI_RB(128, 128, 2, 2, 32)
     CONVMI_RB(512, 64, 4, 1, 32) CONVMI_RB(256, 64, 4, 1, 32) CONVMI_RB(128, 64, 4, 1, 32)
 #undef CONVMI_RB
@@ -823,6 +882,18 @@ bool halo_dx_supported(int dt, const ConvDims& d) {
     return d.sh == 1 && d.sw == 1 && pick_halo(dt, d, dx_sides(d), &p);
 }
 
+bool halo_plan_text(int dt, const ConvDims& d, bool fwd, char* buf, size_t len) {
+    HaloPlan p;
+    if (d.sh != 1 || d.sw != 1 || !pick_halo(dt, d, fwd ? fwd_sides(d) : dx_sides(d), &p)) return false;
+    if (p.R2)
+        snprintf(buf, len, "halo %s %dx%d mf%d tile %dx%d hb%d paired %dx%d in %d rows", dt == DT_BF16 ? "bf16" : "f32",
+                 p.bm, p.bn, p.mf, p.R, p.Q, p.hb, p.R2, p.Q, p.bm2);
+    else
+        snprintf(buf, len, "halo %s %dx%d mf%d tile %dx%d hb%d", dt == DT_BF16 ? "bf16" : "f32", p.bm, p.bn, p.mf,
+                 p.R, p.Q, p.hb);
+    return true;
+}
+
 size_t halo_fwd_ws_bytes(int dt, const ConvDims& d) {
     HaloPlan p;
     if (!halo_fwd_supported(dt, d) || !pick_halo(dt, d, fwd_sides(d), &p)) return 0;
@@ -839,7 +910,8 @@ int halo_fwd_stat_tiles(int dt, const ConvDims& d) {
     const Sides sd = fwd_sides(d);
     HaloPlan p;
     if (d.sh != 1 || d.sw != 1 || !pick_halo(dt, d, sd, &p)) return 0;
-    return (int)(d.N * ceil_div(sd.Hout, p.R) * ceil_div(sd.Wout, p.Q));
+    const int64_t bands = p.R2 ? 2 * ceil_div(sd.Hout, p.R + p.R2) : ceil_div(sd.Hout, p.R);
+    return (int)(d.N * bands * ceil_div(sd.Wout, p.Q));
 }
 
 hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bias, void* z, void* y,
@@ -851,7 +923,7 @@ hipError_t launch_halo_fwd(int dt, const void* x, const void* w, const float* bi
     const HaloGeom g = make_geom(d, sd, p, dt, true);
     if (stats_part) {
         if (bn_eval || !z) return hipErrorInvalidValue;
-        const int ntiles = d.N * g.tiles_r * g.tiles_c;
+        const int ntiles = d.N * (g.R2 ? 2 : 1) * g.tiles_r * g.tiles_c;
         const HFwdStatsOut os{z, bias, d.OC, stats_part, ntiles};
         const hipError_t e = launch_frag_weights(dt, w, (uint4*)ws, d, sd, p, true, s);
         if (e != hipSuccess) return e;

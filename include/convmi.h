@@ -252,6 +252,15 @@ convmi_status conv2d_backward_full(const convmi_desc* desc, const void* x, const
                                    int32_t saved_is_output, const void* dy, void* dx, float* dw, float* db,
                                    int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Name of the kernel plan that `op` (CONVMI_OP_FORWARD or CONVMI_OP_BACKWARD_DATA) takes
+ * for `desc`: "halo <dtype> <block rows>x<block channels> mf<fragment rows> tile <R>x<Q>
+ * hb<halo buffers>" for the stride-1 tile kernel (with " paired <R2>x<Q> in <rows> rows"
+ * when every workgroup also computes a short band of R2 rows), "implicit gemm" or
+ * "direct".  Host-only: no device work, for tests and tuning.  Written into buf, at most
+ * len bytes including the terminating NUL (longer names are cut).  Errors: invalid
+ * descriptor, NULL buf or len 0, another op (CONVMI_ERR_INVALID_ARG). */
+convmi_status convmi_plan_name(const convmi_desc* desc, int32_t op, char* buf, size_t len);
+
 /* Message describing the last non-OK status returned on the calling thread. */
 const char* convmi_last_error(void);
 

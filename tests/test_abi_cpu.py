@@ -282,3 +282,53 @@ def test_random_invalid_descriptors_are_rejected(cm, kw, fault):
     n = C.c_size_t()
     for op in range(6):
         assert cm.lib.convmi_workspace_size(C.byref(d), op, C.byref(n)) == cm.ERR_INVALID_ARG
+
+
+PLAN_RE = re.compile(r"^halo (bf16|f32) (\d+)x(\d+) mf(\d+) tile (\d+)x(\d+) hb([12])(?: paired (\d+)x(\d+) in (\d+) rows)?$")
+
+
+@pytest.mark.parametrize("name", sorted(WL.WORKLOADS))
+def test_plan_names_of_the_workloads(cm, name):
+    """The forward and input-gradient plans each workload takes (host-side planner)."""
+    wl = WL.WORKLOADS[name]
+    s = wl.shape
+    d = cm.make_desc(s.N, s.H, s.W, s.IC, s.OC, s.KH, s.KW, (s.sh, s.sw), (s.ph, s.pw), wl.act, wl.norm,
+                     dtype=cm.BF16 if wl.dtype == WL.BF16 else cm.F32)
+    expect = {"c1": "direct", "c2a": "implicit gemm", "c2b": "implicit gemm", "c2c": "implicit gemm",
+              "c3": "halo f32 256x64 mf16 tile 16x16 hb1",
+              "c4": "halo bf16 224x128 mf16 tile 8x28 hb2 paired 6x28 in 192 rows",
+              "c5": "halo bf16 256x64 mf32 tile 16x16 hb1"}[name]
+    assert cm.plan_name(d, cm.OP_FORWARD) == expect
+    assert cm.plan_name(d, cm.OP_BACKWARD_DATA) == expect
+
+
+def test_plan_name_checks(cm):
+    d = _good(cm)
+    buf = C.create_string_buffer(8)
+    assert cm.lib.convmi_plan_name(C.byref(d), cm.OP_FORWARD, buf, 8) == cm.OK
+    assert len(buf.value) == 7  # cut to the buffer, NUL-terminated
+    assert cm.lib.convmi_plan_name(C.byref(d), cm.OP_FORWARD, None, 8) == cm.ERR_INVALID_ARG
+    assert cm.lib.convmi_plan_name(C.byref(d), cm.OP_FORWARD, buf, 0) == cm.ERR_INVALID_ARG
+    for op in (cm.OP_BACKWARD_WEIGHT, cm.OP_BN_STATS, cm.OP_ACTIVATION_BACKWARD, cm.OP_BACKWARD_FULL, 9):
+        assert cm.lib.convmi_plan_name(C.byref(d), op, buf, 8) == cm.ERR_INVALID_ARG
+    bad = _good(cm, N=0)
+    assert cm.lib.convmi_plan_name(C.byref(bad), cm.OP_FORWARD, buf, 8) == cm.ERR_INVALID_ARG
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(st.integers(1, 96), st.integers(3, 120), st.integers(3, 120), st.sampled_from([(3, 1), (5, 2), (1, 0)]),
+       st.sampled_from([64, 128]))
+def test_paired_band_geometry(cm, N, H, W, kp, IC):
+    """Stride-1 bf16 layers with 128 output channels: a paired plan's bands of R and R2
+    rows tile the image, every band starts inside it, and the tiles fit their blocks."""
+    k, p = kp
+    d = cm.make_desc(N, H, W, IC, 128, k, k, (1, 1), (p, p), 0, 0, dtype=cm.BF16)
+    m = PLAN_RE.match(cm.plan_name(d, cm.OP_FORWARD))
+    if not m or m.group(8) is None:
+        return
+    bm, R, Q, R2, Q2, bm2 = (int(m.group(i)) for i in (2, 5, 6, 8, 9, 10))
+    OH, OW = cm.output_dims(d)
+    assert Q2 == Q and R2 < R and R * Q <= bm and R2 * Q <= bm2 < bm
+    nb = -(-OH // (R + R2))
+    assert nb * R + (nb - 1) * R2 < OH <= nb * (R + R2)
+    assert -(-OW // Q) * Q >= OW
