@@ -29,6 +29,8 @@
 // and writes 16-byte vectors.
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "internal.hpp"
 #include "lds_dma.hpp"
 
@@ -294,6 +296,10 @@ struct HDxOut {
 
 constexpr int kThreadsH = 256;  // four waves, WM x WN
 
+// Waves per SIMD the register budget of halo_rb_kernel is set for: 64-channel bf16 tiles
+// of 16-row fragments fit four workgroups on a CU (128 VGPRs), the others two.
+constexpr int rb_waves(int esize, int bn, int mf) { return esize == 2 && bn == 64 && mf == 16 ? 4 : 2; }
+
 // Second half of the epilogue: the tile's stored values sit in LDS (Cs, rows of LDC
 // elements, pixel m = rr*Q + qq of the tile at row m); thread t writes columns
 // (t % OVR)*VEC .. +VEC of rows t/OVR, t/OVR + NTH/OVR, ...  With Out::kStats it also
@@ -501,19 +507,27 @@ __device__ __forceinline__ void rb_tile(const T* __restrict__ A, const HaloGeom&
             const int p = hpos[i] + toff;
             fo[i] = (uint32_t)(hbase + p * 128 + ((lg ^ swz(p)) << 4));
         }
-        uint4 fa[2][TM];
+        // A fragments of k-step kk + 1 are read during kk's MFMAs (two buffers) where two
+        // waves share a SIMD; with four, the other waves cover the read latency and one
+        // buffer keeps the register budget.
+        constexpr int NFA = rb_waves((int)sizeof(T), BN, MF) > 2 ? 1 : 2;
+        uint4 fa[NFA][TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) fa[0][i] = *(const uint4*)(smem + fo[i]);
 #pragma unroll
         for (int kk = 0; kk < KST; ++kk) {
-            if (kk + 1 < KST) {
+            if (NFA == 2 && kk + 1 < KST) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) fa[(kk + 1) & 1][i] = *(const uint4*)(smem + (fo[i] ^ ((kk + 1) << (MF == 32 ? 5 : 6))));
+                for (int i = 0; i < TM; ++i)
+                    fa[(kk + 1) % NFA][i] = *(const uint4*)(smem + (fo[i] ^ ((kk + 1) << (MF == 32 ? 5 : 6))));
+            } else if (NFA == 1 && kk > 0) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa[0][i] = *(const uint4*)(smem + (fo[i] ^ (kk << (MF == 32 ? 5 : 6))));
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) MM::run(acc[i][j], cur[j][kk], fa[kk & 1][i]);
+                for (int j = 0; j < TN; ++j) MM::run(acc[i][j], cur[j][kk], fa[kk % NFA][i]);
             // The next chunk's halo, issued once this chunk's first MFMAs are under way.
             if (kk == 0 && two && c + 1 < g.nchunks && tap == 0) issue_halo(c + 1, 0, JH);
         }
@@ -581,7 +595,7 @@ __device__ __forceinline__ void rb_tile(const T* __restrict__ A, const HaloGeom&
 // (Running the short band first on half of the workgroups, so that co-resident
 // workgroups reach their epilogues at different times, measured slower on c4.)
 template <typename T, int BM, int BN, int WM, int WN, int ACT, class Out, int MF, int BM2>
-__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void halo_rb_kernel(
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(rb_waves(sizeof(T), BN, MF)))) void halo_rb_kernel(
     const T* __restrict__ A, HaloGeom g, const uint4* __restrict__ Bf, Out out, int tiles_n) {
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     const int tn = tile % tiles_n;
@@ -700,7 +714,7 @@ double plan_cost(int dt, const ConvDims& d, const Sides& sd, int bm, int bn, int
 void pair_bands(const ConvDims& d, const Sides& sd, HaloPlan* p) {
     const int R = p->R, Q = p->Q, R2 = 192 / Q;
     if (R2 < 1 || R2 >= R) return;
-    const int occ = p->lds <= kLdsMax / 2 ? 2 : 1;
+    const int occ = std::min(rb_waves(2, p->bn, p->mf), kLdsMax / p->lds);  // workgroups per CU
     const int64_t slots = (int64_t)kCUs * occ;
     const int64_t per_band = (int64_t)d.N * ceil_div(sd.Wout, Q) * ceil_div(sd.Nn, p->bn);
     const int64_t plain = ceil_div(per_band * ceil_div(sd.Hout, R), slots) * 7;
@@ -756,6 +770,16 @@ bool pick_halo(int dt, const ConvDims& d, const Sides& sd, HaloPlan* best) {
         if (!found) try_bm(128, 32);
         if (found && best->bm == 224) pair_bands(d, sd, best);
         return found;
+    }
+    if (dt == DT_BF16) {
+        // 64 channels: 224-row blocks of 16-row fragments (four workgroups per CU) when
+        // paired bands fill whole rounds of slots; otherwise the 32-row-fragment blocks below
+        try_bm(224, 16);
+        if (found) {
+            pair_bands(d, sd, best);
+            if (best->R2) return true;
+            found = false;
+        }
     }
     // fp32 with 128 output channels: 224-row blocks first (256 rows of 16x16x4 fragments
     // exceed the register budget of two workgroups per CU)
@@ -840,7 +864,10 @@ hipError_t dispatch_bf16(const bf16* A, const HaloGeom& g, const uint4* Bf, cons
         return launch_rb<bf16, BM_, BN_, WM_, WN_, ACT, Out, MF_>(A, g, Bf, out, images, p.lds, s);
     if (p.bm == 224 && p.bn == 128 && p.mf == 16 && p.bm2 == 192)
         return launch_rb<bf16, 224, 128, 2, 2, ACT, Out, 16, 192>(A, g, Bf, out, images, p.lds, s);
+    if (p.bm == 224 && p.bn == 64 && p.mf == 16 && p.bm2 == 192)
+        return launch_rb<bf16, 224, 64, 2, 2, ACT, Out, 16, 192>(A, g, Bf, out, images, p.lds, s);
     CONVMI_RB(256, 128, 2, 2, 32) CONVMI_RB(224, 128, 2, 2, 16) CONVMI_RB(128, 128, 2, 2, 32)
+    CONVMI_RB(224, 64, 2, 2, 16)
     CONVMI_RB(512, 64, 4, 1, 32) CONVMI_RB(256, 64, 4, 1, 32) CONVMI_RB(128, 64, 4, 1, 32)
 #undef CONVMI_RB
     return hipErrorInvalidValue;

@@ -297,7 +297,7 @@ def test_plan_names_of_the_workloads(cm, name):
     expect = {"c1": "direct", "c2a": "implicit gemm", "c2b": "implicit gemm", "c2c": "implicit gemm",
               "c3": "halo f32 256x64 mf16 tile 16x16 hb1",
               "c4": "halo bf16 224x128 mf16 tile 8x28 hb2 paired 6x28 in 192 rows",
-              "c5": "halo bf16 256x64 mf32 tile 16x16 hb1"}[name]
+              "c5": "halo bf16 224x64 mf16 tile 14x16 hb1 paired 12x16 in 192 rows"}[name]
     assert cm.plan_name(d, cm.OP_FORWARD) == expect
     assert cm.plan_name(d, cm.OP_BACKWARD_DATA) == expect
 

@@ -5,8 +5,7 @@ through the plan introspection call, that the paired kernel is the one that runs
 compares full tensors with the fp64 oracle: forward z and y without normalisation, with
 training batch norm (per-tile statistics from the epilogue), evaluation batch norm (the
 normalisation inside the epilogue) and group norm (per-image tile statistics), and the
-input gradient.  Both band orders run in every case (the workgroups of the second half
-of the slots take the short band first)."""
+input gradient; 128-channel plans (two workgroups per CU) and the 64-channel one (four)."""
 import numpy as np
 import pytest
 import torch
@@ -29,6 +28,9 @@ def _require_gpu():
 C56 = (40, 56, 56, 128, 128, 3, 3, 1, 1, 1, 1)
 C54 = (40, 54, 54, 128, 128, 3, 3, 1, 1, 1, 1)
 C56_37 = (37, 56, 56, 128, 128, 3, 3, 1, 1, 1, 1)
+# 64 channels: 224-row blocks of 16-row fragments, four workgroups per CU (c5's plan at
+# 6 images: bands of 14 and 12 rows of 16 pixels)
+C224_64 = (6, 224, 224, 64, 64, 3, 3, 1, 1, 1, 1)
 
 
 def _problem(s, seed):
@@ -52,8 +54,8 @@ def _assert_paired(desc, ops, R2):
         assert f" paired {R2}x" in name, name
 
 
-@pytest.mark.parametrize("case", [(C56, WL.ACT_TANH, 6), (C54, WL.ACT_RELU, 7)],
-                         ids=["56x56_r8+6_tanh", "54x54_r8+7_ragged_relu"])
+@pytest.mark.parametrize("case", [(C56, WL.ACT_TANH, 6), (C54, WL.ACT_RELU, 7), (C224_64, WL.ACT_SIGMOID, 12)],
+                         ids=["56x56_r8+6_tanh", "54x54_r8+7_ragged_relu", "224x224x64_r14+12_sigmoid"])
 def test_paired_forward_and_input_gradient(case):
     s, act, R2 = case
     shape, dt, x, w, b, dy, _, _ = _problem(s, 700)
@@ -129,3 +131,23 @@ def test_paired_group_norm():
     G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r.ravel(), var_r.ravel(),
                       inv_r.ravel(), eps, "paired group fwd", G.TOL[dt])
     G.assert_close(G.host(out["y"]), O.apply_group_norm(zs, act, gamma, beta, mean_r, inv_r), dt, "paired group y")
+
+
+def test_paired_64_channel_batchnorm_training():
+    """Per-tile statistics from the 64-channel paired kernel."""
+    shape, dt, x, w, b, _, gamma, beta = _problem(C224_64, 740)
+    act, mom, eps = WL.ACT_TANH, 0.1, 1e-5
+    rm0 = np.zeros(shape.OC)
+    rv0 = np.ones(shape.OC)
+    desc = G.shape_desc(shape, dt, act, WL.NORM_BATCH, mom, eps)
+    _assert_paired(desc, (0,), 12)
+    out = G.run_forward(desc, dt, G.dev(x, dt), G.dev(w, dt), G.dev(b), G.dev(gamma), G.dev(beta), G.dev(rm0),
+                        G.dev(rv0))
+    z_r = O.conv2d_forward(x, w, b, (1, 1), (1, 1))
+    G.assert_close(G.host(out["z"]), z_r, dt, "paired 64 bn z")
+    zs = WL.round_to(dt, z_r)
+    mean_r, var_r, inv_r, _, _ = O.bn_stats(zs, mom, eps, rm0, rv0)
+    G.assert_bn_stats(G.host(out["save_mean"]), G.host(out["save_inv_std"]), mean_r, var_r, inv_r, eps,
+                      "paired 64 bn fwd", G.TOL[dt])
+    G.assert_close(G.host(out["y"]), O.apply_activation(zs, act, WL.NORM_BATCH, gamma, beta, mean_r, inv_r), dt,
+                   "paired 64 bn y")
