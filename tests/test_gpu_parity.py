@@ -62,6 +62,12 @@ MEDIUM = [
     ((2, 16, 40, 32, 30, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_TANH),
     ((2, 18, 33, 20, 64, 3, 3, 1, 1, 1, 1), WL.F32, WL.ACT_IDENTITY),
     ((3, 12, 12, 64, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_TANH),
+    # 128-channel weight gradients with one output row per stage in a deeper LDS ring:
+    # 36-position rows (3 k-steps, 12 padded positions), 49-position rows (4 k-steps), with
+    # KW = 1 and 2 (generic k-step loop)
+    ((3, 40, 36, 128, 128, 3, 3, 1, 1, 1, 1), WL.BF16, WL.ACT_RELU),
+    ((2, 23, 49, 128, 128, 3, 2, 1, 1, 1, 0), WL.BF16, WL.ACT_TANH),
+    ((2, 17, 60, 128, 128, 1, 1, 1, 1, 0, 0), WL.BF16, WL.ACT_IDENTITY),
     # two-row images: the halo only fits LDS once, so later chunks reload it in place
     ((2, 2, 256, 128, 64, 7, 7, 1, 1, 3, 3), WL.BF16, WL.ACT_RELU),
     ((2, 2, 256, 64, 128, 7, 7, 1, 1, 3, 3), WL.BF16, WL.ACT_IDENTITY),
