@@ -45,11 +45,20 @@ __global__ __launch_bounds__(kThreads) void conv_fwd_direct(const T* __restrict_
 }
 
 // dx[n,ih,iw,ic] = sum over taps landing on (ih,iw) of w*dz (gather form of the
-// scatter in backward_input).  ic fastest: a wave shares the dz pixel.
+// scatter in backward_input).  ic fastest: a wave shares the dz pixel.  Eight lanes
+// share an element and split its output channels (lane j takes oc = j, j + 8, ...); the
+// eight partial sums are added across the lanes in a butterfly in which every lane adds
+// the same pairs (IEEE addition is commutative), so the result depends only on the data.
+// The chain per lane is an eighth as long as with one lane per element.
+constexpr int kDxLanes = 8;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void conv_dx_direct(const T* __restrict__ dz, const T* __restrict__ w,
                                                            T* __restrict__ dx, ConvDims d, int64_t total) {
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int j = threadIdx.x & (kDxLanes - 1);
+    const int64_t step = (int64_t)gridDim.x * (kThreads / kDxLanes);
+    // the loop bound is uniform over each group of eight lanes (same element)
+    for (int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / kDxLanes; i < total; i += step) {
         int ic = (int)(i % d.IC);
         int64_t t = i / d.IC;
         int iw = (int)(t % d.W);
@@ -70,10 +79,13 @@ __global__ __launch_bounds__(kThreads) void conv_dx_direct(const T* __restrict__
                 const T* gp = dz + (((int64_t)n * d.OH + oh) * d.OW + ow) * d.OC;
                 const T* wp = w + ((int64_t)kh * d.KW + kw) * d.IC + ic;
                 const int64_t wstride = (int64_t)d.KH * d.KW * d.IC;
-                for (int oc = 0; oc < d.OC; ++oc) acc = __builtin_fmaf(to_f32(wp[oc * wstride]), to_f32(gp[oc]), acc);
+                for (int oc = j; oc < d.OC; oc += kDxLanes)
+                    acc = __builtin_fmaf(to_f32(wp[oc * wstride]), to_f32(gp[oc]), acc);
             }
         }
-        dx[i] = from_f32<T>(acc);
+#pragma unroll
+        for (int m = 1; m < kDxLanes; m <<= 1) acc += __shfl_xor(acc, m);
+        if (j == 0) dx[i] = from_f32<T>(acc);
     }
 }
 
@@ -148,7 +160,7 @@ hipError_t launch_conv_fwd_direct(int dt, const void* x, const void* w, const fl
 hipError_t launch_conv_dx_direct(int dt, const void* dz, const void* w, void* dx, const ConvDims& d,
                                  hipStream_t s) {
     int64_t total = (int64_t)d.N * d.H * d.W * d.IC;
-    dim3 grid(grid_for(total)), block(kThreads);
+    dim3 grid(grid_for(total * kDxLanes)), block(kThreads);
     if (dt == DT_BF16)
         conv_dx_direct<bf16><<<grid, block, 0, s>>>((const bf16*)dz, (const bf16*)w, (bf16*)dx, d, total);
     else
