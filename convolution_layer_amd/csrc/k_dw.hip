@@ -1031,30 +1031,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // dw = (accumulate ? dw : 0) + sum over slabs; four slab groups (s = q mod 4) per output
 // vector are summed in slab order and then merged in group order: fixed order, so
-// bitwise reproducible.  Loads go out eight at a time before their in-order adds, so a
-// thread keeps eight loads in flight.  Blocks past the dw blocks finish db the same way
-// (64 channels each).  count is a multiple of 4.
-template <int U>
+// bitwise reproducible.  Blocks past the dw blocks finish db the same way (64 channels
+// each).  count is a multiple of 4.
+// sum_strided: a thread's slabs s = first, first + STEP, ... < S go out in batches of U
+// loads before their in-order adds (a batch costs one memory latency, not U); past the
+// last slab the index is clamped to an in-bounds re-read and zero is added instead.
+template <int U, int STEP = 4>
 __device__ __forceinline__ float4 sum_strided(const float4* __restrict__ p, int64_t stride4, int first, int S) {
     float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = first;
-    for (; s + 4 * (U - 1) < S; s += 4 * U) {
+    for (int s = first; s < S; s += STEP * U) {
         float4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = p[(int64_t)(s + 4 * u) * stride4];
+        for (int u = 0; u < U; ++u) v[u] = p[(int64_t)(s + STEP * u < S ? s + STEP * u : S - 1) * stride4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            r.x += v[u].x; r.y += v[u].y; r.z += v[u].z; r.w += v[u].w;
+        for (int u = 0; u < U; ++u) {  // selects, not branches (a branch would let the load sink into it)
+            const bool in = s + STEP * u < S;
+            r.x += in ? v[u].x : 0.f; r.y += in ? v[u].y : 0.f; r.z += in ? v[u].z : 0.f; r.w += in ? v[u].w : 0.f;
         }
-    }
-    for (; s < S; s += 4) {
-        const float4 v = p[(int64_t)s * stride4];
-        r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
     }
     return r;
 }
 
-__global__ __launch_bounds__(NT) void dw_reduce4(const float* __restrict__ part, const float* __restrict__ part_db,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void dw_reduce4(const float* __restrict__ part, const float* __restrict__ part_db,
                                                  float* __restrict__ dw, float* __restrict__ db, int64_t count,
                                                  int OC, int S, int Sdb, int accumulate) {
     __shared__ float4 red[4][64];
@@ -1086,11 +1084,7 @@ __global__ __launch_bounds__(NT) void dw_reduce4(const float* __restrict__ part,
     // 16 thread groups (q, sub) split the slabs: group g = 4q + sub takes s = g mod 16
     float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
     const int grp = q * 4 + sub;
-    if (c4 < oc4)
-        for (int s = grp; s < Sdb; s += 16) {
-            const float4 v = ((const float4*)part_db)[(int64_t)s * oc4 + c4];
-            r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
-        }
+    if (c4 < oc4) r = sum_strided<8, 16>((const float4*)part_db + c4, oc4, grp, Sdb);
     __shared__ float4 rdb[16][16];
     rdb[grp][o & 15] = r;
     __syncthreads();
