@@ -82,9 +82,23 @@ template <> struct HMma<bf16, 16> {
     static __device__ __forceinline__ int row(int lg, int e) { return 4 * lg + e; }
 };
 
-// 16-byte chunk swizzle of a 128-byte LDS row: rows 2j and 2j+1 fall in different bank
-// halves, so any 16 consecutive rows read at one logical chunk hit distinct banks.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// 16-byte chunk swizzle of a 128-byte LDS row (one halo position): the slot of logical
+// chunk k at position p is k ^ swz<MF>(key(p)).  A ds_read_b128 runs in four passes of 16
+// lanes (measured on gfx950 with the bank-conflict counters): lanes 0-7 with 24-31, 8-15
+// with 16-23, 32-39 with 56-63 and 40-47 with 48-55; the 64 banks take 16 distinct 16-byte
+// (position parity, slot) pairs per pass.  With fragments of 16 pixels a pass holds 8
+// consecutive pixels reading chunk L and the next 8 reading chunk L ^ 1, so the slot is
+// 2 * ((key >> 1) & 3): one slot of each XOR-1 pair, the pair's other slot left to the
+// other half.  With 32-pixel fragments both halves read one chunk and pixels 24 apart
+// share a pass: slot (key >> 1) & 7.  Either is conflict-free when a fragment's 16 or 32
+// keys are consecutive integers of its positions' parity.  key = halo row * QS + halo
+// column with QS = HQ - 2*((KW-1)/2) (Q for odd KW): the keys of consecutive tile pixels
+// under one tap are then consecutive even where a fragment crosses a tile row (its raw
+// positions skip the KW-1 halo columns there), and QS = HQ mod 2 keeps the key's parity
+// the position's.
+template <int MF> __device__ __forceinline__ int swz(int key) {
+    return MF == 16 ? ((key >> 1) & 3) << 1 : (key >> 1) & 7;
+}
 
 constexpr int kCUs = 256;
 
@@ -95,6 +109,7 @@ struct HaloGeom {
     int R, Q;              // output tile: R rows x Q columns
     int R2;                // paired bands: rows of the short bands (0: one tile per workgroup)
     int HQ, HP, GH;        // halo row length (Q + KW - 1), positions, 8-position copy groups
+    int QS;                // row length of the swizzle key (HQ - 2*((KW-1)/2))
     int org_r, org_c;      // halo origin relative to the tile origin
     int tiles_r, tiles_c;  // tile rows (paired: pairs of bands) and columns per image
     int nchunks;           // Cin / channels per 128-byte chunk
@@ -412,6 +427,11 @@ __device__ __forceinline__ void rb_tile(const T* __restrict__ A, const HaloGeom&
     constexpr int VEC = 16 / (int)sizeof(T), CK = 128 / (int)sizeof(T), KST = MF == 32 ? 4 : 2,
                   LGS = MF == 32 ? 5 : 4;
     extern __shared__ __align__(1024) unsigned char smem[];
+    // Swizzle key: row*QS + column (conflict-free also for fragments that cross a tile
+    // row) in the bf16 two-wave kernels; the raw position in the others, which have no
+    // register to spare for it and whose plans use 16-pixel rows (16-pixel fragments
+    // never cross one).
+    constexpr bool KEYED = sizeof(T) == 2 && rb_waves(2, BN, MF) == 2;
 
     const int t = threadIdx.x, lane = t & 63;
     const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -438,23 +458,27 @@ __device__ __forceinline__ void rb_tile(const T* __restrict__ A, const HaloGeom&
             const int p = grp * 8 + rg;
             const void* src = &kZero16;
             if (p < HPt) {
-                const int hr = fdiv(p, g.fHQ);
-                const int ih = hr0 + hr, iw = hc0 + (p - hr * g.HQ);
+                const int hr = fdiv(p, g.fHQ), hc = p - hr * g.HQ;
+                const int ih = hr0 + hr, iw = hc0 + hc, key = KEYED ? hr * g.QS + hc : p;
                 if ((unsigned)ih < (unsigned)g.Hin && (unsigned)iw < (unsigned)g.Win)
-                    src = Aimg + ((int64_t)ih * g.Win + iw) * g.Cin + c * CK + (pc ^ swz(p)) * VEC;
+                    src = Aimg + ((int64_t)ih * g.Win + iw) * g.Cin + c * CK + (pc ^ swz<MF>(key)) * VEC;
             }
             dma16(src, __builtin_amdgcn_readfirstlane(dstb + grp * 1024));
         }
     };
     const int wm = wid / WN, wn = wid % WN;
     const int lr = lane & (MF - 1), lg = lane >> LGS;
+    // halo position of each fragment's pixel at tap 0 (KEYED: in the low 16 bits, the
+    // swizzle key in the high 16)
     int hpos[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         int m = wm * TM * MF + i * MF + lr;
-        if (m >= R * g.Q) m = 0;  // rows past the tile read a valid position; never stored
-        const int rr = fdiv(m, g.fQ);
-        hpos[i] = rr * g.HQ + (m - rr * g.Q);
+        // rows past the tile read a valid pixel (never stored); KEYED: one whose key keeps
+        // the lane's residue mod 16, so it does not collide with the fragment's other lanes
+        if (m >= R * g.Q) m = KEYED && R * g.Q >= 16 ? (m & 15) : 0;
+        const int rr = fdiv(m, g.fQ), cc = m - rr * g.Q;
+        hpos[i] = KEYED ? (rr * g.HQ + cc) | ((rr * g.QS + cc) << 16) : rr * g.HQ + cc;
     }
     // B fragments: 32-row group (n0 + wn*TN*32)/32 + j, step st, k-step kk at
     // ((group * nsteps + st) * 4 + kk) * 64 + lane
@@ -496,7 +520,8 @@ __device__ __forceinline__ void rb_tile(const T* __restrict__ A, const HaloGeom&
         // paths makes the compiler wait for it at the merge as if it were on every path,
         // which would stall each step on the next step's fragments.
         load_b(st + 1 < nsteps ? st + 1 : st, nxt);
-        const int toff = g.sign > 0 ? kh * g.HQ + kw : (g.KH - 1 - kh) * g.HQ + (g.KW - 1 - kw);
+        const int th = g.sign > 0 ? kh : g.KH - 1 - kh, tw = g.sign > 0 ? kw : g.KW - 1 - kw;
+        const int toff = th * g.HQ + tw, tkey = th * g.QS + tw;
         const int hbase = __builtin_amdgcn_readfirstlane((two ? (c & 1) : 0) * halo_bytes);
         // LDS offset of the A fragment at k-step 0; the halo buffer and every 128-byte row
         // start are 128-byte aligned, so k-step kk (chunk G*kk + lg = G*kk ^ lg, G = 2 or 4
@@ -504,8 +529,9 @@ __device__ __forceinline__ void rb_tile(const T* __restrict__ A, const HaloGeom&
         uint32_t fo[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int p = hpos[i] + toff;
-            fo[i] = (uint32_t)(hbase + p * 128 + ((lg ^ swz(p)) << 4));
+            const int p = (KEYED ? hpos[i] & 0xffff : hpos[i]) + toff;
+            const int key = KEYED ? (hpos[i] >> 16) + tkey : p;
+            fo[i] = (uint32_t)(hbase + p * 128 + ((lg ^ swz<MF>(key)) << 4));
         }
         // A fragments of k-step kk + 1 are read during kk's MFMAs (two buffers) where two
         // waves share a SIMD; with four, the other waves cover the read latency and one
@@ -803,6 +829,7 @@ HaloGeom make_geom(const ConvDims& d, const Sides& sd, const HaloPlan& p, int dt
     g.R2 = p.R2;
     g.Q = p.Q;
     g.HQ = p.Q + d.KW - 1;
+    g.QS = g.HQ - 2 * ((d.KW - 1) / 2);
     g.HP = (p.R + d.KH - 1) * g.HQ;
     g.GH = (g.HP + 7) / 8;
     g.org_r = fwd ? -d.ph : d.ph - d.KH + 1;
