@@ -561,10 +561,15 @@ struct Dw3Geom {
 
 // 16-byte chunk swizzle of an LDS row of ROWB bytes: 4 consecutive rows read at the same
 // 32-byte column piece (bf16 transposing reads) or 64-byte piece (fp32 reads) land in
-// different slots of the 256 bytes the banks span.  256-byte rows: chunk ^ 4*(row%4);
-// 128-byte rows (two rows per bank span): chunk ^ 2*((row/2)%2).
+// different slots of the 256 bytes the banks span.  256-byte rows: chunk ^ 4*(row%4).
+// 128-byte rows (two rows per bank span): chunk ^ 4*((row/2)%2).  An XOR with 2 there
+// left the transposing reads 2-way conflicted on the bank-conflict counters; the XOR
+// with 4 is conflict-free under each lane-pass grouping of ds_read_b64_tr_b16 that is
+// consistent with the counters, at every row offset the taps and k-steps produce.  The
+// swizzle has period 4 in the row, so the second segment's rows, a multiple of 4
+// further, keep it.
 template <int ROWB> __device__ __forceinline__ int sw3(int row) {
-    return ROWB == 256 ? (row & 3) << 2 : ((row >> 1) & 1) << 1;
+    return ROWB == 256 ? (row & 3) << 2 : ((row >> 1) & 1) << 2;
 }
 
 // Stage copies of the stride-1 weight-gradient kernels, for tiles of CH channels of T
