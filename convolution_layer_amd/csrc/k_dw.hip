@@ -285,8 +285,14 @@ __global__ __launch_bounds__(NT) void dw_kernel(const T* __restrict__ x, const T
 // address (so lane r pointing at row kb + r/4, column c0 + 4*(r%4) makes lane i receive
 // positions kb..kb+3 of column c0 + i); for fp32 with one 4-byte read per position.
 // 16-byte chunks are XOR-swizzled by (row & 3) << 1 so the four rows a 16-lane group
-// touches fall in distinct banks.  Two ring stages, two workgroups per CU.
-__device__ __forceinline__ int dswz(int row) { return (row & 3) << 1; }
+// touches fall in distinct banks; in rows of 256 bytes or more read as fp32 or as 32-row
+// bf16 fragments by (row & 3) << 2, since there the four rows' 64-byte column pieces
+// (fp32) or 32-byte pieces of both lane halves (bf16) only stay apart with steps of four
+// chunks (the steps of two left those reads 2-way conflicted on the bank-conflict
+// counters).  Two ring stages, two workgroups per CU.
+template <int ES, int MF> __device__ __forceinline__ int dswz(int row, int R) {
+    return (row & 3) << (R >= 256 && (ES == 4 || MF == 32) ? 2 : 1);
+}
 
 typedef short dw_short4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) dw_short4* dw_lds4_t;
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
         const int j = wid + 4 * q;
         if (j < IA) {
             const int row = j * ROWS_A + lane / CA;
-            const int lc = (lane % CA) ^ dswz(row);
+            const int lc = (lane % CA) ^ dswz<ES, MF>(row, RA);
             rowi[q] = row;
             colo[q] = oc0 + lc * VEC;
             cok[q] = colo[q] < g.OC;
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
         } else {
             const int jb = j - IA;
             const int row = jb * ROWS_B + lane / CB;
-            const int lc = (lane % CB) ^ dswz(row);
+            const int lc = (lane % CB) ^ dswz<ES, MF>(row, RB);
             const int k = k0 + lc * VEC;
             rowi[q] = row;
             colo[q] = k;
@@ -406,7 +412,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
             for (int half = 0; half < 2; ++half) {
                 const int row = kb + 4 * half + (lr >> 2);
                 const int cb = 2 * (c + 4 * (lr & 3));  // byte offset of the lane's 8-byte piece
-                const int off = row * R + ((((cb >> 4) ^ dswz(row)) << 4) | (cb & 15));
+                const int off = row * R + ((((cb >> 4) ^ dswz<ES, MF>(row, R)) << 4) | (cb & 15));
                 h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(base + off));
             }
             v.x = __builtin_bit_cast(uint2, h[0]).x; v.y = __builtin_bit_cast(uint2, h[0]).y;
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
             for (int s4 = 0; s4 < 4; ++s4) {
                 const int row = kb + 4 * s4;
                 const int cb = 4 * (c + lr);
-                const int off = row * R + ((((cb >> 4) ^ dswz(row)) << 4) | (cb & 15));
+                const int off = row * R + ((((cb >> 4) ^ dswz<ES, MF>(row, R)) << 4) | (cb & 15));
                 r[s4] = *(const uint32_t*)(base + off);
             }
             return make_uint4(r[0], r[1], r[2], r[3]);
@@ -435,7 +441,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
         for (int half = 0; half < 2; ++half) {
             const int row = kb + 4 * half + (l16 >> 2);
             const int cb = 2 * (c + 16 * hi + 4 * (l16 & 3));
-            const int off = row * R + ((((cb >> 4) ^ dswz(row)) << 4) | (cb & 15));
+            const int off = row * R + ((((cb >> 4) ^ dswz<ES, MF>(row, R)) << 4) | (cb & 15));
             h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds4_t)(base + off));
         }
         v.x = __builtin_bit_cast(uint2, h[0]).x; v.y = __builtin_bit_cast(uint2, h[0]).y;
@@ -497,7 +503,7 @@ __global__ __launch_bounds__(NT) void dw2_kernel(const T* __restrict__ x, const 
         if (do_db) {
             const unsigned char* As = smem + (k & 1) * STAGE;
             for (int row = t / CA; row < BK; row += NT / CA) {
-                const uint4 v = *(const uint4*)(As + row * RA + ((db_chunk ^ dswz(row)) << 4));
+                const uint4 v = *(const uint4*)(As + row * RA + ((db_chunk ^ dswz<ES, MF>(row, RA)) << 4));
                 MM::add_channels(v, dbs);
             }
         }
