@@ -653,33 +653,28 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(rb_wa
 // the matrix are zero.
 template <typename T>
 __global__ __launch_bounds__(256) void frag_weights(const T* __restrict__ w, uint4* __restrict__ dst, int Nn,
-                                                    int taps, int Cin, int nsteps, int groups, int fwd, int mf) {
+                                                    int taps, int Cin, int nsteps, int fwd, int mf) {
+    // block (st, group) writes the kst*64 units of one step of one row group; thread
+    // kk*64 + lane writes unit (..., kk) * 64 + lane (no per-unit index division)
     constexpr int EV = 16 / (int)sizeof(T), CK = 128 / (int)sizeof(T);  // per 16 bytes, per 128-byte chunk
     const int kst = mf == 32 ? 4 : 2;
-    const int64_t total = (int64_t)groups * nsteps * kst * 64;
-    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
-        const int l = (int)(u & 63);
-        const int64_t q = u >> 6;
-        const int kk = (int)(q % kst);
-        const int64_t q2 = q / kst;
-        const int st = (int)(q2 % nsteps);
-        const int grp = (int)(q2 / nsteps);
-        const int row = grp * mf + (l % mf);
-        const int chunk = st / taps, tap = st - chunk * taps;
-        const int ch0 = chunk * CK + kk * (CK / kst) + (l / mf) * EV;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (row < Nn) {
-            if (fwd) {
-                v = *(const uint4*)(w + ((int64_t)row * taps + tap) * Cin + ch0);
-            } else {
-                T e[EV];
+    const int st = blockIdx.x, grp = blockIdx.y;
+    const int l = threadIdx.x & 63, kk = threadIdx.x >> 6;
+    const int row = grp * mf + (l & (mf - 1));
+    const int chunk = st / taps, tap = st - chunk * taps;
+    const int ch0 = chunk * CK + kk * (CK / kst) + (l / mf) * EV;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < Nn) {
+        if (fwd) {
+            v = *(const uint4*)(w + ((int64_t)row * taps + tap) * Cin + ch0);
+        } else {
+            T e[EV];
 #pragma unroll
-                for (int k = 0; k < EV; ++k) e[k] = w[((int64_t)(ch0 + k) * taps + tap) * Nn + row];
-                __builtin_memcpy(&v, e, 16);
-            }
+            for (int k = 0; k < EV; ++k) e[k] = w[((int64_t)(ch0 + k) * taps + tap) * Nn + row];
+            __builtin_memcpy(&v, e, 16);
         }
-        dst[u] = v;
     }
+    dst[((int64_t)((int64_t)grp * nsteps + st) * kst + kk) * 64 + l] = v;
 }
 
 // ------------------------------------------------------------------ host side
@@ -912,15 +907,16 @@ hipError_t launch_frag_weights(int dt, const void* w, uint4* dst, const ConvDims
                                const HaloPlan& p, bool fwd, hipStream_t s) {
     const int taps = d.KH * d.KW;
     const int nsteps = (sd.Cin * (int)dtype_size(dt) / 128) * taps;
-    const int groups = (int)(ceil_div(sd.Nn, p.bn) * (p.bn / p.mf));
-    const int64_t units = (int64_t)groups * nsteps * (p.mf == 32 ? 4 : 2) * 64;
-    const int grid = (int)(ceil_div(units, 256) < 2048 ? ceil_div(units, 256) : 2048);
+    const int64_t groups = ceil_div(sd.Nn, p.bn) * (p.bn / p.mf);
+    if (groups > 65535) return hipErrorInvalidValue;  // grid y limit (Nn above a million channels)
+    const dim3 grid((unsigned)nsteps, (unsigned)groups);
+    const int threads = (p.mf == 32 ? 4 : 2) * 64;
     if (dt == DT_BF16)
-        frag_weights<bf16><<<grid, 256, 0, s>>>((const bf16*)w, dst, sd.Nn, taps, sd.Cin, nsteps, groups, fwd ? 1 : 0,
-                                                 p.mf);
+        frag_weights<bf16><<<grid, threads, 0, s>>>((const bf16*)w, dst, sd.Nn, taps, sd.Cin, nsteps, fwd ? 1 : 0,
+                                                     p.mf);
     else
-        frag_weights<float><<<grid, 256, 0, s>>>((const float*)w, dst, sd.Nn, taps, sd.Cin, nsteps, groups,
-                                                  fwd ? 1 : 0, p.mf);
+        frag_weights<float><<<grid, threads, 0, s>>>((const float*)w, dst, sd.Nn, taps, sd.Cin, nsteps, fwd ? 1 : 0,
+                                                      p.mf);
     return hipGetLastError();
 }
 

@@ -455,9 +455,9 @@ __global__ __launch_bounds__(NT) void dx_weights(const T* __restrict__ w, T* __r
                                                  int KWs) {
     const int Ncol = d.sh * d.sw * d.IC;
     const int Kb = KHs * KWs * d.OC;
-    const int64_t total = (int64_t)Ncol * Kb;
-    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total; i += (int64_t)gridDim.x * NT) {
-        const int k = (int)(i % Kb), col = (int)(i / Kb);
+    const int total = Ncol * Kb;  // below 2^31 (checked by the launcher): 32-bit index arithmetic
+    for (int i = blockIdx.x * NT + threadIdx.x; i < total; i += gridDim.x * NT) {
+        const int col = i / Kb, k = i - col * Kb;
         const int oc = k % d.OC, ab = k / d.OC;
         const int b = ab % KWs, a = ab / KWs;
         const int ic = col % d.IC, ph_ = col / d.IC;
@@ -640,6 +640,7 @@ hipError_t launch_igemm_dx(int dt, const void* dz, const void* w, void* dx, cons
     // rearranged weights into the workspace
     {
         const int64_t total = (int64_t)Ncol * Kb;
+        if (total > INT32_MAX - 4096 * (int64_t)NT) return hipErrorInvalidValue;
         const int grid = (int)(ceil_div(total, NT) < 4096 ? ceil_div(total, NT) : 4096);
         if (dt == DT_BF16)
             dx_weights<bf16><<<grid, NT, 0, s>>>((const bf16*)w, (bf16*)ws, d, KHs, KWs);
