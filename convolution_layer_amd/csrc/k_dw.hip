@@ -1063,9 +1063,10 @@ __device__ __forceinline__ float4 sum_strided(const float4* __restrict__ p, int6
     return r;
 }
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void dw_reduce4(const float* __restrict__ part, const float* __restrict__ part_db,
-                                                 float* __restrict__ dw, float* __restrict__ db, int64_t count,
-                                                 int OC, int S, int Sdb, int accumulate) {
+// (register budget for two waves per SIMD: a batch of 24 float4 loads stays in flight)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void dw_reduce4(
+    const float* __restrict__ part, const float* __restrict__ part_db, float* __restrict__ dw, float* __restrict__ db,
+    int64_t count, int OC, int S, int Sdb, int accumulate) {
     __shared__ float4 red[4][64];
     const int q = threadIdx.x >> 6, o = threadIdx.x & 63;
     const int64_t n4 = count >> 2;

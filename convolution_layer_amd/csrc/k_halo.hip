@@ -94,8 +94,8 @@ template <> struct HMma<bf16, 16> {
 // keys are consecutive integers of its positions' parity.  key = halo row * QS + halo
 // column with QS = HQ - 2*((KW-1)/2) (Q for odd KW): the keys of consecutive tile pixels
 // under one tap are then consecutive even where a fragment crosses a tile row (its raw
-// positions skip the KW-1 halo columns there), and QS = HQ mod 2 keeps the key's parity
-// the position's.
+// positions skip the KW-1 halo columns there), and QS, of HQ's parity, keeps the key's
+// parity the position's.
 template <int MF> __device__ __forceinline__ int swz(int key) {
     return MF == 16 ? ((key >> 1) & 3) << 1 : (key >> 1) & 7;
 }
